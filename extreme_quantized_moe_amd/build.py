@@ -1,0 +1,64 @@
+"""Build libmilo.so (HIP, gfx950) in-tree with hipcc.
+
+    python -m extreme_quantized_moe_amd.build [--verbose]
+
+Each translation unit is compiled to an object in _build/ (in parallel), then
+linked into extreme_quantized_moe_amd/libmilo.so.  Always recompiles.
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libmilo.so")
+SOURCES = ["abi.cpp", "quant_pack.hip", "route.hip", "combine.hip", "lowrank.hip",
+           "gemm_decode.hip", "gemm_prefill.hip"]
+ARCH = os.environ.get("MILO_OFFLOAD_ARCH", "gfx950")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # no packed fp32 arithmetic (v_pk_*_f32) in any generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _compile(src):
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    return src, obj, r.returncode, r.stdout + r.stderr, cmd
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        for src, obj, rc, out, cmd in ex.map(_compile, SOURCES):
+            if verbose or rc:
+                sys.stderr.write(f"[milo build] {src}: rc={rc}\n")
+                if out.strip():
+                    lines = [l for l in out.splitlines() if "packed-fp32-ops" not in l]
+                    sys.stderr.write("\n".join(lines[-60:]) + "\n")
+            if rc:
+                raise RuntimeError(f"hipcc failed on {src}: {' '.join(cmd)}")
+            objs.append(obj)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode:
+        raise RuntimeError("link failed: " + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    if verbose:
+        sys.stderr.write(f"[milo build] wrote {LIB}\n")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="--verbose" in sys.argv)

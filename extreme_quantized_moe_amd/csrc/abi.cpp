@@ -1,0 +1,292 @@
+// The C ABI of libmilo (declared in include/milo.h): argument validation,
+// workspace planning and kernel dispatch.  Host code only; every check runs
+// before anything is enqueued.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gemm_common.hpp"
+
+namespace milo {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+}
+
+int32_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MILO_OK;
+  set_error("%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+  return MILO_ERR_HIP;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+#define MILO_FAIL(code, ...)   \
+  do {                         \
+    set_error(__VA_ARGS__);    \
+    return (code);             \
+  } while (0)
+
+GemmArgs make_gemm_args(const milo_gemm_desc* d, const GemmPlan& p, char* ws) {
+  GemmArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = d->x;
+  a.sorted_pairs = d->sorted_pairs;
+  a.offsets = d->offsets;
+  a.slot_w = d->slot_w;
+  for (int f = 0; f < 2; ++f) {
+    const milo_weights& w = d->w[f < d->n_w ? f : 0];
+    a.packed[f] = w.packed;
+    a.sz[f] = w.sz;
+    a.U[f] = w.U;
+    a.rank[f] = w.rank;
+  }
+  a.T = (const uint16_t*)(ws + p.off_t);
+  a.y = d->y;
+  a.words_per_expert = milo_packed_words(d->N, d->K);
+  a.sz_per_expert = milo_sz_words(d->N, d->K);
+  a.N = d->N;
+  a.K = d->K;
+  a.kblocks = p.kblocks;
+  a.n_tiles = p.n_tiles;
+  a.gather_div = d->gather_div;
+  a.num_experts = d->num_experts;
+  a.n_w = d->n_w;
+  a.rp = p.rp;
+  a.max_rank = d->max_rank;
+  a.epilogue = d->epilogue;
+  a.ksplit = p.dec_ksplit;
+  a.dec_max_rows = p.dec_max_rows;
+  a.pre_min_rows = p.pre_launch ? (p.dec_mt ? p.dec_max_rows : 0) : 0;
+  return a;
+}
+
+static int32_t validate_gemm(const milo_gemm_desc* d) {
+  if (!d) MILO_FAIL(MILO_ERR_NULL, "desc is NULL");
+  if (d->num_experts < 1 || d->num_experts > 256)
+    MILO_FAIL(MILO_ERR_SHAPE, "num_experts=%d outside 1..256", d->num_experts);
+  if (d->N <= 0 || d->K <= 0 || d->N > 65536 || d->K > 65536 || d->N % 64 || d->K % 128)
+    MILO_FAIL(MILO_ERR_SHAPE, "N=%d K=%d: need N %% 64 == 0, K %% 128 == 0, both in 1..65536", d->N, d->K);
+  if (d->max_rank < 0 || d->max_rank > kMaxRank || d->max_rank % 8)
+    MILO_FAIL(MILO_ERR_RANK, "max_rank=%d: need 0..64, multiple of 8", d->max_rank);
+  if (d->epilogue < MILO_EPI_NONE || d->epilogue > MILO_EPI_ROUTE_SCALE)
+    MILO_FAIL(MILO_ERR_ARG, "unknown epilogue %d", d->epilogue);
+  if (d->path < MILO_PATH_AUTO || d->path > MILO_PATH_PREFILL)
+    MILO_FAIL(MILO_ERR_ARG, "unknown path %d", d->path);
+  if ((d->epilogue == MILO_EPI_SWIGLU) != (d->n_w == 2) || (d->n_w != 1 && d->n_w != 2))
+    MILO_FAIL(MILO_ERR_ARG, "n_w=%d does not match epilogue %d (SWIGLU needs 2, others 1)", d->n_w, d->epilogue);
+  if (d->num_pairs < 0 || d->num_pairs > (1 << 20))
+    MILO_FAIL(MILO_ERR_SHAPE, "num_pairs=%d outside 0..1048576", d->num_pairs);
+  if (d->max_rows_per_expert < 0) MILO_FAIL(MILO_ERR_SHAPE, "max_rows_per_expert < 0");
+  if (d->gather_div < 0) MILO_FAIL(MILO_ERR_SHAPE, "gather_div < 0");
+  if (d->x_rows < 0) MILO_FAIL(MILO_ERR_SHAPE, "x_rows < 0");
+  if (!d->x || !d->offsets || !d->y) MILO_FAIL(MILO_ERR_NULL, "x, offsets and y are required");
+  if ((d->gather_div > 0 || d->epilogue == MILO_EPI_ROUTE_SCALE) && !d->sorted_pairs)
+    MILO_FAIL(MILO_ERR_NULL, "sorted_pairs is required with gather_div > 0 or ROUTE_SCALE");
+  if (d->epilogue == MILO_EPI_ROUTE_SCALE && (!d->slot_w || d->y_rows < 1))
+    MILO_FAIL(MILO_ERR_NULL, "ROUTE_SCALE needs slot_w and y_rows >= 1");
+  for (int f = 0; f < d->n_w; ++f) {
+    const milo_weights& w = d->w[f];
+    if (!w.packed || !w.sz) MILO_FAIL(MILO_ERR_NULL, "w[%d].packed / sz is NULL", f);
+    if (d->max_rank > 0 && (!w.U || !w.V || !w.rank))
+      MILO_FAIL(MILO_ERR_NULL, "w[%d].U / V / rank is NULL with max_rank > 0", f);
+    if (!aligned(w.packed, 16) || !aligned(w.sz, 16) || !aligned(w.U, 16) || !aligned(w.V, 16))
+      MILO_FAIL(MILO_ERR_ALIGN, "w[%d] pointers must be 16-byte aligned", f);
+    if (w.rank && !aligned(w.rank, 4)) MILO_FAIL(MILO_ERR_ALIGN, "w[%d].rank must be 4-byte aligned", f);
+  }
+  if (!aligned(d->x, 16) || !aligned(d->y, 16))
+    MILO_FAIL(MILO_ERR_ALIGN, "x and y must be 16-byte aligned");
+  if (!aligned(d->offsets, 4) || !aligned(d->sorted_pairs, 4) || !aligned(d->slot_w, 4))
+    MILO_FAIL(MILO_ERR_ALIGN, "offsets, sorted_pairs, slot_w must be 4-byte aligned");
+  return MILO_OK;
+}
+
+int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
+  memset(p, 0, sizeof *p);
+  p->n_tiles = d->N / kTileRows;
+  p->kblocks = d->K / kTileK;
+  p->rp = d->max_rank == 0 ? 0 : (int)round_up((size_t)d->max_rank, 32);
+  const int P = d->num_pairs;
+  int rows_bound = d->max_rows_per_expert > 0 ? d->max_rows_per_expert : P;
+  if (rows_bound > P) rows_bound = P;
+  if (P == 0) return MILO_OK;  // nothing to do
+
+  auto mt_for = [](int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); };
+  if (d->path == MILO_PATH_DECODE) {
+    if (rows_bound > kDecodeMaxRows)
+      MILO_FAIL(MILO_ERR_SHAPE, "decode path needs <= %d rows per expert (bound %d)", kDecodeMaxRows, rows_bound);
+    p->dec_mt = mt_for(rows_bound);
+  } else if (d->path == MILO_PATH_PREFILL) {
+    p->dec_mt = 0;
+    p->pre_launch = 1;
+  } else if (rows_bound <= kDecodeMaxRows) {
+    p->dec_mt = mt_for(rows_bound);
+  } else {
+    p->dec_mt = 2;
+    p->pre_launch = 1;
+  }
+  p->dec_max_rows = 16 * p->dec_mt;
+  p->pre_tiles = (P + 127) / 128 + d->num_experts;
+
+  if (p->dec_mt) {
+    const int active = d->num_experts < P ? d->num_experts : P;
+    const int blocks = active * p->n_tiles;
+    int ks = (1024 + blocks - 1) / blocks;
+    int ks_max = p->kblocks / 4;
+    if (ks_max < 1) ks_max = 1;
+    if (ks > ks_max) ks = ks_max;
+    if (ks < 1) ks = 1;
+    p->dec_ksplit = ks;
+  }
+  p->lr_tiles = (P + 15) / 16 + d->num_experts;
+  p->lr_kchunks = 1;
+  if (p->rp && rows_bound <= kDecodeMaxRows && p->lr_tiles <= kMaxLrCounters) {
+    int kc = d->K / 32 / 4;
+    p->lr_kchunks = kc > 16 ? 16 : (kc < 1 ? 1 : kc);
+  }
+
+  // The counter regions sit at fixed offsets at the start of every workspace,
+  // whatever the call, so that counters left at zero by one call are still
+  // counters (and zero) for the next call that uses the same workspace.
+  size_t off = 0;
+  p->off_lr_cnt = off;
+  off += (size_t)kMaxLrCounters * 4;
+  p->off_dec_cnt = off;
+  off += (size_t)kMaxDecCounters * 4;
+  p->off_t = off;
+  off += round_up((size_t)P * d->n_w * p->rp * 2, 256);
+  p->off_lr_part = off;
+  if (p->lr_kchunks > 1) off += round_up((size_t)p->lr_kchunks * p->lr_tiles * 16 * d->n_w * p->rp * 4, 256);
+  p->off_dec_part = off;
+  if (p->dec_ksplit > 1)
+    off += round_up((size_t)p->dec_ksplit * d->num_experts * p->n_tiles * d->n_w * p->dec_mt * 16 * 64 * 4, 256);
+  p->total = off;
+  return MILO_OK;
+}
+
+}  // namespace milo
+
+using namespace milo;
+
+extern "C" {
+
+int32_t milo_abi_version(void) { return MILO_ABI_VERSION; }
+int32_t milo_layout_version(void) { return MILO_LAYOUT_VERSION; }
+
+const char* milo_status_string(int32_t s) {
+  switch (s) {
+    case MILO_OK: return "ok";
+    case MILO_ERR_NULL: return "a required pointer is NULL";
+    case MILO_ERR_SHAPE: return "a size violates the documented constraints";
+    case MILO_ERR_ALIGN: return "a pointer is not aligned as documented";
+    case MILO_ERR_RANK: return "compensator rank outside the supported range";
+    case MILO_ERR_WORKSPACE: return "workspace missing or too small";
+    case MILO_ERR_ARG: return "an enum or flag argument has no meaning";
+    case MILO_ERR_HIP: return "a HIP runtime call or launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* milo_last_error(void) { return g_err; }
+
+int64_t milo_packed_words(int64_t rows, int64_t K) { return 3 * rows * K / 32; }
+int64_t milo_sz_words(int64_t rows, int64_t K) { return rows * K / 64; }
+
+int32_t milo_quantize_rtn_int3(const float* W, int64_t rows, int64_t K, uint8_t* codes,
+                               uint16_t* scale, uint16_t* zero, void* stream) {
+  g_err[0] = 0;
+  if (!W || !codes || !scale || !zero) MILO_FAIL(MILO_ERR_NULL, "W, codes, scale, zero are required");
+  if (rows < 1 || K < 64 || K % 64 || rows > (1ll << 31) || K > (1ll << 31))
+    MILO_FAIL(MILO_ERR_SHAPE, "rows=%lld K=%lld: need rows >= 1, K >= 64, K %% 64 == 0",
+              (long long)rows, (long long)K);
+  if (!aligned(W, 4) || !aligned(scale, 2) || !aligned(zero, 2))
+    MILO_FAIL(MILO_ERR_ALIGN, "W must be 4-byte and scale/zero 2-byte aligned");
+  return launch_quantize(W, rows, K, codes, scale, zero, (hipStream_t)stream);
+}
+
+int32_t milo_pack_int3(const uint8_t* codes, const uint16_t* scale, const uint16_t* zero,
+                       int64_t rows, int64_t K, uint32_t* packed, uint32_t* sz, void* stream) {
+  g_err[0] = 0;
+  if (!codes || !scale || !zero || !packed || !sz)
+    MILO_FAIL(MILO_ERR_NULL, "codes, scale, zero, packed, sz are required");
+  if (rows <= 0 || K <= 0 || rows % 64 || K % 128 || rows > (1ll << 31) || K > (1ll << 31))
+    MILO_FAIL(MILO_ERR_SHAPE, "rows=%lld K=%lld: need rows %% 64 == 0 and K %% 128 == 0",
+              (long long)rows, (long long)K);
+  if (!aligned(codes, 16) || !aligned(packed, 16) || !aligned(sz, 16) || !aligned(scale, 2) || !aligned(zero, 2))
+    MILO_FAIL(MILO_ERR_ALIGN, "codes, packed, sz must be 16-byte aligned");
+  return launch_pack(codes, scale, zero, rows, K, packed, sz, (hipStream_t)stream);
+}
+
+size_t milo_route_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t S) {
+  (void)k;
+  if (T <= 256) return 0;
+  const size_t nb = ((size_t)T + 255) / 256;
+  return round_up(nb * (size_t)(E + S) * 4, 256);
+}
+
+int32_t milo_route_sort(const float* logits, int32_t T, int32_t E, int32_t k, int32_t S,
+                        int32_t renormalize, int32_t* topk_ids, float* topk_w, float* slot_w,
+                        int32_t* sorted_pairs, int32_t* pair_pos, int32_t* offsets,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!logits || !topk_ids || !topk_w || !slot_w || !sorted_pairs || !pair_pos || !offsets)
+    MILO_FAIL(MILO_ERR_NULL, "logits and all outputs are required");
+  if (T < 1 || T > 65536) MILO_FAIL(MILO_ERR_SHAPE, "T=%d outside 1..65536", T);
+  if (E < 1 || k < 1 || k > E || k > 8 || S < 0 || E + S > 256 || k + S > 16)
+    MILO_FAIL(MILO_ERR_SHAPE, "E=%d k=%d S=%d: need 1 <= k <= min(E, 8), E + S <= 256, k + S <= 16", E, k, S);
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(slot_w, 4) ||
+      !aligned(sorted_pairs, 4) || !aligned(pair_pos, 4) || !aligned(offsets, 4))
+    MILO_FAIL(MILO_ERR_ALIGN, "routing arrays must be 4-byte aligned");
+  const size_t need = milo_route_workspace_bytes(T, E, k, S);
+  if (need && (!workspace || ws_bytes < need))
+    MILO_FAIL(MILO_ERR_WORKSPACE, "route workspace %zu bytes < required %zu", ws_bytes, need);
+  if (need && !aligned(workspace, 4)) MILO_FAIL(MILO_ERR_ALIGN, "workspace must be 4-byte aligned");
+  return launch_route(logits, T, E, k, S, renormalize ? 1 : 0, topk_ids, topk_w, slot_w, sorted_pairs,
+                      pair_pos, offsets, workspace, (hipStream_t)stream);
+}
+
+size_t milo_moe_gemm_workspace_bytes(const milo_gemm_desc* d) {
+  if (validate_gemm(d) != MILO_OK) return 0;
+  GemmPlan p;
+  if (plan_gemm(d, &p) != MILO_OK) return 0;
+  return p.total;
+}
+
+int32_t milo_moe_w3a16_lowrank_gemm(const milo_gemm_desc* d, void* workspace, size_t ws_bytes,
+                                    void* stream) {
+  g_err[0] = 0;
+  int32_t rc = validate_gemm(d);
+  if (rc != MILO_OK) return rc;
+  GemmPlan p;
+  rc = plan_gemm(d, &p);
+  if (rc != MILO_OK) return rc;
+  if (d->num_pairs == 0) return MILO_OK;
+  if (p.total && (!workspace || ws_bytes < p.total))
+    MILO_FAIL(MILO_ERR_WORKSPACE, "gemm workspace %zu bytes < required %zu", ws_bytes, p.total);
+  if (p.total && !aligned(workspace, 256)) MILO_FAIL(MILO_ERR_ALIGN, "workspace must be 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  rc = launch_lowrank(d, p, ws, st);
+  if (rc != MILO_OK) return rc;
+  rc = launch_gemm_decode(d, p, ws, st);
+  if (rc != MILO_OK) return rc;
+  return launch_gemm_prefill(d, p, ws, st);
+}
+
+int32_t milo_moe_combine(const float* y, int32_t T, int32_t slots, int32_t H, uint16_t* out,
+                         void* stream) {
+  g_err[0] = 0;
+  if (!y || !out) MILO_FAIL(MILO_ERR_NULL, "y and out are required");
+  if (T < 1 || slots < 1 || slots > 16 || H < 4 || H % 4)
+    MILO_FAIL(MILO_ERR_SHAPE, "T=%d slots=%d H=%d: need T >= 1, 1 <= slots <= 16, H %% 4 == 0", T, slots, H);
+  if (!aligned(y, 16) || !aligned(out, 16)) MILO_FAIL(MILO_ERR_ALIGN, "y and out must be 16-byte aligned");
+  return launch_combine(y, T, slots, H, out, (hipStream_t)stream);
+}
+
+}  // extern "C"

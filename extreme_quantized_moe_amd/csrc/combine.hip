@@ -1,0 +1,39 @@
+// Weighted combine of a token's slot outputs: out[t] = sum_j y[t*slots + j]
+// in slot order (float32), rounded once to float16.
+// [talk] = "MiLo: Efficient Quantized MoE Inference with Mixture of Low-Rank
+// Compensators" (MLSys 2025 talk write-up), Background: a token's output
+// combines the outputs of the experts it activates.
+#include "milo_internal.hpp"
+
+namespace milo {
+
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ y, int T, int slots,
+                                                      int H, uint16_t* __restrict__ out) {
+  const int hq = H >> 2;
+  const int64_t total = (int64_t)T * hq;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / hq;
+    const int h4 = (int)(i - t * hq);
+    const float4* src = (const float4*)(y + (size_t)t * slots * H) + h4;
+    float4 acc = src[0];
+    for (int j = 1; j < slots; ++j) {
+      const float4 v = src[(size_t)j * hq];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    uint2 o;
+    o.x = (uint32_t)float_to_half_bits(acc.x) | ((uint32_t)float_to_half_bits(acc.y) << 16);
+    o.y = (uint32_t)float_to_half_bits(acc.z) | ((uint32_t)float_to_half_bits(acc.w) << 16);
+    ((uint2*)(out + (size_t)t * H))[h4] = o;
+  }
+}
+
+int32_t launch_combine(const float* y, int T, int slots, int H, uint16_t* out, hipStream_t st) {
+  const int64_t work = (int64_t)T * (H / 4);
+  int64_t g = (work + 255) / 256;
+  if (g > 16384) g = 16384;
+  hipLaunchKernelGGL(combine_kernel, dim3((int)g), dim3(256), 0, st, y, T, slots, H, out);
+  return hip_status(hipGetLastError(), "combine_kernel launch");
+}
+
+}  // namespace milo

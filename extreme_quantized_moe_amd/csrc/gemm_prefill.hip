@@ -1,0 +1,241 @@
+// Matrix-core (prefill) path of the routed W3A16 + low-rank grouped GEMM.
+//
+// [talk] = "MiLo: Efficient Quantized MoE Inference with Mixture of Low-Rank
+// Compensators" (MLSys 2025 talk write-up).  MiLo Kernel: int3 x fp16 GEMM
+// with fused dequantization; asynchronous global loads overlap memory with
+// compute.  MiLo Algorithm: W_out = W_quant + U V.
+//
+// Block = 128 rows of one expert (pairs in sorted order) x 4 waves.  Each wave
+// owns one 64-wide output tile of one weight family (SWIGLU: waves (W1, W3) x
+// two n-tiles; otherwise four n-tiles of the one family), so every packed
+// weight tile is read and dequantized by exactly one wave.  Activation rows
+// are staged through LDS (128 rows x 128 K, double buffered, rows padded by
+// 16 bytes against bank conflicts) and shared by the four waves; the next
+// K block's activations and weights are loaded into registers while the
+// current one is computed.  Weights are dequantized in registers (int3 pair
+// extraction + one fused multiply-add per value in fp32, rounded once to
+// fp16) and multiplied on v_mfma_f32_16x16x32_f16 with fp32 accumulation.
+// Epilogue: low-rank term as two more matrix-core K-steps per 32 ranks, then
+// SWIGLU through LDS, or fp16 store, or route-weighted fp32 scatter.
+#include "gemm_common.hpp"
+
+namespace milo {
+
+constexpr int kBM = 128;                 // rows per block
+constexpr int kMT = kBM / 16;            // m-tiles per wave
+constexpr int kXStride = kTileK + 8;     // LDS row stride in halves (272 B)
+constexpr int kXBuf = kBM * kXStride;    // halves per buffer
+
+// (expert, first row, rows) of the `tile`-th 128-row tile among the experts
+// with more than min_rows rows.
+__device__ __forceinline__ bool find_tile128(const int32_t* offsets, int num_experts, int min_rows,
+                                             int tile, int* e_out, int* m0_out, int* rows_out) {
+  int cum = 0;
+  for (int e = 0; e < num_experts; ++e) {
+    const int m = offsets[e + 1] - offsets[e];
+    if (m <= min_rows) continue;
+    const int nt = (m + kBM - 1) / kBM;
+    if (tile < cum + nt) {
+      *e_out = e;
+      *m0_out = (tile - cum) * kBM;
+      *rows_out = m;
+      return true;
+    }
+    cum += nt;
+  }
+  return false;
+}
+
+template <int NW>
+__global__ void __launch_bounds__(256) gemm_prefill_kernel(GemmArgs a) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
+  int e, m0, M;
+  if (!find_tile128(a.offsets, a.num_experts, a.pre_min_rows, blockIdx.x, &e, &m0, &M)) return;
+  const int base = a.offsets[e];
+  const int f = (NW == 2) ? (wave & 1) : 0;
+  const int nt = (NW == 2) ? (2 * blockIdx.y + (wave >> 1)) : (4 * blockIdx.y + wave);
+  const bool wave_on = nt < a.n_tiles;
+
+  // ---- activation staging: thread loads 8 chunks of 16 B per K block
+  const uint16_t* xsrc[8];
+  int xdst[8];
+  bool xok[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = tid + 256 * j;
+    const int row = c >> 4, kc = c & 15;
+    const int m = m0 + row;
+    xok[j] = m < M;
+    int xr = 0;
+    if (xok[j]) xr = a.gather_div > 0 ? a.sorted_pairs[base + m] / a.gather_div : base + m;
+    xsrc[j] = a.x + (size_t)xr * a.K + 8 * kc;
+    xdst[j] = row * kXStride + 8 * kc;
+  }
+  u32x4 xreg[8];
+  auto load_x = [&](int kb) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      xreg[j] = xok[j] ? *(const u32x4*)(xsrc[j] + (size_t)kb * kTileK) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *(u32x4*)(lds + buf * kXBuf + xdst[j]) = xreg[j];
+  };
+
+  // ---- weights of this wave
+  const uint32_t* tbase = a.packed[f] + e * a.words_per_expert + (size_t)(wave_on ? nt : 0) * a.kblocks * kTileWords;
+  const uint32_t* sbase = a.sz[f] + e * a.sz_per_expert + (size_t)(wave_on ? nt : 0) * a.kblocks * kTileSzWords;
+  u32x4 wq[3], wz[2];
+  auto load_w = [&](int kb) {
+    const uint32_t* tp = tbase + (size_t)kb * kTileWords;
+    const uint32_t* sp = sbase + (size_t)kb * kTileSzWords + 8 * (lane & 15);
+    wq[0] = *(const u32x4*)(tp + 4 * lane);
+    wq[1] = *(const u32x4*)(tp + 256 + 4 * lane);
+    wq[2] = *(const u32x4*)(tp + 512 + 4 * lane);
+    wz[0] = *(const u32x4*)(sp);
+    wz[1] = *(const u32x4*)(sp + 4);
+  };
+
+  f32x4 acc[kMT][4];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_x(0);
+  if (wave_on) load_w(0);
+  store_x(0);
+  __syncthreads();
+
+  const int KB = a.kblocks;
+  for (int kb = 0; kb < KB; ++kb) {
+    const int buf = kb & 1;
+    // dequantize this K block's weights (registers) before the next loads land
+    f16x8 wf[4][4];
+    if (wave_on) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t h[16];
+        extract_triplet(wq[0][i], wq[1][i], wq[2][i], h);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int idx = 2 * i + g;
+          const GroupConst gc = group_const(idx < 4 ? wz[0][idx] : wz[1][idx - 4]);
+          wf[i][2 * g] = dequant_step(h, 2 * g, gc);
+          wf[i][2 * g + 1] = dequant_step(h, 2 * g + 1, gc);
+        }
+      }
+    }
+    if (kb + 1 < KB) {
+      load_x(kb + 1);
+      if (wave_on) load_w(kb + 1);
+    }
+    if (wave_on) {
+      const uint16_t* xb = lds + buf * kXBuf + (lane & 15) * kXStride + 8 * (lane >> 4);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+          const f16x8 xa = *(const f16x8*)(xb + mt * 16 * kXStride + 32 * s);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][i] = mfma16x16x32(xa, wf[i][s], acc[mt][i]);
+        }
+      }
+    }
+    if (kb + 1 < KB) store_x(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- low-rank term: (x V^T) U^T as extra K steps
+  if (wave_on && a.rp > 0) {
+    const int RW = a.n_w * a.rp;
+    const int rk = a.rank[f][e];
+    for (int s2 = 0; s2 < a.rp / 32; ++s2) {
+      const int j0 = 32 * s2 + 8 * (lane >> 4);
+      f16x8 ub[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = nt * kTileRows + 16 * i + (lane & 15);
+        ub[i] = j0 < rk ? *(const f16x8*)(a.U[f] + ((size_t)e * a.N + n) * a.max_rank + j0) : f16x8{};
+      }
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+        const int m = m0 + mt * 16 + (lane & 15);
+        const f16x8 ta = m < M ? *(const f16x8*)(a.T + (size_t)(base + m) * RW + f * a.rp + j0) : f16x8{};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = mfma16x16x32(ta, ub[i], acc[mt][i]);
+      }
+    }
+  }
+
+  // ---- epilogue
+  if (NW == 2) {
+    // waves with f == 1 (W3) hand their tile to the partner wave (wave - 1)
+    float* ex = (float*)lds + (wave >> 1) * (kBM * 64);
+    if (wave_on && f == 1) {
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            ex[(mt * 16 + 4 * (lane >> 4) + r) * 64 + 16 * i + (lane & 15)] = acc[mt][i][r];
+    }
+    __syncthreads();
+    if (!wave_on || f == 1) return;
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int mm = mt * 16 + 4 * (lane >> 4) + r;
+        if (m0 + mm >= M) continue;
+        uint16_t* yrow = (uint16_t*)a.y + (size_t)(base + m0 + mm) * a.N + nt * kTileRows;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * i + (lane & 15);
+          const float h3 = ex[mm * 64 + n];
+          yrow[n] = float_to_half_bits(silu(acc[mt][i][r]) * h3);
+        }
+      }
+    return;
+  }
+  if (!wave_on) return;
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mm = mt * 16 + 4 * (lane >> 4) + r;
+      if (m0 + mm >= M) continue;
+      const int i_pair = base + m0 + mm;
+      if (a.epilogue == MILO_EPI_ROUTE_SCALE) {
+        const int s = a.sorted_pairs[i_pair];
+        const float w = a.slot_w[s];
+        float* yrow = (float*)a.y + (size_t)s * a.N + nt * kTileRows;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yrow[16 * i + (lane & 15)] = acc[mt][i][r] * w;
+      } else {
+        uint16_t* yrow = (uint16_t*)a.y + (size_t)i_pair * a.N + nt * kTileRows;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yrow[16 * i + (lane & 15)] = float_to_half_bits(acc[mt][i][r]);
+      }
+    }
+}
+
+GemmArgs make_gemm_args(const milo_gemm_desc* d, const GemmPlan& p, char* ws);
+
+int32_t launch_gemm_prefill(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st) {
+  if (!p.pre_launch) return MILO_OK;
+  GemmArgs a = make_gemm_args(d, p, ws);
+  const size_t lds_bytes = 2 * kXBuf * sizeof(uint16_t);   // >= 2 x 128 x 64 fp32 for SWIGLU
+  if (d->n_w == 2) {
+    dim3 grid(p.pre_tiles, (p.n_tiles + 1) / 2);
+    hipLaunchKernelGGL(gemm_prefill_kernel<2>, grid, dim3(256), lds_bytes, st, a);
+  } else {
+    dim3 grid(p.pre_tiles, (p.n_tiles + 3) / 4);
+    hipLaunchKernelGGL(gemm_prefill_kernel<1>, grid, dim3(256), lds_bytes, st, a);
+  }
+  return hip_status(hipGetLastError(), "gemm_prefill_kernel launch");
+}
+
+}  // namespace milo

@@ -1,0 +1,122 @@
+// Internal declarations shared by the libmilo translation units (device
+// helpers, kernel launchers).  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/milo.h"
+
+namespace milo {
+
+// ---------------------------------------------------------------- types
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kTileRows = 64;      // rows (output features) per packed tile
+constexpr int kTileK = 128;        // input features per packed tile
+constexpr int kTileWords = 768;    // 3 planes x 64 lanes x 4 words
+constexpr int kTileSzWords = 128;  // 64 rows x 2 groups
+constexpr int kGroup = 64;
+constexpr int kMaxRank = 64;
+constexpr int kDecodeMaxRows = 64;  // largest expert row count of the small-M path
+constexpr int kMaxLrCounters = 2048;          // split-K counters of the low-rank pre-pass
+constexpr int kMaxDecCounters = 256 * 1024;   // (expert, n-tile) counters of the small-M kernel
+
+// Per-pair constant offsets of the "off + q" float16 encoding produced by the
+// code extraction (see dequant_triplet): pair pi of a triplet holds codes at
+// mantissa bits 4..6 (value 64 + q) or 7..9 (value 8 + q).
+__host__ __device__ constexpr int pair_offset(int pi) {
+  return (pi == 15) ? 64 : ((pi % 5 == 2 || pi % 5 == 4) ? 8 : 64);
+}
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b) {
+  return (a & mask) | b;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+__device__ __forceinline__ uint16_t float_to_half_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (_Float16)v);  // round to nearest even
+}
+
+// Extract the 16 code pairs of one layout-v1 triplet (words w0, w1, w2) into
+// float16x2 words holding (off + q_even, off + q_odd) with off = pair_offset.
+__device__ __forceinline__ void extract_triplet(uint32_t w0, uint32_t w1, uint32_t w2,
+                                                uint32_t out[16]) {
+  const uint32_t M64 = 0x54005400u;  // float16 64.0 in both halves
+  const uint32_t M8 = 0x48004800u;   // float16 8.0 in both halves
+  const uint32_t LO = 0x00700070u;   // bits 4..6 of each half
+  const uint32_t HI = 0x03800380u;   // bits 7..9 of each half
+  uint32_t w[3] = {w0, w1, w2};
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    uint32_t a = w[p];
+    uint32_t sh = a >> 6;
+    out[5 * p + 0] = and_or(a << 3, LO, M64);   // bits 1..3  -> 4..6
+    out[5 * p + 1] = and_or(a, LO, M64);        // bits 4..6
+    out[5 * p + 2] = and_or(a, HI, M8);         // bits 7..9
+    out[5 * p + 3] = and_or(sh, LO, M64);       // bits 10..12 -> 4..6
+    out[5 * p + 4] = and_or(sh, HI, M8);        // bits 13..15 -> 7..9
+  }
+  uint32_t s = and_or(w0 << 4, 0x00100010u, M64);
+  s = and_or(w1 << 5, 0x00200020u, s);
+  out[15] = and_or(w2 << 6, 0x00400040u, s);
+}
+
+// (off + q) -> (q - z) * s as float16, computed as fma(h, s, -(off + z) s) in
+// float32 and rounded once.
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t h, float s, float c) {
+  f16x2 v = __builtin_bit_cast(f16x2, h);
+  f16x2 r;
+  r[0] = (_Float16)__builtin_fmaf((float)v[0], s, c);
+  r[1] = (_Float16)__builtin_fmaf((float)v[1], s, c);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// ---------------------------------------------------------------- host side
+void set_error(const char* fmt, ...);
+int32_t hip_status(hipError_t e, const char* what);
+
+// launchers (return MILO_OK or MILO_ERR_HIP)
+int32_t launch_quantize(const float* W, int64_t rows, int64_t K, uint8_t* codes,
+                        uint16_t* scale, uint16_t* zero, hipStream_t st);
+int32_t launch_pack(const uint8_t* codes, const uint16_t* scale, const uint16_t* zero,
+                    int64_t rows, int64_t K, uint32_t* packed, uint32_t* sz, hipStream_t st);
+int32_t launch_route(const float* logits, int T, int E, int k, int S, int renorm,
+                     int32_t* ids, float* w, float* slot_w, int32_t* sorted_pairs,
+                     int32_t* pair_pos, int32_t* offsets, void* ws, hipStream_t st);
+int32_t launch_combine(const float* y, int T, int slots, int H, uint16_t* out, hipStream_t st);
+
+// Resolved plan of one grouped-GEMM call (host side).
+struct GemmPlan {
+  int n_tiles;       // N / 64
+  int kblocks;       // K / 128
+  int rp;            // compensator rank padded to 32 (0 = no compensator)
+  int lr_kchunks;    // split of K in the low-rank pre-pass
+  int lr_tiles;      // grid.x of the low-rank pre-pass (16-row tiles)
+  int dec_mt;        // 16-row m-tiles of the small-M kernel (0 = not launched)
+  int dec_max_rows;  // experts with at most this many rows use the small-M kernel
+  int dec_ksplit;    // split-K factor of the small-M kernel
+  int pre_launch;    // launch the tile kernel
+  int pre_tiles;     // grid.x bound of the tile kernel
+  // workspace carve-up (byte offsets)
+  size_t off_lr_cnt, off_dec_cnt, off_t, off_lr_part, off_dec_part, total;
+};
+int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p);
+int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st);
+int32_t launch_gemm_decode(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st);
+int32_t launch_gemm_prefill(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st);
+
+}  // namespace milo

@@ -1,0 +1,150 @@
+// Offline weight preparation on the GPU: RTN int3 quantization and the
+// layout-v1 repack.
+//
+// [talk] = "MiLo: Efficient Quantized MoE Inference with Mixture of Low-Rank
+// Compensators" (MLSys 2025 talk write-up).  Background: RTN is the simplest
+// calibration-free quantizer; MiLo Algorithm / Key Findings: int3 weights
+// with an asymmetric zero point; MiLo Kernel, "Bit Packing": 32 three-bit
+// values in three 32-bit words, no bit wasted.
+#include "milo_internal.hpp"
+
+namespace milo {
+
+// float64 -> float16 bits, round to nearest even, computed directly from the
+// double (a float32 intermediate would round twice).
+__device__ uint16_t f64_to_f16_rne(double x) {
+  uint64_t b = (uint64_t)__double_as_longlong(x);
+  uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+  int ex = (int)((b >> 52) & 0x7FF);
+  uint64_t mant = b & 0xFFFFFFFFFFFFFull;
+  if (ex == 0x7FF) return sign | 0x7C00u | (mant ? 0x200u : 0u);
+  int e = ex - 1023;
+  if (ex == 0) return sign;                  // float64 subnormals underflow
+  if (e > 15) return sign | 0x7C00u;
+  if (e >= -14) {                            // normal float16
+    uint64_t m = mant >> 42, rem = mant & ((1ull << 42) - 1), half = 1ull << 41;
+    uint32_t h = ((uint32_t)(e + 15) << 10) | (uint32_t)m;
+    if (rem > half || (rem == half && (m & 1))) h += 1;  // may carry into exponent
+    return (uint16_t)(sign | h);
+  }
+  if (e < -25) return sign;
+  uint64_t full = (1ull << 52) | mant;       // value = full * 2^(e-52)
+  int shift = 52 - (e + 24);                 // 43..53: in units of 2^-24
+  uint64_t q = full >> shift, rem = full & ((1ull << shift) - 1), half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (q & 1))) q += 1;
+  return (uint16_t)(sign | q);
+}
+
+__device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
+  return (double)(float)__builtin_bit_cast(_Float16, h);
+}
+
+// One wave per (row, group): lane = column inside the group.
+__global__ void __launch_bounds__(256) quantize_kernel(const float* __restrict__ W, int64_t rows,
+                                                       int64_t K, uint8_t* __restrict__ codes,
+                                                       uint16_t* __restrict__ scale,
+                                                       uint16_t* __restrict__ zero) {
+  const int lane = threadIdx.x & 63;
+  const int64_t groups = K / kGroup;
+  const int64_t total = rows * groups;
+  const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t gi = wave0; gi < total; gi += nwaves) {
+    const int64_t r = gi / groups, g = gi - r * groups;
+    const int64_t idx = r * K + g * kGroup + lane;
+    const float w = W[idx];
+    float lo = w, hi = w;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, o));
+      hi = fmaxf(hi, __shfl_xor(hi, o));
+    }
+    uint16_t sb = f64_to_f16_rne(((double)hi - (double)lo) / 7.0);
+    if ((sb & 0x7FFFu) == 0) sb = 0x3C00u;  // s == 0 -> 1
+    const double s = f16_bits_to_f64(sb);
+    double zr = -(double)lo / s;
+    zr = fmin(fmax(zr, -65504.0), 65504.0);
+    const uint16_t zb = f64_to_f16_rne(zr);
+    const double z = f16_bits_to_f64(zb);
+    double q = rint((double)w / s + z);
+    q = fmin(fmax(q, 0.0), 7.0);
+    codes[idx] = (uint8_t)q;
+    if (lane == 0) {
+      scale[r * groups + g] = sb;
+      zero[r * groups + g] = zb;
+    }
+  }
+}
+
+// One thread per triplet (tile, lane L, row group i).
+__global__ void __launch_bounds__(256) pack_kernel(const uint8_t* __restrict__ codes,
+                                                   const uint16_t* __restrict__ scale,
+                                                   const uint16_t* __restrict__ zero,
+                                                   int64_t rows, int64_t K,
+                                                   uint32_t* __restrict__ packed,
+                                                   uint32_t* __restrict__ sz) {
+  const int64_t kblocks = K / kTileK;
+  const int64_t ntrip = (rows / kTileRows) * kblocks * 256;
+  for (int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; tid < ntrip;
+       tid += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t tile = tid >> 8;
+    const int L = (int)((tid >> 2) & 63);
+    const int i = (int)(tid & 3);
+    const int64_t rt = tile / kblocks, kb = tile - rt * kblocks;
+    const int64_t r = rt * kTileRows + 16 * i + (L & 15);
+    const int kq = L >> 4;
+    uint32_t word[3] = {0u, 0u, 0u};
+    const uint8_t* rowp = codes + r * K + kb * kTileK + 8 * kq;
+#pragma unroll
+    for (int step = 0; step < 4; ++step) {
+      // codes c = 8 step + t, t = 0..7, at column 128 kb + 32 step + 8 kq + t
+      uint64_t eight = *(const uint64_t*)(rowp + 32 * step);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t q = (uint32_t)((eight >> (8 * t)) & 7u);
+        const int c = 8 * step + t, pi = c >> 1, h = c & 1;
+        if (pi < 15) {
+          word[pi / 5] |= q << (16 * h + 1 + 3 * (pi % 5));
+        } else {
+#pragma unroll
+          for (int b = 0; b < 3; ++b) word[b] |= ((q >> b) & 1u) << (16 * h);
+        }
+      }
+    }
+    uint32_t* tp = packed + tile * kTileWords + 4 * L + i;
+    tp[0] = word[0];
+    tp[256] = word[1];
+    tp[512] = word[2];
+    if (kq < 2) {  // lanes of K-quarters 0 and 1 write the row's two group words
+      const int64_t gg = 2 * kb + kq;
+      const int64_t groups = K / kGroup;
+      sz[tile * kTileSzWords + 8 * (L & 15) + 2 * i + kq] =
+          (uint32_t)scale[r * groups + gg] | ((uint32_t)zero[r * groups + gg] << 16);
+    }
+  }
+}
+
+static int grid_for(int64_t work, int per_block) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+int32_t launch_quantize(const float* W, int64_t rows, int64_t K, uint8_t* codes,
+                        uint16_t* scale, uint16_t* zero, hipStream_t st) {
+  const int64_t waves = rows * (K / kGroup);
+  hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(waves, 4)), dim3(256), 0, st, W, rows, K,
+                     codes, scale, zero);
+  return hip_status(hipGetLastError(), "quantize_kernel launch");
+}
+
+int32_t launch_pack(const uint8_t* codes, const uint16_t* scale, const uint16_t* zero,
+                    int64_t rows, int64_t K, uint32_t* packed, uint32_t* sz, hipStream_t st) {
+  const int64_t ntrip = (rows / kTileRows) * (K / kTileK) * 256;
+  hipLaunchKernelGGL(pack_kernel, dim3(grid_for(ntrip, 256)), dim3(256), 0, st, codes, scale,
+                     zero, rows, K, packed, sz);
+  return hip_status(hipGetLastError(), "pack_kernel launch");
+}
+
+}  // namespace milo

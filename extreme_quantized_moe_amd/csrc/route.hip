@@ -1,0 +1,187 @@
+// Softmax top-k routing and the stable expert sort of (token, slot) pairs.
+//
+// [talk] = "MiLo: Efficient Quantized MoE Inference with Mixture of Low-Rank
+// Compensators" (MLSys 2025 talk write-up), Background: an MoE layer activates
+// only a subset of its experts per token.  The router itself is not given on
+// the pages; this is the usual softmax top-k (ties -> lower expert id).
+//
+// Three phases, each deterministic:
+//   1. route_topk  (one thread per token, 256 tokens per block): top-k,
+//      weights, and per-block stable ranks of each slot among the slots of the
+//      same expert, from an LDS bitmap [expert][token-in-block].
+//   2. route_scan  (one block): per expert, exclusive prefix of the block
+//      counts; exclusive prefix over experts -> offsets.
+//   3. route_scatter: final positions.
+// With a single token block, phase 1 does all three (one launch).
+#include "milo_internal.hpp"
+
+namespace milo {
+
+constexpr int kRouteBlock = 256;
+constexpr int kMaxExperts = 256;
+constexpr int kBitWords = kRouteBlock / 32;
+
+__device__ __forceinline__ int slot_expert(const int32_t* ids_row, int j, int k, int E) {
+  return j < k ? ids_row[j] : E + (j - k);
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim == 256).
+__device__ int block_exclusive_scan(int v, int* lds, int* total) {
+  const int tid = threadIdx.x;
+  lds[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kRouteBlock; off <<= 1) {
+    int add = tid >= off ? lds[tid - off] : 0;
+    __syncthreads();
+    lds[tid] += add;
+    __syncthreads();
+  }
+  const int incl = lds[tid];
+  *total = lds[kRouteBlock - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ void __launch_bounds__(kRouteBlock)
+route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int renorm,
+           int32_t* __restrict__ ids, float* __restrict__ topw, float* __restrict__ slot_w,
+           int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
+           int32_t* __restrict__ offsets, int32_t* __restrict__ block_counts) {
+  __shared__ uint32_t bits[kMaxExperts][kBitWords];
+  __shared__ int scan_lds[kRouteBlock];
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x * kRouteBlock + tid;
+  const int ET = E + S, slots = k + S;
+  for (int x = tid; x < kMaxExperts * kBitWords; x += kRouteBlock) (&bits[0][0])[x] = 0u;
+  __syncthreads();
+
+  int my_ids[16];
+  if (t < T) {
+    const float* row = logits + (size_t)t * E;
+    uint32_t taken[kMaxExperts / 32];
+#pragma unroll
+    for (int x = 0; x < kMaxExperts / 32; ++x) taken[x] = 0u;
+    float mx = row[0];
+    for (int e = 1; e < E; ++e) mx = fmaxf(mx, row[e]);
+    float den = 0.f;
+    for (int e = 0; e < E; ++e) den += expf(row[e] - mx);
+    float sel[8];
+    float selsum = 0.f;
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      float bv = 0.f;
+      for (int e = 0; e < E; ++e) {
+        if ((taken[e >> 5] >> (e & 31)) & 1u) continue;
+        const float v = row[e];
+        if (best < 0 || v > bv) { best = e; bv = v; }
+      }
+      taken[best >> 5] |= 1u << (best & 31);
+      my_ids[j] = best;
+      sel[j] = expf(bv - mx);
+      selsum += sel[j];
+    }
+    for (int j = 0; j < k; ++j) {
+      const float w = renorm ? sel[j] / selsum : sel[j] / den;
+      ids[(size_t)t * k + j] = my_ids[j];
+      topw[(size_t)t * k + j] = w;
+      slot_w[(size_t)t * slots + j] = w;
+    }
+    for (int j = k; j < slots; ++j) {
+      my_ids[j] = E + (j - k);
+      slot_w[(size_t)t * slots + j] = 1.0f;
+    }
+    for (int j = 0; j < slots; ++j)
+      atomicOr(&bits[my_ids[j]][tid >> 5], 1u << (tid & 31));
+  }
+  __syncthreads();
+
+  // stable rank of each slot among earlier tokens of this block with the same expert
+  int rank[16];
+  if (t < T) {
+    for (int j = 0; j < slots; ++j) {
+      const uint32_t* row = bits[my_ids[j]];
+      int c = 0;
+      for (int w = 0; w < (tid >> 5); ++w) c += __popc(row[w]);
+      c += __popc(row[tid >> 5] & ((1u << (tid & 31)) - 1u));
+      rank[j] = c;
+    }
+  }
+  int count = 0;
+  if (tid < ET) {
+    for (int w = 0; w < kBitWords; ++w) count += __popc(bits[tid][w]);
+  }
+  if (gridDim.x == 1) {
+    int total;
+    const int off = block_exclusive_scan(tid < ET ? count : 0, scan_lds, &total);
+    // scan_lds is free again; keep each expert's offset in it
+    if (tid < ET) scan_lds[tid] = off;
+    if (tid == 0) offsets[ET] = total;
+    __syncthreads();
+    if (tid < ET) offsets[tid] = scan_lds[tid];
+    if (t < T) {
+      for (int j = 0; j < slots; ++j) {
+        const int s = t * slots + j;
+        const int pos = scan_lds[my_ids[j]] + rank[j];
+        sorted_pairs[pos] = s;
+        pair_pos[s] = pos;
+      }
+    }
+  } else {
+    if (tid < ET) block_counts[(size_t)blockIdx.x * ET + tid] = count;
+    if (t < T)
+      for (int j = 0; j < slots; ++j) pair_pos[t * slots + j] = rank[j];
+  }
+}
+
+__global__ void __launch_bounds__(kRouteBlock)
+route_scan(int nblocks, int ET, int32_t* __restrict__ block_counts, int32_t* __restrict__ offsets) {
+  __shared__ int scan_lds[kRouteBlock];
+  const int tid = threadIdx.x;
+  int run = 0;
+  if (tid < ET) {
+    for (int b = 0; b < nblocks; ++b) {
+      const int c = block_counts[(size_t)b * ET + tid];
+      block_counts[(size_t)b * ET + tid] = run;   // becomes the block's base
+      run += c;
+    }
+  }
+  int total;
+  const int off = block_exclusive_scan(tid < ET ? run : 0, scan_lds, &total);
+  if (tid < ET) offsets[tid] = off;
+  if (tid == 0) offsets[ET] = total;
+}
+
+__global__ void __launch_bounds__(kRouteBlock)
+route_scatter(int T, int E, int k, int S, const int32_t* __restrict__ ids,
+              const int32_t* __restrict__ block_base, const int32_t* __restrict__ offsets,
+              int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos) {
+  const int t = blockIdx.x * kRouteBlock + threadIdx.x;
+  if (t >= T) return;
+  const int ET = E + S, slots = k + S;
+  for (int j = 0; j < slots; ++j) {
+    const int e = slot_expert(ids + (size_t)t * k, j, k, E);
+    const int s = t * slots + j;
+    const int pos = offsets[e] + block_base[(size_t)blockIdx.x * ET + e] + pair_pos[s];
+    sorted_pairs[pos] = s;
+    pair_pos[s] = pos;
+  }
+}
+
+int32_t launch_route(const float* logits, int T, int E, int k, int S, int renorm,
+                     int32_t* ids, float* w, float* slot_w, int32_t* sorted_pairs,
+                     int32_t* pair_pos, int32_t* offsets, void* ws, hipStream_t st) {
+  const int nblocks = (T + kRouteBlock - 1) / kRouteBlock;
+  int32_t* counts = (int32_t*)ws;
+  hipLaunchKernelGGL(route_topk, dim3(nblocks), dim3(kRouteBlock), 0, st, logits, T, E, k, S,
+                     renorm, ids, w, slot_w, sorted_pairs, pair_pos, offsets, counts);
+  int32_t rc = hip_status(hipGetLastError(), "route_topk launch");
+  if (rc != MILO_OK || nblocks == 1) return rc;
+  hipLaunchKernelGGL(route_scan, dim3(1), dim3(kRouteBlock), 0, st, nblocks, E + S, counts, offsets);
+  rc = hip_status(hipGetLastError(), "route_scan launch");
+  if (rc != MILO_OK) return rc;
+  hipLaunchKernelGGL(route_scatter, dim3(nblocks), dim3(kRouteBlock), 0, st, T, E, k, S, ids,
+                     counts, offsets, sorted_pairs, pair_pos);
+  return hip_status(hipGetLastError(), "route_scatter launch");
+}
+
+}  // namespace milo

@@ -1,0 +1,237 @@
+"""Thin torch-facing binding of libmilo (same call names as include/milo.h
+without the `milo_` prefix).  torch supplies device memory and the current
+stream; every computation runs in the library's HIP kernels.  There is no
+fallback: if libmilo.so is missing, importing the binding raises."""
+import ctypes as C
+
+import torch
+
+from . import _lib as L
+from ._lib import check
+
+_DEV_CHECKED = set()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("libmilo needs contiguous CUDA (HIP) tensors")
+
+
+def packed_words(rows, K):
+    return int(L.lib().milo_packed_words(rows, K))
+
+
+def sz_words(rows, K):
+    return int(L.lib().milo_sz_words(rows, K))
+
+
+def quantize_rtn_int3(W):
+    """fp32 [rows][K] -> (codes u8 [rows][K], scale fp16 [rows][K/64], zero fp16)."""
+    W = W.contiguous()
+    _cuda(W)
+    rows, K = W.shape
+    codes = torch.empty((rows, K), dtype=torch.uint8, device=W.device)
+    scale = torch.empty((rows, K // 64), dtype=torch.float16, device=W.device)
+    zero = torch.empty_like(scale)
+    check("milo_quantize_rtn_int3", L.lib().milo_quantize_rtn_int3(
+        _p(W), rows, K, _p(codes), _p(scale), _p(zero), _stream()))
+    return codes, scale, zero
+
+
+def pack_int3(codes, scale, zero):
+    """codes u8 [rows][K], scale/zero fp16 [rows][K/64] -> (packed int32 words,
+    tiled scale/zero int32 words) in layout v1 (bit patterns in int32)."""
+    _cuda(codes, scale, zero)
+    rows, K = codes.shape
+    packed = torch.empty(packed_words(rows, K), dtype=torch.int32, device=codes.device)
+    sz = torch.empty(sz_words(rows, K), dtype=torch.int32, device=codes.device)
+    check("milo_pack_int3", L.lib().milo_pack_int3(
+        _p(codes), _p(scale), _p(zero), rows, K, _p(packed), _p(sz), _stream()))
+    return packed, sz
+
+
+_route_ws = {}
+
+
+def route_sort(logits, k, S=0, renormalize=True):
+    """Softmax top-k routing + expert sort.  Returns dict of device tensors:
+    ids [T][k], w [T][k], slot_w [T*(k+S)], sorted_pairs, pair_pos [T*(k+S)],
+    offsets [E+S+1]."""
+    logits = logits.contiguous()
+    _cuda(logits)
+    T, E = logits.shape
+    slots = k + S
+    dev = logits.device
+    out = {
+        "ids": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "w": torch.empty((T, k), dtype=torch.float32, device=dev),
+        "slot_w": torch.empty(T * slots, dtype=torch.float32, device=dev),
+        "sorted_pairs": torch.empty(T * slots, dtype=torch.int32, device=dev),
+        "pair_pos": torch.empty(T * slots, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + S + 1, dtype=torch.int32, device=dev),
+    }
+    nbytes = int(L.lib().milo_route_workspace_bytes(T, E, k, S))
+    ws = None
+    if nbytes:
+        key = (dev.index, nbytes)
+        ws = _route_ws.get(key)
+        if ws is None:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            _route_ws[key] = ws
+    check("milo_route_sort", L.lib().milo_route_sort(
+        _p(logits), T, E, k, S, 1 if renormalize else 0, _p(out["ids"]), _p(out["w"]),
+        _p(out["slot_w"]), _p(out["sorted_pairs"]), _p(out["pair_pos"]), _p(out["offsets"]),
+        _p(ws), nbytes, _stream()))
+    return out
+
+
+class Family:
+    """One projection family (e.g. every expert's W1) in the library's format:
+    packed int3 codes (layout v1), tiled scale/zero, compensator factors
+    U [E][N][max_rank] and V [E][max_rank][K] (fp16, zero beyond each expert's
+    rank) and the device rank array."""
+
+    def __init__(self, packed, sz, U, V, rank, num_experts, N, K, max_rank):
+        self.packed, self.sz, self.U, self.V, self.rank = packed, sz, U, V, rank
+        self.num_experts, self.N, self.K, self.max_rank = num_experts, N, K, max_rank
+
+    @staticmethod
+    def from_dense(Ws, As, Bs, max_rank=None, device="cuda"):
+        """Ws: list of fp32 [N][K]; As: list of fp16 [K][r_e]; Bs: fp16 [r_e][N]
+        (the compensator as X A B, i.e. V = A^T, U = B^T).  Quantizes each W on
+        the GPU (RTN int3, group 64) and packs all experts in one call."""
+        E = len(Ws)
+        N, K = Ws[0].shape
+        ranks = [int(a.shape[1]) for a in As]
+        R = max(ranks) if max_rank is None else max_rank
+        codes = torch.empty((E * N, K), dtype=torch.uint8, device=device)
+        scale = torch.empty((E * N, K // 64), dtype=torch.float16, device=device)
+        zero = torch.empty_like(scale)
+        for e, W in enumerate(Ws):
+            c, s, z = quantize_rtn_int3(W.to(device=device, dtype=torch.float32))
+            codes[e * N:(e + 1) * N] = c
+            scale[e * N:(e + 1) * N] = s
+            zero[e * N:(e + 1) * N] = z
+        packed, sz = pack_int3(codes, scale, zero)
+        U = torch.zeros((E, N, max(R, 1)), dtype=torch.float16, device=device)
+        V = torch.zeros((E, max(R, 1), K), dtype=torch.float16, device=device)
+        for e in range(E):
+            r = ranks[e]
+            if r:
+                U[e, :, :r] = Bs[e].to(device).t()
+                V[e, :r, :] = As[e].to(device).t()
+        rank = torch.tensor(ranks, dtype=torch.int32, device=device)
+        return Family(packed, sz, U, V, rank, E, N, K, R)
+
+    def weights_struct(self):
+        w = L.MiloWeights()
+        w.packed = self.packed.data_ptr()
+        w.sz = self.sz.data_ptr()
+        w.U = self.U.data_ptr()
+        w.V = self.V.data_ptr()
+        w.rank = self.rank.data_ptr()
+        return w
+
+    def nbytes(self):
+        return {"packed": self.packed.numel() * 4, "sz": self.sz.numel() * 4,
+                "U": self.U.numel() * 2, "V": self.V.numel() * 2}
+
+
+_gemm_ws = {}
+
+
+def _workspace(dev, nbytes):
+    """A zero-filled workspace per device, grown on demand (the library leaves
+    its counters at zero after every call)."""
+    key = dev.index
+    ws = _gemm_ws.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _gemm_ws[key] = ws
+    return ws
+
+
+def make_gemm_desc(families, x, offsets, num_pairs, epilogue, y, sorted_pairs=None,
+                   gather_div=0, slot_w=None, y_rows=0, max_rows_per_expert=0,
+                   path=L.PATH_AUTO):
+    f0 = families[0]
+    d = L.MiloGemmDesc()
+    d.num_experts, d.N, d.K, d.max_rank = f0.num_experts, f0.N, f0.K, f0.max_rank
+    d.n_w = len(families)
+    for i, f in enumerate(families):
+        d.w[i] = f.weights_struct()
+    d.x = x.data_ptr()
+    d.x_rows = x.shape[0]
+    d.gather_div = gather_div
+    d.sorted_pairs = None if sorted_pairs is None else sorted_pairs.data_ptr()
+    d.offsets = offsets.data_ptr()
+    d.num_pairs = num_pairs
+    d.max_rows_per_expert = max_rows_per_expert
+    d.slot_w = None if slot_w is None else slot_w.data_ptr()
+    d.y_rows = y_rows
+    d.epilogue = epilogue
+    d.y = y.data_ptr()
+    d.path = path
+    return d
+
+
+def moe_w3a16_lowrank_gemm(families, x, offsets, num_pairs, epilogue, y, sorted_pairs=None,
+                           gather_div=0, slot_w=None, y_rows=0, max_rows_per_expert=0,
+                           path=L.PATH_AUTO, workspace=None):
+    """Routed W3A16 + low-rank grouped GEMM (see include/milo.h).  Writes y."""
+    _cuda(x, offsets, y, sorted_pairs, slot_w)
+    d = make_gemm_desc(families, x, offsets, num_pairs, epilogue, y, sorted_pairs, gather_div,
+                       slot_w, y_rows, max_rows_per_expert, path)
+    nbytes = int(L.lib().milo_moe_gemm_workspace_bytes(C.byref(d)))
+    ws = workspace if workspace is not None else _workspace(x.device, nbytes)
+    check("milo_moe_w3a16_lowrank_gemm", L.lib().milo_moe_w3a16_lowrank_gemm(
+        C.byref(d), _p(ws) if nbytes else None, ws.numel() if nbytes else 0, _stream()))
+    return y
+
+
+def moe_combine(y, T, slots, out=None):
+    """fp32 [T*slots][H] -> fp16 [T][H]: sum of each token's slots in order."""
+    _cuda(y)
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float16, device=y.device)
+    check("milo_moe_combine", L.lib().milo_moe_combine(_p(y), T, slots, H, _p(out), _stream()))
+    return out
+
+
+class MoELayer:
+    """A routed SwiGLU MoE FFN with int3 + low-rank experts:
+    route -> fused gate/up GEMM + SwiGLU -> fused down GEMM + route scale ->
+    combine (four library calls)."""
+
+    def __init__(self, w1, w3, w2, E, k, S=0, renormalize=True):
+        self.w1, self.w3, self.w2 = w1, w3, w2
+        self.E, self.k, self.S, self.renormalize = E, k, S, renormalize
+        self.H, self.F = w2.N, w1.N
+
+    def forward(self, x, logits, path=L.PATH_AUTO, return_all=False):
+        T = x.shape[0]
+        slots = self.k + self.S
+        P = T * slots
+        r = route_sort(logits, self.k, self.S, self.renormalize)
+        G = torch.empty((P, self.F), dtype=torch.float16, device=x.device)
+        moe_w3a16_lowrank_gemm((self.w1, self.w3), x, r["offsets"], P, L.EPI_SWIGLU, G,
+                               sorted_pairs=r["sorted_pairs"], gather_div=slots,
+                               max_rows_per_expert=T, path=path)
+        Y = torch.empty((P, self.H), dtype=torch.float32, device=x.device)
+        moe_w3a16_lowrank_gemm((self.w2,), G, r["offsets"], P, L.EPI_ROUTE_SCALE, Y,
+                               sorted_pairs=r["sorted_pairs"], gather_div=0,
+                               slot_w=r["slot_w"], y_rows=P, max_rows_per_expert=T, path=path)
+        out = moe_combine(Y, T, slots)
+        if return_all:
+            return out, {"route": r, "G": G, "Y": Y}
+        return out

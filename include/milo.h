@@ -1,0 +1,251 @@
+/*
+ * milo.h -- C ABI of libmilo, an MI355X (gfx950) implementation of the MiLo
+ * W3A16 + low-rank-compensated MoE expert GEMM.
+ *
+ * Sources ("the pages"):
+ *   [talk] "MiLo: Efficient Quantized MoE Inference with Mixture of Low-Rank
+ *          Compensators", write-up of the MLSys 2025 talk: sections Background,
+ *          Technical Deep Dive (MiLo Algorithm, MiLo Kernel), Experimental
+ *          Setup & Results.
+ *   [abs]  the arXiv abstract of the same paper (2504.02658).
+ *
+ * General rules for every entry point:
+ *   - All tensor pointers are DEVICE pointers to caller-owned memory (the
+ *     library never allocates or frees).  Scalars and descriptor structs are
+ *     host values.  `stream` is a hipStream_t (NULL = default stream).
+ *   - Calls are asynchronous: they enqueue kernels on `stream` and return.
+ *     No entry point synchronises the host with the device.
+ *   - Every shape, pointer, alignment and workspace check runs on the host
+ *     before anything is enqueued; on an error nothing is enqueued and the
+ *     return value is a nonzero milo_status.  Launch failures return
+ *     MILO_ERR_HIP.  Details of the last error of the calling thread are in
+ *     milo_last_error().  Device faults surface at the caller's next
+ *     synchronisation, as with any HIP kernel.
+ *   - float16 values are passed as uint16_t bit patterns (IEEE binary16).
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     (no floating-point atomics; fixed reduction orders).
+ */
+#ifndef MILO_H
+#define MILO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MILO_ABI_VERSION 1
+#define MILO_LAYOUT_VERSION 1
+
+typedef enum milo_status {
+  MILO_OK = 0,
+  MILO_ERR_NULL = 1,       /* a required pointer is NULL                   */
+  MILO_ERR_SHAPE = 2,      /* a size violates the documented constraints   */
+  MILO_ERR_ALIGN = 3,      /* a pointer is not aligned as documented       */
+  MILO_ERR_RANK = 4,       /* compensator rank outside the supported range */
+  MILO_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required   */
+  MILO_ERR_ARG = 6,        /* an enum or flag argument has no meaning      */
+  MILO_ERR_HIP = 7         /* a HIP runtime call or launch failed          */
+} milo_status;
+
+int32_t milo_abi_version(void);      /* MILO_ABI_VERSION    */
+int32_t milo_layout_version(void);   /* MILO_LAYOUT_VERSION */
+/* Static description of a status code (never NULL). */
+const char* milo_status_string(int32_t status);
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* milo_last_error(void);
+
+/* ======================================================================
+ * Offline weight preparation (not on the timed path)
+ * ====================================================================== */
+
+/*
+ * Group-wise asymmetric int3 round-to-nearest quantization.
+ * [talk] Background names RTN as the simplest calibration-free quantizer;
+ * MiLo Algorithm / Key Findings describe int3 weights with an asymmetric
+ * zero point.  Per row and group of 64 consecutive columns, in float64:
+ *     lo, hi = min, max;   s = f16_rne((hi - lo) / 7), s = 1 if that is 0;
+ *     z = f16_rne(clamp(-lo / s, -65504, 65504));
+ *     q = clamp(rint(w / s + z), 0, 7)    (round half to even)
+ * and the weight is represented as (q - z) * s.
+ *
+ * W      : float32 [rows][K], row-major.
+ * codes  : out, uint8 [rows][K] (values 0..7).
+ * scale  : out, float16 bits [rows][K/64].
+ * zero   : out, float16 bits [rows][K/64].
+ * Constraints: rows >= 1, K >= 64, K % 64 == 0.  W must be finite.
+ */
+int32_t milo_quantize_rtn_int3(const float* W, int64_t rows, int64_t K,
+                               uint8_t* codes, uint16_t* scale, uint16_t* zero,
+                               void* stream);
+
+/* Number of uint32 words of the packed codes of a rows x K matrix: 3*rows*K/32. */
+int64_t milo_packed_words(int64_t rows, int64_t K);
+/* Number of uint32 words of the tiled scale/zero of a rows x K matrix: rows*K/64. */
+int64_t milo_sz_words(int64_t rows, int64_t K);
+
+/*
+ * Repack int3 codes into packed layout v1 and tile the scale/zero pairs.
+ * [talk] MiLo Kernel, "Bit Packing": 32 three-bit values are stored in three
+ * 32-bit words without wasting a bit.  Layout v1 keeps that density with its
+ * own bit assignment:
+ *   Tile (rt, kb) = rows [64 rt, 64 rt + 64) x columns [128 kb, 128 kb + 128),
+ *   tile index t = rt * (K/128) + kb, 768 words at packed[768 t ...].
+ *   Word 256 p + 4 L + i of a tile (plane p = 0..2, lane L = 0..63, row group
+ *   i = 0..3) is word p of the triplet holding row 64 rt + 16 i + (L mod 16),
+ *   codes c = 0..31 at column 128 kb + 32 (c div 8) + 8 (L div 16) + (c mod 8).
+ *   Code c = 2 pi + h (pair pi, half h): for pi < 15 it occupies bits
+ *   [16 h + 1 + 3 (pi mod 5), +3) of word pi div 5; for pi = 15 bit b of the
+ *   code is bit 16 h of word b.
+ *   Scale/zero: sz[128 t + 8 (r mod 16) + 2 ((r mod 64) div 16) + (g mod 2)] =
+ *   scale_bits | zero_bits << 16 for row r, group g (t from r and g div 2).
+ * A batch of experts with equal shapes is packed in one call by stacking
+ * them as rows (expert e's rows start at e*N; N % 64 == 0 keeps tiles inside
+ * one expert), giving expert e's packed words at e * milo_packed_words(N, K).
+ *
+ * codes  : uint8 [rows][K], only the low 3 bits are used.
+ * scale, zero : float16 bits [rows][K/64].
+ * packed : out, uint32 [milo_packed_words(rows, K)], 16-byte aligned.
+ * sz     : out, uint32 [milo_sz_words(rows, K)], 16-byte aligned.
+ * Constraints: rows % 64 == 0, K % 128 == 0, rows, K > 0.
+ */
+int32_t milo_pack_int3(const uint8_t* codes, const uint16_t* scale,
+                       const uint16_t* zero, int64_t rows, int64_t K,
+                       uint32_t* packed, uint32_t* sz, void* stream);
+
+/* ======================================================================
+ * Routing
+ * ====================================================================== */
+
+/* Workspace bytes milo_route_sort needs for these sizes (may be 0). */
+size_t milo_route_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t S);
+
+/*
+ * Softmax top-k routing and the expert-sorted (token, slot) pair list.
+ * [talk] Background: each token activates only a subset of the experts.
+ * For token t: the k largest logits (ties -> lower expert id), ordered by
+ * decreasing logit; p = softmax(logits[t]) in float32; routed weight
+ * w = p_j / sum over the k picks (renormalize != 0) or p_j (renormalize == 0).
+ * Slot j of token t has slot index s = t*(k+S) + j; slots j >= k are the S
+ * shared experts E + (j - k) with weight 1.  Pairs are sorted by
+ * (expert, s).
+ *
+ * logits      : float32 [T][E], finite.
+ * topk_ids    : out, int32 [T][k].
+ * topk_w      : out, float32 [T][k].
+ * slot_w      : out, float32 [T*(k+S)]   weight of each slot.
+ * sorted_pairs: out, int32 [T*(k+S)]     slot indices in (expert, s) order.
+ * pair_pos    : out, int32 [T*(k+S)]     inverse: pair_pos[sorted_pairs[i]] = i.
+ * offsets     : out, int32 [E+S+1]       offsets[e] = #pairs with expert < e.
+ * workspace   : milo_route_workspace_bytes(T,E,k,S) bytes (NULL if 0).
+ * Constraints: 1 <= T <= 65536, 1 <= k <= min(E, 8), E + S <= 256,
+ *              k + S <= 16.  All outputs 4-byte aligned.
+ */
+int32_t milo_route_sort(const float* logits, int32_t T, int32_t E, int32_t k,
+                        int32_t S, int32_t renormalize, int32_t* topk_ids,
+                        float* topk_w, float* slot_w, int32_t* sorted_pairs,
+                        int32_t* pair_pos, int32_t* offsets, void* workspace,
+                        size_t ws_bytes, void* stream);
+
+/* ======================================================================
+ * Routed W3A16 + low-rank grouped GEMM
+ * ====================================================================== */
+
+/*
+ * One projection family (e.g. all experts' W1) of num_experts experts, each an
+ * N x K matrix (output x input), stored as:
+ *   packed : layout v1 codes, expert e at packed + e * milo_packed_words(N, K).
+ *   sz     : tiled scale/zero, expert e at sz + e * milo_sz_words(N, K).
+ *   U      : float16 [num_experts][N][max_rank]  the compensator factor U of
+ *            [talk] MiLo Algorithm (W_out = W_quant + U V, U is out x R).
+ *   V      : float16 [num_experts][max_rank][K]  the factor V (R x in).
+ *   rank   : DEVICE int32 [num_experts], 0 <= rank[e] <= max_rank,
+ *            rank[e] % 8 == 0.  Columns of U and rows of V at or beyond
+ *            rank[e] are never read.
+ * U and V may be NULL when max_rank == 0.
+ */
+typedef struct milo_weights {
+  const uint32_t* packed;
+  const uint32_t* sz;
+  const uint16_t* U;
+  const uint16_t* V;
+  const int32_t* rank;
+} milo_weights;
+
+enum {
+  MILO_EPI_NONE = 0,        /* y fp16 [num_pairs][N]: Y in pair order        */
+  MILO_EPI_SWIGLU = 1,      /* y fp16 [num_pairs][N]: silu(Y_w0) * Y_w1      */
+  MILO_EPI_ROUTE_SCALE = 2  /* y fp32 [y_rows][N]: row sorted_pairs[i] gets
+                               Y_i * slot_w[sorted_pairs[i]]                */
+};
+enum { MILO_PATH_AUTO = 0, MILO_PATH_DECODE = 1, MILO_PATH_PREFILL = 2 };
+
+typedef struct milo_gemm_desc {
+  int32_t num_experts;          /* experts in the weight arrays (E + S)       */
+  int32_t N, K;                 /* output and input features of each expert   */
+  int32_t max_rank;             /* 0..64, multiple of 8                       */
+  int32_t n_w;                  /* 1, or 2 for MILO_EPI_SWIGLU (w[0]=gate W1,
+                                   w[1]=up W3)                                 */
+  milo_weights w[2];
+  const uint16_t* x;            /* fp16 [x_rows][K]                           */
+  int32_t x_rows;
+  int32_t gather_div;           /* >0: pair i reads x row sorted_pairs[i] /
+                                   gather_div; 0: pair i reads x row i        */
+  const int32_t* sorted_pairs;  /* int32 [num_pairs] (may be NULL if
+                                   gather_div == 0 and epilogue != ROUTE_SCALE) */
+  const int32_t* offsets;       /* int32 [num_experts + 1], expert e owns pairs
+                                   [offsets[e], offsets[e+1])                  */
+  int32_t num_pairs;            /* P = offsets[num_experts]                    */
+  int32_t max_rows_per_expert;  /* host upper bound on offsets[e+1]-offsets[e]
+                                   (e.g. T for top-k routing); 0 = num_pairs  */
+  const float* slot_w;          /* ROUTE_SCALE only: float32 [y_rows]          */
+  int32_t y_rows;               /* ROUTE_SCALE only: rows of y                 */
+  int32_t epilogue;             /* MILO_EPI_*                                  */
+  void* y;                      /* output, see MILO_EPI_*                      */
+  int32_t path;                 /* MILO_PATH_*                                 */
+} milo_gemm_desc;
+
+/* Workspace bytes milo_moe_w3a16_lowrank_gemm needs for this descriptor. */
+size_t milo_moe_gemm_workspace_bytes(const milo_gemm_desc* desc);
+
+/*
+ * The fused routed grouped GEMM.  For every pair i of expert e (rows of x
+ * gathered through sorted_pairs when gather_div > 0), and each weight family w:
+ *     Y_w[i] = x_i . deq(W_w,e)^T + (x_i . V_w,e^T) . U_w,e^T
+ * [talk] MiLo Algorithm (W_out = W_quant + U V) and MiLo Kernel (int3 x fp16
+ * GEMM with dequantization fused into the kernel), with deq(q) = (q - z) * s
+ * per 64-column group, fp16 activations and fp32 accumulation.  Then the
+ * epilogue: NONE stores Y_0 as fp16; SWIGLU stores silu(Y_0) * Y_1 as fp16
+ * (silu(u) = u / (1 + exp(-u))); ROUTE_SCALE stores Y_0 * slot_w[s] as fp32
+ * into row s = sorted_pairs[i] (rows of y that no pair maps to are not
+ * written).  The path (small-M streaming kernel or matrix-core tile kernel)
+ * is chosen per expert from its row count on the device unless forced.
+ *
+ * workspace: milo_moe_gemm_workspace_bytes(desc) bytes, 256-byte aligned.
+ *   It MUST be zero-filled before its first use; every call leaves its
+ *   synchronisation counters at zero again.  Two calls that overlap in time
+ *   must not share a workspace.
+ * Constraints: N % 64 == 0, K % 128 == 0, N, K <= 65536, 1 <= num_experts
+ *   <= 256, num_pairs <= 1048576, x/y/U/V 16-byte aligned; for SWIGLU both
+ *   families have the same N, K, max_rank.
+ */
+int32_t milo_moe_w3a16_lowrank_gemm(const milo_gemm_desc* desc,
+                                    void* workspace, size_t ws_bytes,
+                                    void* stream);
+
+/*
+ * Weighted combine: out[t][h] = sum over j = 0..slots-1, in that order, of
+ * y[t*slots + j][h] (fp32 adds), rounded to fp16 (nearest even).  y already
+ * holds the route-weighted slot outputs (MILO_EPI_ROUTE_SCALE).
+ * [talk] Background: a token's output is the combination of the outputs of
+ * the experts it activates.
+ * y   : float32 [T*slots][H];  out : fp16 [T][H].  H % 4 == 0, 16-byte aligned.
+ */
+int32_t milo_moe_combine(const float* y, int32_t T, int32_t slots, int32_t H,
+                         uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MILO_H */

@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/milo.h declares, and rejects bad arguments before
+touching the device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "milo.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from extreme_quantized_moe_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(milo_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_versions_and_strings(L):
+    lib = L.lib()
+    assert lib.milo_abi_version() == 1
+    assert lib.milo_layout_version() == 1
+    for s in range(8):
+        assert len(lib.milo_status_string(s)) > 0
+    assert lib.milo_packed_words(64, 128) == 768
+    assert lib.milo_sz_words(64, 128) == 128
+
+
+def test_pack_rejects_before_launch(L):
+    lib = L.lib()
+    fake = C.c_void_p(0x1000)   # never dereferenced: validation fails first
+    assert lib.milo_pack_int3(None, fake, fake, 64, 128, fake, fake, None) == 1
+    assert lib.milo_pack_int3(fake, fake, fake, 32, 128, fake, fake, None) == 2
+    assert lib.milo_pack_int3(fake, fake, fake, 64, 96, fake, fake, None) == 2
+    assert lib.milo_pack_int3(C.c_void_p(0x1001), fake, fake, 64, 128, fake, fake, None) == 3
+    assert b"rows" in lib.milo_last_error() or b"aligned" in lib.milo_last_error()
+
+
+def test_quantize_rejects(L):
+    lib = L.lib()
+    fake = C.c_void_p(0x1000)
+    assert lib.milo_quantize_rtn_int3(fake, 4, 100, fake, fake, fake, None) == 2
+    assert lib.milo_quantize_rtn_int3(None, 4, 128, fake, fake, fake, None) == 1
+
+
+def test_route_rejects(L):
+    lib = L.lib()
+    f = C.c_void_p(0x1000)
+    args = lambda T, E, k, S, ws=None, wsb=0: lib.milo_route_sort(f, T, E, k, S, 1, f, f, f, f, f, f, ws, wsb, None)
+    assert args(0, 8, 2, 0) == 2
+    assert args(16, 8, 9, 0) == 2
+    assert args(16, 8, 0, 0) == 2
+    assert args(16, 250, 2, 10) == 2          # E + S > 256
+    assert args(16, 8, 8, 9) == 2             # k + S > 16
+    assert args(1000, 8, 2, 0) == 5           # needs workspace
+    assert lib.milo_route_workspace_bytes(256, 8, 2, 0) == 0
+    assert lib.milo_route_workspace_bytes(1000, 8, 2, 0) > 0
+
+
+def _desc(L, **kw):
+    d = L.MiloGemmDesc()
+    d.num_experts, d.N, d.K, d.max_rank, d.n_w = 8, 1024, 512, 16, 1
+    for i in range(2):
+        d.w[i].packed = d.w[i].sz = d.w[i].U = d.w[i].V = 0x10000
+        d.w[i].rank = 0x10000
+    d.x = 0x20000
+    d.x_rows = 16
+    d.offsets = 0x30000
+    d.sorted_pairs = 0x40000
+    d.num_pairs = 32
+    d.epilogue = L.EPI_NONE
+    d.y = 0x50000
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("N", 1000, 2), ("K", 500, 2), ("num_experts", 0, 2), ("num_experts", 300, 2),
+    ("max_rank", 12, 4), ("max_rank", 72, 4), ("epilogue", 7, 6), ("path", 5, 6),
+    ("n_w", 2, 6), ("x", 0, 1), ("offsets", 0, 1), ("y", 0, 1), ("x", 0x20008, 3),
+    ("num_pairs", -1, 2), ("epilogue", 2, 1),
+])
+def test_gemm_rejects(L, field, value, code):
+    lib = L.lib()
+    d = _desc(L, **{field: value})
+    if field == "epilogue" and value == 2:
+        d.slot_w = None
+    assert lib.milo_moe_w3a16_lowrank_gemm(C.byref(d), None, 0, None) == code
+    assert len(lib.milo_last_error()) > 0
+
+
+def test_gemm_workspace_query_and_shortfall(L):
+    lib = L.lib()
+    d = _desc(L)
+    need = lib.milo_moe_gemm_workspace_bytes(C.byref(d))
+    assert need > 0
+    assert lib.milo_moe_w3a16_lowrank_gemm(C.byref(d), None, 0, None) == 5
+    assert lib.milo_moe_w3a16_lowrank_gemm(C.byref(d), C.c_void_p(0x100000), need - 1, None) == 5
+    assert lib.milo_moe_w3a16_lowrank_gemm(C.byref(d), C.c_void_p(0x100010), need, None) == 3
+    forced = _desc(L, path=L.PATH_DECODE, num_pairs=4096, max_rows_per_expert=100)
+    assert lib.milo_moe_w3a16_lowrank_gemm(C.byref(forced), None, 0, None) == 2
+
+
+def test_combine_rejects(L):
+    lib = L.lib()
+    f = C.c_void_p(0x1000)
+    assert lib.milo_moe_combine(None, 4, 2, 64, f, None) == 1
+    assert lib.milo_moe_combine(f, 4, 2, 66, f, None) == 2
+    assert lib.milo_moe_combine(f, 4, 0, 64, f, None) == 2
+    assert lib.milo_moe_combine(C.c_void_p(0x1004), 4, 2, 64, f, None) == 3

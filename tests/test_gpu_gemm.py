@@ -1,0 +1,215 @@
+"""The routed W3A16 + low-rank grouped GEMM vs the oracle (float64, unfused):
+relative Frobenius error <= 1e-3 and max abs error <= 2e-2 on fp16 outputs,
+for both kernel paths, every epilogue, ragged expert sizes and the special
+cases of the method (rank 0, zero compensator, zero weights)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.configs import C1
+from tests.gpu_helpers import assert_close, make_family, to_np
+
+pytestmark = pytest.mark.gpu
+
+PATHS = {"auto": 0, "decode": 1, "prefill": 2}
+
+
+def _m():
+    import extreme_quantized_moe_amd as m
+    return m
+
+
+def test_c1_single_linear_all_paths():
+    m = _m()
+    d = synth.gen_linear(C1)
+    fam = m.Family.from_dense([d["W"].cuda()], [d["A"]], [d["B"]])
+    q, s, z = oracle.quantize_rtn_int3(d["W"].numpy())
+    ref = oracle.linear_ref(d["X"].numpy(), q, s, z, d["A"].numpy(), d["B"].numpy())
+    x = d["X"].cuda()
+    offsets = torch.tensor([0, C1.M], dtype=torch.int32, device="cuda")
+    for name, path in PATHS.items():
+        y = torch.empty((C1.M, C1.N), dtype=torch.float16, device="cuda")
+        m.moe_w3a16_lowrank_gemm((fam,), x, offsets, C1.M, m.EPI_NONE, y, path=path)
+        torch.cuda.synchronize()
+        assert_close(to_np(y), ref, f"C1 {name}")
+    # the compensator matters at this tolerance: dropping it must fail the bar
+    ref_nolr = oracle.linear_ref(d["X"].numpy(), q, s, z)
+    assert oracle.rel_fro(ref_nolr, ref) > 5e-3
+
+
+def _route(T, E, k, S, seed, skew=None):
+    g = torch.Generator().manual_seed(seed)
+    logits = torch.randn((T, E), generator=g)
+    if skew is not None:
+        logits[:, skew] += 6.0
+    return logits
+
+
+def _moe_case(E, S, N, K, ranks, T, k, epilogue, path, seed, skew=None, zero_w=False, zero_lr=False):
+    m = _m()
+    ET = E + S
+    logits = _route(T, E, k, S, seed, skew)
+    r = m.route_sort(logits.cuda(), k, S, True)
+    ref_r = oracle.route_ref(logits.numpy(), k, S, True)
+    slots = k + S
+    P = T * slots
+    g = torch.Generator().manual_seed(seed + 1)
+    if epilogue == m.EPI_ROUTE_SCALE:
+        # down projection input: one row per pair, in sorted order
+        x = (torch.randn((P, K), generator=g)).half()
+        gather = 0
+    else:
+        x = (torch.randn((T, K), generator=g)).half()
+        gather = slots
+    nfam = 2 if epilogue == m.EPI_SWIGLU else 1
+    fams, refs = [], []
+    for f in range(nfam):
+        fam, ref = make_family(seed * 10 + f, ET, N, K, ranks, zero_w=zero_w, zero_lr=zero_lr)
+        fams.append(fam)
+        refs.append(ref)
+    if epilogue == m.EPI_ROUTE_SCALE:
+        y = torch.full((P, N), float("nan"), dtype=torch.float32, device="cuda")
+    else:
+        y = torch.empty((P, N), dtype=torch.float16, device="cuda")
+    m.moe_w3a16_lowrank_gemm(tuple(fams), x.cuda(), r["offsets"], P, epilogue, y,
+                             sorted_pairs=r["sorted_pairs"], gather_div=gather, slot_w=r["slot_w"],
+                             y_rows=P, max_rows_per_expert=T, path=path)
+    torch.cuda.synchronize()
+    got = to_np(y).astype(np.float64)
+    xs = x.numpy()
+    sp, off = ref_r["sorted_pairs"], ref_r["offsets"]
+    want = np.zeros((P, N))
+    for e in range(ET):
+        seg = sp[off[e]:off[e + 1]]
+        if seg.size == 0:
+            continue
+        rows = xs[seg // slots] if gather else xs[off[e]:off[e + 1]]
+        outs = []
+        for f in range(nfam):
+            q, s, z = refs[f]["q"][e]
+            outs.append(oracle.linear_ref(rows, q, s, z, refs[f]["A"][e], refs[f]["B"][e]))
+        if epilogue == m.EPI_SWIGLU:
+            val = oracle.silu(outs[0]) * outs[1]
+        else:
+            val = outs[0]
+        if epilogue == m.EPI_ROUTE_SCALE:
+            want[seg] = val * ref_r["slot_w"].reshape(-1)[seg][:, None]
+        else:
+            want[off[e]:off[e + 1]] = val
+    return got, want
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill", "auto"])
+@pytest.mark.parametrize("epi", ["none", "swiglu", "route"])
+def test_small_moe(path, epi):
+    m = _m()
+    epilogue = {"none": m.EPI_NONE, "swiglu": m.EPI_SWIGLU, "route": m.EPI_ROUTE_SCALE}[epi]
+    # 5 routed + 1 shared experts, ragged ranks (0 .. 64), K = 3 blocks, N = 3 tiles
+    got, want = _moe_case(E=5, S=1, N=192, K=384, ranks=[16, 0, 64, 8, 32, 24], T=24, k=2,
+                          epilogue=epilogue, path=PATHS[path], seed=3)
+    assert_close(got, want, f"small moe {path} {epi}")
+
+
+@pytest.mark.parametrize("T", [1, 7, 33, 64])
+def test_decode_row_counts(T):
+    m = _m()
+    got, want = _moe_case(E=4, S=0, N=128, K=256, ranks=[16, 32, 48, 64], T=T, k=2,
+                          epilogue=m.EPI_SWIGLU, path=PATHS["decode"], seed=T)
+    assert_close(got, want, f"decode T={T}")
+
+
+@pytest.mark.parametrize("T", [100, 300])
+def test_prefill_ragged_tiles(T):
+    m = _m()
+    # skewed routing: expert 2 gets every token (several 128-row tiles + tail),
+    # others few or none
+    got, want = _moe_case(E=6, S=0, N=256, K=512, ranks=[8, 16, 32, 64, 0, 40], T=T, k=2,
+                          epilogue=m.EPI_ROUTE_SCALE, path=PATHS["auto"], seed=T, skew=2)
+    assert_close(got, want, f"prefill T={T}")
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_zero_weights_isolate_lowrank(path):
+    m = _m()
+    got, want = _moe_case(E=3, S=0, N=128, K=256, ranks=[16, 32, 64], T=12, k=2,
+                          epilogue=m.EPI_NONE, path=PATHS[path], seed=21, zero_w=True)
+    assert np.abs(want).max() > 0
+    assert_close(got, want, f"W=0 {path}")
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_zero_compensator(path):
+    m = _m()
+    got, want = _moe_case(E=3, S=0, N=128, K=256, ranks=[16, 32, 64], T=12, k=2,
+                          epilogue=m.EPI_NONE, path=PATHS[path], seed=22, zero_lr=True)
+    assert_close(got, want, f"A=B=0 {path}")
+
+
+def test_rank_zero_everywhere():
+    m = _m()
+    got, want = _moe_case(E=2, S=0, N=64, K=128, ranks=[0, 0], T=5, k=1,
+                          epilogue=m.EPI_NONE, path=PATHS["auto"], seed=23)
+    assert_close(got, want, "rank 0")
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_deterministic(path):
+    m = _m()
+    fam, _ = make_family(40, 4, 128, 1024, [16, 32, 64, 8])
+    g = torch.Generator().manual_seed(41)
+    T, k = 16, 2
+    logits = torch.randn((T, 4), generator=g)
+    r = m.route_sort(logits.cuda(), k, 0, True)
+    x = torch.randn((T, 1024), generator=g).half().cuda()
+    P = T * k
+    outs = []
+    for _ in range(3):
+        y = torch.empty((P, 128), dtype=torch.float32, device="cuda")
+        m.moe_w3a16_lowrank_gemm((fam,), x, r["offsets"], P, m.EPI_ROUTE_SCALE, y,
+                                 sorted_pairs=r["sorted_pairs"], gather_div=k, slot_w=r["slot_w"],
+                                 y_rows=P, max_rows_per_expert=T, path=PATHS[path])
+        torch.cuda.synchronize()
+        outs.append(y.clone())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_direct_output_guard_band():
+    """Output rows written in place inside a larger sentinel-filled buffer."""
+    m = _m()
+    fam, ref = make_family(50, 2, 128, 256, [16, 32])
+    g = torch.Generator().manual_seed(51)
+    T = 8
+    x = torch.randn((T, 256), generator=g).half()
+    offsets = torch.tensor([0, 3, T], dtype=torch.int32, device="cuda")
+    big = torch.full(((T + 4) * 128,), -7.0, dtype=torch.float16, device="cuda")
+    y = big[2 * 128:(T + 2) * 128].view(T, 128)
+    for path in (1, 2):
+        m.moe_w3a16_lowrank_gemm((fam,), x.cuda(), offsets, T, m.EPI_NONE, y, path=path)
+        torch.cuda.synchronize()
+        assert torch.all(big[:2 * 128] == -7.0) and torch.all(big[(T + 2) * 128:] == -7.0)
+        want = np.concatenate([
+            oracle.linear_ref(x.numpy()[:3], *ref["q"][0], ref["A"][0], ref["B"][0]),
+            oracle.linear_ref(x.numpy()[3:], *ref["q"][1], ref["A"][1], ref["B"][1])])
+        assert_close(to_np(y), want, f"in-place path {path}")
+
+
+def test_workspace_reused_across_different_plans():
+    """One zero-initialised workspace serves calls whose plans differ (split
+    pre-pass vs not, split-K vs not) in any order."""
+    m = _m()
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    fam, ref = make_family(60, 3, 128, 1024, [16, 32, 64])
+    g = torch.Generator().manual_seed(61)
+    for T, path in [(200, 2), (10, 1), (200, 0), (3, 1), (10, 1)]:
+        x = torch.randn((T, 1024), generator=g).half()
+        cut = [0, T // 3, (2 * T) // 3, T]
+        offsets = torch.tensor(cut, dtype=torch.int32, device="cuda")
+        y = torch.empty((T, 128), dtype=torch.float16, device="cuda")
+        m.moe_w3a16_lowrank_gemm((fam,), x.cuda(), offsets, T, m.EPI_NONE, y,
+                                 max_rows_per_expert=T, path=path, workspace=ws)
+        torch.cuda.synchronize()
+        want = np.concatenate([oracle.linear_ref(x.numpy()[cut[e]:cut[e + 1]], *ref["q"][e],
+                                                 ref["A"][e], ref["B"][e]) for e in range(3)])
+        assert_close(to_np(y), want, f"reuse T={T} path={path}")
