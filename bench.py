@@ -1,0 +1,392 @@
+#!/usr/bin/env python3
+"""Benchmark of the MiLo W3A16 + low-rank MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config C2|C3|C4|C5|C1] [--batch T]
+
+A step is one pass of the whole hot path over one batch of synthetic tokens:
+route (softmax top-k + expert sort) -> low-rank pre-pass + fused gate/up
+W3A16 GEMM with SwiGLU -> low-rank pre-pass + fused down W3A16 GEMM with
+route scaling -> slot combine.  C5 steps through 32 layers.  Weights are
+seeded random (RTN int3 g64 on the GPU); inputs are resident in HBM before the
+timed region; single-layer workloads rotate through --copies independent
+weight sets so that the 256 MB last-level cache cannot serve the weights.
+
+Prints ONE JSON line.  The default workload is C2 (Mixtral-8x7B-shaped MoE FFN
+at decode, 16 tokens), the configuration the metric is quoted on.
+"""
+import argparse
+import ctypes as C
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores
+METRIC = "MoE-layer tokens/s + achieved HBM TB/s (decode) / MFMA % (prefill)"
+
+WORKLOAD_TEXT = {
+    "C1": "single expert linear, X 16x512 fp16, W 1024x512 int3 g64, rank 16 compensator",
+    "C2": "Mixtral-8x7B-shaped MoE FFN decode: 16 tokens, H=4096, F=14336, 8 experts top-2 "
+          "(renormalised softmax), SwiGLU, int3 g64 weights, per-expert ranks from {16,32,64}",
+    "C3": "Mixtral-8x7B-shaped MoE FFN prefill: 4096 tokens, H=4096, F=14336, 8 experts top-2, "
+          "int3 g64, ranks from {16,32,64}",
+    "C4": "DeepSeekMoE-16B-shaped layer: 256 tokens, H=2048, 64 routed experts (F=1408) top-6 "
+          "+ 2 shared (rank 32), Zipf(1.2) router skew, int3 g64, ranks from {8,16,32}",
+    "C5": "32 Mixtral-8x7B-shaped MoE blocks (int3 g64 + rank {16,32,64} compensators resident), decode",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--batch", type=int, default=None, help="tokens (C5 sweep: 1/8/32/64)")
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, 5 times "
+                         "(calibrates HBM byte counters against a known size)")
+    return ap.parse_args()
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def src_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------
+class Layer:
+    """One MoE layer's device weights, buffers and prebuilt call descriptors."""
+
+    def __init__(self, m, cfg, layer_idx, X, logits, path, ws):
+        import synth
+        import torch
+        L = m._lib
+        self.m, self.cfg = m, cfg
+        self.ranks = synth.gen_ranks(cfg, layer_idx)
+        ET = cfg.E + cfg.S
+        fam = {}
+        for n, a, b in (("W1", "A1", "B1"), ("W3", "A3", "B3"), ("W2", "A2", "B2")):
+            Ws, As, Bs = [], [], []
+            for e in range(ET):
+                d = synth.gen_expert(cfg, layer_idx, e, self.ranks[e], device="cuda", which=(n,))
+                Ws.append(d[n])
+                As.append(d[a])
+                Bs.append(d[b])
+            fam[n] = m.Family.from_dense(Ws, As, Bs, max_rank=max(self.ranks))
+            del Ws
+        self.fam = fam
+        T, slots = cfg.T, cfg.slots
+        P = T * slots
+        dev = "cuda"
+        self.X, self.logits = X, logits
+        self.route = {
+            "ids": torch.empty((T, cfg.k), dtype=torch.int32, device=dev),
+            "w": torch.empty((T, cfg.k), dtype=torch.float32, device=dev),
+            "slot_w": torch.empty(P, dtype=torch.float32, device=dev),
+            "sorted_pairs": torch.empty(P, dtype=torch.int32, device=dev),
+            "pair_pos": torch.empty(P, dtype=torch.int32, device=dev),
+            "offsets": torch.empty(ET + 1, dtype=torch.int32, device=dev),
+        }
+        self.route_wsb = int(L.lib().milo_route_workspace_bytes(T, cfg.E, cfg.k, cfg.S))
+        self.route_ws = torch.empty(max(self.route_wsb, 256), dtype=torch.uint8, device=dev)
+        self.G = torch.empty((P, cfg.F), dtype=torch.float16, device=dev)
+        self.Y = torch.empty((P, cfg.H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, cfg.H), dtype=torch.float16, device=dev)
+        r = self.route
+        self.d13 = m.ops.make_gemm_desc((fam["W1"], fam["W3"]), X, r["offsets"], P, L.EPI_SWIGLU,
+                                        self.G, sorted_pairs=r["sorted_pairs"], gather_div=slots,
+                                        max_rows_per_expert=T, path=path)
+        self.d2 = m.ops.make_gemm_desc((fam["W2"],), self.G, r["offsets"], P, L.EPI_ROUTE_SCALE,
+                                       self.Y, sorted_pairs=r["sorted_pairs"], gather_div=0,
+                                       slot_w=r["slot_w"], y_rows=P, max_rows_per_expert=T, path=path)
+        self.d13.flags = L.GEMM_PREPASS_DONE
+        self.d2.flags = L.GEMM_PREPASS_DONE
+        lib = L.lib()
+        need = max(lib.milo_moe_gemm_workspace_bytes(C.byref(self.d13)),
+                   lib.milo_moe_gemm_workspace_bytes(C.byref(self.d2)))
+        assert need > 0 and ws.numel() >= need, (need, ws.numel())
+        self.ws = ws
+        self.P, self.T, self.slots = P, T, slots
+
+    def step(self, stream, ev13=None):
+        L = self.m._lib
+        lib = L.lib()
+        r = self.route
+        p = lambda t: C.c_void_p(t.data_ptr())
+        cfg = self.cfg
+        chk = L.check
+        chk("route", lib.milo_route_sort(p(self.logits), cfg.T, cfg.E, cfg.k, cfg.S,
+                                         1 if cfg.renormalize else 0, p(r["ids"]), p(r["w"]),
+                                         p(r["slot_w"]), p(r["sorted_pairs"]), p(r["pair_pos"]),
+                                         p(r["offsets"]), p(self.route_ws), self.route_wsb, stream))
+        wsp, wsb = p(self.ws), self.ws.numel()
+        chk("prepass13", lib.milo_moe_lowrank_prepass(C.byref(self.d13), wsp, wsb, stream))
+        if ev13 is not None:
+            ev13[0].record()
+        chk("gemm13", lib.milo_moe_w3a16_lowrank_gemm(C.byref(self.d13), wsp, wsb, stream))
+        if ev13 is not None:
+            ev13[1].record()
+        chk("prepass2", lib.milo_moe_lowrank_prepass(C.byref(self.d2), wsp, wsb, stream))
+        chk("gemm2", lib.milo_moe_w3a16_lowrank_gemm(C.byref(self.d2), wsp, wsb, stream))
+        chk("combine", lib.milo_moe_combine(p(self.Y), cfg.T, self.slots, cfg.H, p(self.out), stream))
+
+    # algorithmic bytes / flops from the routed row counts (host copies)
+    def work(self, offsets):
+        cfg = self.cfg
+        H, F = cfg.H, cfg.F
+        rows = [int(offsets[e + 1] - offsets[e]) for e in range(cfg.E + cfg.S)]
+        b13 = b2 = 0
+        f13 = f2 = 0
+        touched = 0
+        for e, M in enumerate(rows):
+            if M == 0:
+                continue
+            touched += 1
+            r = self.ranks[e]
+            # gate/up kernel: W1, W3 packed + scale/zero + U (N x r) per matrix,
+            # gathered X rows, T rows, G written
+            b13 += 2 * (3 * F * H // 8 + F * H // 16 + F * r * 2) + M * H * 2 + M * 2 * r * 2 + M * F * 2
+            b2 += (3 * H * F // 8 + H * F // 16 + H * r * 2) + M * F * 2 + M * r * 2 + M * H * 4
+            f13 += 2 * M * 2 * F * H + 2 * M * 2 * r * (H + F)
+            f2 += 2 * M * H * F + 2 * M * r * (H + F)
+        # pre-pass reads of V (V1, V3: r x H; V2: r x F; fp16) for touched experts
+        vbytes = sum((2 * r * H + r * F) * 2 for e, r in enumerate(self.ranks) if rows[e])
+        layer_bytes = b13 + b2 + vbytes + cfg.T * H * 2 * 2 + cfg.T * cfg.E * 4
+        return {"rows": rows, "touched": touched, "bytes13": b13, "bytes2": b2, "flops13": f13,
+                "flops2": f2, "layer_bytes": layer_bytes, "layer_flops": f13 + f2}
+
+
+def cpu_baseline(cfg, layer, offsets, budget_s):
+    """The CPU oracle (float64 NumPy, as it stands) on a bounded sample of the
+    same layer: routing of all tokens plus the expert FFNs of as many touched
+    experts as fit the time budget, scaled to the whole layer."""
+    import numpy as np
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+    X = layer.X.cpu().numpy()
+    logits = layer.logits.cpu().numpy()
+    t0 = time.perf_counter()
+    rt = oracle.route_ref(logits, cfg.k, cfg.S, cfg.renormalize)
+    t_route = time.perf_counter() - t0
+    sp, off = rt["sorted_pairs"], rt["offsets"]
+    touched = [e for e in range(cfg.E + cfg.S) if off[e + 1] > off[e]]
+    done, t_exp, pairs_done = [], 0.0, 0
+    for e in touched:
+        exp = synth.gen_expert(cfg, 0, e, layer.ranks[e], device="cuda")
+        qe = oracle.quantize_expert({k: v.cpu() for k, v in exp.items()})   # offline, untimed
+        seg = sp[off[e]:off[e + 1]]
+        rows = X[seg // cfg.slots]
+        t1 = time.perf_counter()
+        oracle.expert_ffn_ref(rows, qe)
+        t_exp += time.perf_counter() - t1
+        done.append(e)
+        pairs_done += seg.size
+        del qe
+        if t_exp > budget_s:
+            break
+    scale = cfg.P / max(pairs_done, 1)
+    layer_s = t_route + t_exp * scale
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": cfg.T / layer_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"oracle.route_ref on all {cfg.T} tokens + oracle.expert_ffn_ref (float64 dequant + "
+                  f"matmul) for {len(done)} of {len(touched)} touched experts ({pairs_done} of {cfg.P} "
+                  f"pairs) in {t_route + t_exp:.1f} s, scaled x{scale:.2f} by pairs to the whole layer",
+        "layer_seconds": layer_s,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path: the MoE layer is measured on one MI355X.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import extreme_quantized_moe_amd as m
+    import synth
+    from synth import configs as SC
+
+    torch.cuda.set_device(0)
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_each_way": n, "copies": 5}))
+        return
+    cfg = SC.get_config(args.config)
+    if args.config == "C1":
+        return bench_c1(args, m, cfg)
+    if args.batch:
+        cfg = cfg.with_(T=args.batch)
+    path = {"auto": 0, "decode": 1, "prefill": 2}[args.path]
+    stack = cfg.layers > 1
+    nsets = cfg.layers if stack else args.copies
+    log(f"building {nsets} weight set(s) of {args.config} (T={cfg.T}) on the GPU")
+    X = synth.gen_tokens(cfg, 0, device="cuda")
+    t0 = time.time()
+    layers = []
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    for i in range(nsets):
+        logits = synth.gen_logits(cfg, i if stack else 0, device="cuda")
+        layers.append(Layer(m, cfg, i if stack else 0, X, logits, path, ws) if (stack or i == 0)
+                      else Layer(m, cfg, 100 + i, X, logits, path, ws))
+    torch.cuda.synchronize()
+    log(f"weights ready in {time.time() - t0:.1f} s")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run_step(i, ev=None):
+        if stack:
+            for li, lay in enumerate(layers):
+                lay.step(stream, ev if li == 0 else None)
+        else:
+            layers[i % nsets].step(stream, ev)
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        run_step(i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    k13_us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1000.0
+
+    # work accounting (after the timed region)
+    works = []
+    for lay in layers:
+        offs = lay.route["offsets"].cpu().numpy()
+        works.append(lay.work(offs))
+    w0 = works[0] if stack else None
+    if stack:
+        layer_bytes = sum(w["layer_bytes"] for w in works)
+        layer_flops = sum(w["layer_flops"] for w in works)
+        k_bytes, k_flops = works[0]["bytes13"], works[0]["flops13"]
+    else:
+        used = [works[i % nsets] for i in range(args.steps)]
+        layer_bytes = sum(w["layer_bytes"] for w in used) / len(used)
+        layer_flops = sum(w["layer_flops"] for w in used) / len(used)
+        k_bytes = sum(w["bytes13"] for w in used) / len(used)
+        k_flops = sum(w["flops13"] for w in used) / len(used)
+        w0 = works[0]
+    tokens_per_s = cfg.T / (ms_step / 1000.0)
+    prefill = cfg.T * cfg.k / cfg.E > 64
+    kname = "gemm_prefill_kernel<2> (gate/up + SwiGLU)" if prefill else "gemm_decode_kernel<MT,2> (gate/up + SwiGLU)"
+    if prefill:
+        achieved = k_flops / (k13_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = k_bytes / (k13_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(args.config, cfg.T)}
+    roof.update({"kernel": kname, "alg_bytes_per_launch": int(k_bytes), "alg_flops_per_launch": int(k_flops),
+                 "avg_launch_us": round(k13_us, 2)})
+    res = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}",
+            "tokens": cfg.T, "layers": cfg.layers, "experts": cfg.E, "shared": cfg.S, "top_k": cfg.k,
+            "hidden": cfg.H, "ffn": cfg.F, "weight_sets_rotated": nsets,
+            "touched_experts": w0["touched"],
+            "step_alg_bytes": int(layer_bytes), "step_alg_flops": int(layer_flops),
+            "achieved_TBps_step": round(layer_bytes / (ms_step * 1e-3) / 1e12, 3),
+            "achieved_TFLOPs_step": round(layer_flops / (ms_step * 1e-3) / 1e12, 2),
+            "host_seconds_timed": round(t_host, 3),
+            "path": args.path,
+        },
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(cfg, layers[0], None, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res))
+
+
+def traffic_for(config, T):
+    """Measured HBM traffic of the dominant kernel from a committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    f = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(f):
+        return None
+    try:
+        d = json.load(open(f))
+        ent = d.get(f"{config}_T{T}")
+        if not ent or ent.get("src_hash") != src_hash(ent.get("src_files", [])):
+            return None
+        return ent.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def bench_c1(args, m, cfg):
+    import torch
+    import synth
+    d = synth.gen_linear(cfg, device="cuda")
+    fam = m.Family.from_dense([d["W"]], [d["A"]], [d["B"]])
+    x = d["X"]
+    offsets = torch.tensor([0, cfg.M], dtype=torch.int32, device="cuda")
+    y = torch.empty((cfg.M, cfg.N), dtype=torch.float16, device="cuda")
+    for _ in range(args.warmup):
+        m.moe_w3a16_lowrank_gemm((fam,), x, offsets, cfg.M, m.EPI_NONE, y)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(args.steps):
+        m.moe_w3a16_lowrank_gemm((fam,), x, offsets, cfg.M, m.EPI_NONE, y)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    print(json.dumps({"metric": "single linear latency", "value": round(ms * 1000, 2), "unit": "us",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+                      "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+                      "data": "synthetic", "config": {"workload": "C1: " + WORKLOAD_TEXT["C1"]},
+                      "roofline": None, "cpu_baseline": None}))
+
+
+if __name__ == "__main__":
+    main()

@@ -10,6 +10,7 @@ STATUS_NAMES = {0: "MILO_OK", 1: "MILO_ERR_NULL", 2: "MILO_ERR_SHAPE", 3: "MILO_
                 4: "MILO_ERR_RANK", 5: "MILO_ERR_WORKSPACE", 6: "MILO_ERR_ARG", 7: "MILO_ERR_HIP"}
 EPI_NONE, EPI_SWIGLU, EPI_ROUTE_SCALE = 0, 1, 2
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
+GEMM_PREPASS_DONE = 1
 
 
 class MiloWeights(C.Structure):
@@ -26,7 +27,7 @@ class MiloGemmDesc(C.Structure):
         ("sorted_pairs", C.c_void_p), ("offsets", C.c_void_p),
         ("num_pairs", C.c_int32), ("max_rows_per_expert", C.c_int32),
         ("slot_w", C.c_void_p), ("y_rows", C.c_int32), ("epilogue", C.c_int32),
-        ("y", C.c_void_p), ("path", C.c_int32),
+        ("y", C.c_void_p), ("path", C.c_int32), ("flags", C.c_int32),
     ]
 
 
@@ -47,7 +48,7 @@ def lib():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} not found: build it with "
-                          "`python -m extreme_quantized_moe_amd.build` (no fallback path exists)")
+                          "`python extreme_quantized_moe_amd/build.py` (no fallback path exists)")
     L = C.CDLL(LIB_PATH)
     i32, i64, vp, sz = C.c_int32, C.c_int64, C.c_void_p, C.c_size_t
     sig = {
@@ -63,6 +64,7 @@ def lib():
         "milo_route_sort": (i32, [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "milo_moe_gemm_workspace_bytes": (sz, [C.POINTER(MiloGemmDesc)]),
         "milo_moe_w3a16_lowrank_gemm": (i32, [C.POINTER(MiloGemmDesc), vp, sz, vp]),
+        "milo_moe_lowrank_prepass": (i32, [C.POINTER(MiloGemmDesc), vp, sz, vp]),
         "milo_moe_combine": (i32, [vp, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():

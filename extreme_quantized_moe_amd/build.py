@@ -1,6 +1,6 @@
 """Build libmilo.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m extreme_quantized_moe_amd.build [--verbose]
+    python extreme_quantized_moe_amd/build.py [--verbose]
 
 Each translation unit is compiled to an object in _build/ (in parallel), then
 linked into extreme_quantized_moe_amd/libmilo.so.  Always recompiles.

@@ -55,6 +55,9 @@ GemmArgs make_gemm_args(const milo_gemm_desc* d, const GemmPlan& p, char* ws) {
   a.K = d->K;
   a.kblocks = p.kblocks;
   a.n_tiles = p.n_tiles;
+  a.groups = d->K / kGroup;
+  a.xsum = (const float*)(ws + p.off_xs);
+  a.xoff = a.xsum + (size_t)d->num_experts * a.groups * kDecodeMaxRows;
   a.gather_div = d->gather_div;
   a.num_experts = d->num_experts;
   a.n_w = d->n_w;
@@ -117,7 +120,7 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
   if (rows_bound > P) rows_bound = P;
   if (P == 0) return MILO_OK;  // nothing to do
 
-  auto mt_for = [](int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); };
+  auto mt_for = [](int rows) { return rows <= 16 ? 1 : 2; };
   if (d->path == MILO_PATH_DECODE) {
     if (rows_bound > kDecodeMaxRows)
       MILO_FAIL(MILO_ERR_SHAPE, "decode path needs <= %d rows per expert (bound %d)", kDecodeMaxRows, rows_bound);
@@ -135,34 +138,26 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
   p->pre_tiles = (P + 127) / 128 + d->num_experts;
 
   if (p->dec_mt) {
+    // split K only when the (expert, n-tile) blocks cannot fill the chip;
+    // splits are summed by a separate reduce kernel
     const int active = d->num_experts < P ? d->num_experts : P;
     const int blocks = active * p->n_tiles;
-    int ks = (1024 + blocks - 1) / blocks;
-    int ks_max = p->kblocks / 4;
+    int ks = blocks >= 384 ? 1 : (512 + blocks - 1) / blocks;
+    int ks_max = p->kblocks / 8;
     if (ks_max < 1) ks_max = 1;
     if (ks > ks_max) ks = ks_max;
     if (ks < 1) ks = 1;
     p->dec_ksplit = ks;
   }
   p->lr_tiles = (P + 15) / 16 + d->num_experts;
-  p->lr_kchunks = 1;
-  if (p->rp && rows_bound <= kDecodeMaxRows && p->lr_tiles <= kMaxLrCounters) {
-    int kc = d->K / 32 / 4;
-    p->lr_kchunks = kc > 16 ? 16 : (kc < 1 ? 1 : kc);
-  }
+  const int nrt = d->n_w * p->rp / 16;
+  p->lr_tiles_per_block = rows_bound <= kDecodeMaxRows ? 1 : (nrt > 0 ? nrt : 1);
 
-  // The counter regions sit at fixed offsets at the start of every workspace,
-  // whatever the call, so that counters left at zero by one call are still
-  // counters (and zero) for the next call that uses the same workspace.
   size_t off = 0;
-  p->off_lr_cnt = off;
-  off += (size_t)kMaxLrCounters * 4;
-  p->off_dec_cnt = off;
-  off += (size_t)kMaxDecCounters * 4;
   p->off_t = off;
   off += round_up((size_t)P * d->n_w * p->rp * 2, 256);
-  p->off_lr_part = off;
-  if (p->lr_kchunks > 1) off += round_up((size_t)p->lr_kchunks * p->lr_tiles * 16 * d->n_w * p->rp * 4, 256);
+  p->off_xs = off;
+  if (p->dec_mt) off += round_up((size_t)2 * d->num_experts * (d->K / kGroup) * kDecodeMaxRows * 4, 256);
   p->off_dec_part = off;
   if (p->dec_ksplit > 1)
     off += round_up((size_t)p->dec_ksplit * d->num_experts * p->n_tiles * d->n_w * p->dec_mt * 16 * 64 * 4, 256);
@@ -258,22 +253,40 @@ size_t milo_moe_gemm_workspace_bytes(const milo_gemm_desc* d) {
   return p.total;
 }
 
+static int32_t prepare_call(const milo_gemm_desc* d, void* workspace, size_t ws_bytes, GemmPlan* p) {
+  int32_t rc = validate_gemm(d);
+  if (rc != MILO_OK) return rc;
+  if (d->flags & ~MILO_GEMM_PREPASS_DONE) MILO_FAIL(MILO_ERR_ARG, "unknown flags 0x%x", d->flags);
+  rc = plan_gemm(d, p);
+  if (rc != MILO_OK) return rc;
+  if (d->num_pairs == 0) return MILO_OK;
+  if (p->total && (!workspace || ws_bytes < p->total))
+    MILO_FAIL(MILO_ERR_WORKSPACE, "gemm workspace %zu bytes < required %zu", ws_bytes, p->total);
+  if (p->total && !aligned(workspace, 256)) MILO_FAIL(MILO_ERR_ALIGN, "workspace must be 256-byte aligned");
+  return MILO_OK;
+}
+
+int32_t milo_moe_lowrank_prepass(const milo_gemm_desc* d, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  g_err[0] = 0;
+  GemmPlan p;
+  int32_t rc = prepare_call(d, workspace, ws_bytes, &p);
+  if (rc != MILO_OK || d->num_pairs == 0) return rc;
+  return launch_lowrank(d, p, (char*)workspace, (hipStream_t)stream);
+}
+
 int32_t milo_moe_w3a16_lowrank_gemm(const milo_gemm_desc* d, void* workspace, size_t ws_bytes,
                                     void* stream) {
   g_err[0] = 0;
-  int32_t rc = validate_gemm(d);
-  if (rc != MILO_OK) return rc;
   GemmPlan p;
-  rc = plan_gemm(d, &p);
-  if (rc != MILO_OK) return rc;
-  if (d->num_pairs == 0) return MILO_OK;
-  if (p.total && (!workspace || ws_bytes < p.total))
-    MILO_FAIL(MILO_ERR_WORKSPACE, "gemm workspace %zu bytes < required %zu", ws_bytes, p.total);
-  if (p.total && !aligned(workspace, 256)) MILO_FAIL(MILO_ERR_ALIGN, "workspace must be 256-byte aligned");
+  int32_t rc = prepare_call(d, workspace, ws_bytes, &p);
+  if (rc != MILO_OK || d->num_pairs == 0) return rc;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  rc = launch_lowrank(d, p, ws, st);
-  if (rc != MILO_OK) return rc;
+  if (!(d->flags & MILO_GEMM_PREPASS_DONE)) {
+    rc = launch_lowrank(d, p, ws, st);
+    if (rc != MILO_OK) return rc;
+  }
   rc = launch_gemm_decode(d, p, ws, st);
   if (rc != MILO_OK) return rc;
   return launch_gemm_prefill(d, p, ws, st);

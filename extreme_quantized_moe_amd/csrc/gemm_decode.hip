@@ -10,15 +10,24 @@
 // packed weights once from HBM: block (n-tile of 64 output features, expert,
 // K split) = 4 waves, wave w takes the 128-wide K blocks w, w+4, ... of the
 // block's range.  Per K block a wave issues three 16-byte loads per lane for
-// the 64 x 128 codes (one per plane of layout v1) and two for the scale/zero
-// words, extracts the int3 pairs in registers, dequantizes them to float16
-// and feeds 16x16x32 f16 matrix-core ops with the rows of the expert as the A
-// operand (16 rows per m-tile, rows beyond the expert's count are zero).
-// Loads of the next K block are issued before the current one is consumed.
-// Waves are summed in LDS in wave order, K splits by the last block to finish
-// in split order, then the epilogue (low-rank term already added by wave 0 of
-// split 0) stores fp16 (NONE / SWIGLU) or scales and scatters fp32
-// (ROUTE_SCALE).
+// the 64 x 128 codes (one per plane of layout v1), two for the scale/zero
+// words, four per 16-row m-tile for the activation fragments and four per
+// m-tile for the per-group activation sums; these loads run DEPTH-1 K blocks
+// ahead of the block being consumed (a register ring).
+//
+// Dequantization is folded out of the inner product.  The extraction turns a
+// pair of int3 codes into two exact float16 values off + q (off = 64 or 8,
+// one v_and_or_b32 per pair), and the matrix cores compute, per 64-wide group
+// g, P = sum_k x_k (off_k + q_k) starting from the accumulator value
+// -(sum_k x_k off_k) - z sum_k x_k (both sums precomputed per row and group by
+// the pre-pass), so that P = sum_k x_k (q_k - z) up to fp32 rounding; then
+// y += s P in fp32.  No weight is rounded to float16.  The expert's rows are
+// the A operand (16 per m-tile, rows beyond the expert's count are zero) and
+// the codes the B operand.  Waves are summed in LDS in wave order.  With one
+// K split the block applies the epilogue itself; with several, each split
+// stores its sum and gemm_decode_reduce adds the splits in split order and
+// applies the epilogue (no cross-block synchronisation inside a kernel).  The
+// low-rank term is added by wave 0 of split 0.
 #include "gemm_common.hpp"
 
 namespace milo {
@@ -26,6 +35,12 @@ namespace milo {
 struct WTile {
   u32x4 q[3];
   u32x4 z[2];
+};
+
+template <int MT, int NW>
+struct Stage {
+  WTile w[NW];
+  f16x8 x[MT][4];
 };
 
 __device__ __forceinline__ void load_wtile(WTile& t, const uint32_t* tp, const uint32_t* sp, int lane) {
@@ -43,45 +58,119 @@ __device__ __forceinline__ uint32_t sz_word(const WTile& t, int i, int g) {
   return idx < 4 ? t.z[0][idx] : t.z[1][idx - 4];
 }
 
-template <int MT, int NW>
+template <int MT>
 __device__ __forceinline__ void consume_tile(const WTile& t, const f16x8 (&xa)[MT][4],
-                                             f32x4 (&acc)[MT][4], int lane) {
+                                             const f32x4 (&xs)[2][MT], const f32x4 (&xo)[2][MT],
+                                             f32x4 (&acc)[MT][4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint32_t h[16];
     extract_triplet(t.q[0][i], t.q[1][i], t.q[2][i], h);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const GroupConst gc = group_const(sz_word(t, i, g));
+      const uint32_t w = sz_word(t, i, g);
+      const float s = half_bits_to_float(w & 0xFFFFu);
+      const float z = half_bits_to_float(w >> 16);
 #pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        const int step = 2 * g + ss;
-        const f16x8 wb = dequant_step(h, step, gc);
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 p;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt][i] = mfma16x16x32(xa[mt][step], wb, acc[mt][i]);
+        for (int r = 0; r < 4; ++r) p[r] = __builtin_fmaf(-z, xs[g][mt][r], -xo[g][mt][r]);
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+          const int step = 2 * g + ss;
+          const u32x4 u = {h[4 * step], h[4 * step + 1], h[4 * step + 2], h[4 * step + 3]};
+          p = mfma16x16x32(xa[mt][step], __builtin_bit_cast(f16x8, u), p);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mt][i][r] = __builtin_fmaf(s, p[r], acc[mt][i][r]);
       }
     }
   }
 }
 
 template <int MT, int NW>
-__global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs a) {
+struct DecodeCtx {
+  const uint32_t* tbase[NW];
+  const uint32_t* sbase[NW];
+  const uint16_t* xp[MT];
+  const float* lds_xs;    // [local group][16 MT rows], then xo at + lds_half
+  int lds_half;
+  int g0;                 // first group of the block's K range
+  bool xok[MT];
+  int lane;
+
+  __device__ __forceinline__ void load(Stage<MT, NW>& S, int kb) const {
+#pragma unroll
+    for (int f = 0; f < NW; ++f)
+      load_wtile(S.w[f], tbase[f] + (size_t)kb * kTileWords, sbase[f] + (size_t)kb * kTileSzWords, lane);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        S.x[mt][s] = xok[mt] ? *(const f16x8*)(xp[mt] + (size_t)kb * kTileK + 32 * s) : f16x8{};
+  }
+  __device__ __forceinline__ void consume(const Stage<MT, NW>& S, int kb, f32x4 (&acc)[NW][MT][4]) const {
+    f32x4 xs[2][MT], xo[2][MT];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const float* q = lds_xs + (2 * kb + g - g0) * (16 * MT) + mt * 16 + 4 * (lane >> 4);
+        xs[g][mt] = *(const f32x4*)q;
+        xo[g][mt] = *(const f32x4*)(q + lds_half);
+      }
+#pragma unroll
+    for (int f = 0; f < NW; ++f) consume_tile<MT>(S.w[f], S.x, xs, xo, acc[f]);
+  }
+};
+
+// Final values -> outputs.  res[f][c] holds output (m, n) = (o >> 6, o & 63)
+// with o = threadIdx.x + 256 c of the 64-wide n-tile nt of expert e.
+template <int NW, int KPER>
+__device__ __forceinline__ void decode_epilogue(const GemmArgs& a, int e, int nt, int base, int M,
+                                                const float (&res)[NW][KPER]) {
+#pragma unroll
+  for (int c = 0; c < KPER; ++c) {
+    const int o = threadIdx.x + 256 * c;
+    const int m = o >> 6, n = o & 63;
+    if (m >= M) continue;
+    const int i = base + m;
+    const int col = nt * kTileRows + n;
+    if (a.epilogue == MILO_EPI_ROUTE_SCALE) {
+      const int s = a.sorted_pairs[i];
+      ((float*)a.y)[(size_t)s * a.N + col] = res[0][c] * a.slot_w[s];
+    } else {
+      float v = res[0][c];
+      if (NW == 2) v = silu(v) * res[NW - 1][c];
+      ((uint16_t*)a.y)[(size_t)i * a.N + col] = float_to_half_bits(v);
+    }
+  }
+}
+
+template <int MT, int NW, int DEPTH>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 2 : 1, MT == 1 ? 2 : 1)))
+gemm_decode_kernel(GemmArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nt = blockIdx.x, e = blockIdx.y, ks = blockIdx.z;
   const int base = a.offsets[e];
   const int M = a.offsets[e + 1] - base;
   if (M == 0 || M > a.dec_max_rows) return;
 
-  // A operand (rows of the expert) pointers
-  const uint16_t* xp[MT];
-  bool xok[MT];
+  DecodeCtx<MT, NW> cx;
+  cx.lane = lane;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + (lane & 15);
-    xok[mt] = m < M;
+    cx.xok[mt] = m < M;
     int xr = 0;
-    if (xok[mt]) xr = a.gather_div > 0 ? a.sorted_pairs[base + m] / a.gather_div : base + m;
-    xp[mt] = a.x + (size_t)xr * a.K + 8 * (lane >> 4);
+    if (cx.xok[mt]) xr = a.gather_div > 0 ? a.sorted_pairs[base + m] / a.gather_div : base + m;
+    cx.xp[mt] = a.x + (size_t)xr * a.K + 8 * (lane >> 4);
+  }
+#pragma unroll
+  for (int f = 0; f < NW; ++f) {
+    cx.tbase[f] = a.packed[f] + e * a.words_per_expert + (size_t)nt * a.kblocks * kTileWords;
+    cx.sbase[f] = a.sz[f] + e * a.sz_per_expert + (size_t)nt * a.kblocks * kTileSzWords;
   }
 
   f32x4 acc[NW][MT][4];
@@ -92,40 +181,51 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[f][mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int kb0 = (int)((int64_t)a.kblocks * ks / a.ksplit);
-  const int kb1 = (int)((int64_t)a.kblocks * (ks + 1) / a.ksplit);
-  const uint32_t* tbase[NW];
-  const uint32_t* sbase[NW];
-#pragma unroll
-  for (int f = 0; f < NW; ++f) {
-    tbase[f] = a.packed[f] + e * a.words_per_expert + (size_t)nt * a.kblocks * kTileWords;
-    sbase[f] = a.sz[f] + e * a.sz_per_expert + (size_t)nt * a.kblocks * kTileSzWords;
-  }
+  // K range of this block and the K blocks of this wave: kbw + 4 j, j < cnt
+  const int kbA = (int)((int64_t)a.kblocks * ks / a.ksplit);
+  const int kbB = (int)((int64_t)a.kblocks * (ks + 1) / a.ksplit);
+  const int kb0 = kbA + wave;
+  const int kb1 = kbB;
+  const int cnt = kb0 < kb1 ? (kb1 - kb0 + 3) / 4 : 0;
 
-  int kb = kb0 + wave;
-  WTile cur[NW], nxt[NW];
-  if (kb < kb1) {
-#pragma unroll
-    for (int f = 0; f < NW; ++f)
-      load_wtile(cur[f], tbase[f] + (size_t)kb * kTileWords, sbase[f] + (size_t)kb * kTileSzWords, lane);
+  // group sums of the block's rows over its K range -> LDS
+  extern __shared__ __align__(16) float smem[];
+  const int ngr = 2 * (kbB - kbA);
+  cx.lds_xs = smem;
+  cx.lds_half = ngr * 16 * MT;
+  cx.g0 = 2 * kbA;
+  for (int o = threadIdx.x; o < ngr * 16 * MT; o += 256) {
+    const int gl = o / (16 * MT), m = o - gl * (16 * MT);
+    const size_t src = ((size_t)e * a.groups + cx.g0 + gl) * kDecodeMaxRows + m;
+    smem[o] = a.xsum[src];
+    smem[cx.lds_half + o] = a.xoff[src];
   }
-  for (; kb < kb1; kb += 4) {
-    const int kn = kb + 4;
-    if (kn < kb1) {
+  __syncthreads();
+
+  Stage<MT, NW> ring[DEPTH];
 #pragma unroll
-      for (int f = 0; f < NW; ++f)
-        load_wtile(nxt[f], tbase[f] + (size_t)kn * kTileWords, sbase[f] + (size_t)kn * kTileSzWords, lane);
+  for (int d = 0; d < DEPTH - 1; ++d)
+    if (d < cnt) cx.load(ring[d], kb0 + 4 * d);
+  int j = 0;
+  // K block of ring entry consumed at step (j + d): kb0 + 4 (j + d)
+  // steady state: every prefetch in range, so loads are unconditional and
+  // each consume waits only for the batch issued DEPTH-1 steps earlier
+  for (; j + 2 * DEPTH - 1 <= cnt; j += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      cx.load(ring[(d + DEPTH - 1) % DEPTH], kb0 + 4 * (j + d + DEPTH - 1));
+      cx.consume(ring[d], kb0 + 4 * (j + d), acc);
     }
-    f16x8 xa[MT][4];
+  }
+  // tail: at most 2 DEPTH - 2 blocks left
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+  for (int t = 0; t < 2; ++t, j += DEPTH) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        xa[mt][s] = xok[mt] ? *(const f16x8*)(xp[mt] + (size_t)kb * kTileK + 32 * s) : f16x8{};
-#pragma unroll
-    for (int f = 0; f < NW; ++f) consume_tile<MT, NW>(cur[f], xa, acc[f], lane);
-#pragma unroll
-    for (int f = 0; f < NW; ++f) cur[f] = nxt[f];
+    for (int d = 0; d < DEPTH; ++d) {
+      const int jn = j + d + DEPTH - 1;
+      if (jn < cnt) cx.load(ring[(d + DEPTH - 1) % DEPTH], kb0 + 4 * jn);
+      if (j + d < cnt) cx.consume(ring[d], kb0 + 4 * (j + d), acc);
+    }
   }
 
   // low-rank term (x V^T) U^T: two more K steps per 32 ranks, added once
@@ -157,12 +257,11 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs a) {
   // ---- cross-wave reduction (wave order), one weight family at a time
   constexpr int kOut = MT * 16 * 64;       // outputs per family per block
   constexpr int kPer = kOut / 256;         // per thread
-  __shared__ float red[4][kOut];
-  __shared__ int is_last;
+  float (*red)[kOut] = (float (*)[kOut])smem;   // reuses the group-sum LDS
   float res[NW][kPer];
 #pragma unroll
   for (int f = 0; f < NW; ++f) {
-    if (f) __syncthreads();
+    __syncthreads();
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -180,62 +279,54 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs a) {
     }
   }
 
-  // ---- split-K: last block to finish sums the splits in split order
-  if (a.ksplit > 1) {
-    const size_t slot = ((size_t)e * a.n_tiles + nt);
-    float* mine = a.part + ((size_t)ks * a.num_experts * a.n_tiles + slot) * (NW * kOut);
+  if (a.ksplit > 1) {  // partial sums for gemm_decode_reduce
+    float* mine = a.part + (((size_t)ks * a.num_experts + e) * a.n_tiles + nt) * (NW * kOut);
 #pragma unroll
     for (int f = 0; f < NW; ++f)
 #pragma unroll
       for (int c = 0; c < kPer; ++c) mine[f * kOut + threadIdx.x + 256 * c] = res[f][c];
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int prev = atomicAdd(&a.cnt[slot], 1);
-      is_last = (prev == a.ksplit - 1);
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
+    return;
+  }
+  decode_epilogue<NW, kPer>(a, e, nt, base, M, res);
+}
+
+// Sum of the K splits in split order, then the epilogue.
+template <int MT, int NW>
+__global__ void __launch_bounds__(256) gemm_decode_reduce(GemmArgs a) {
+  const int nt = blockIdx.x, e = blockIdx.y;
+  const int base = a.offsets[e];
+  const int M = a.offsets[e + 1] - base;
+  if (M == 0 || M > a.dec_max_rows) return;
+  constexpr int kOut = MT * 16 * 64;
+  constexpr int kPer = kOut / 256;
+  float res[NW][kPer];
+#pragma unroll
+  for (int f = 0; f < NW; ++f)
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) res[f][c] = 0.f;
+  for (int s = 0; s < a.ksplit; ++s) {
+    const float* p = a.part + (((size_t)s * a.num_experts + e) * a.n_tiles + nt) * (NW * kOut);
 #pragma unroll
     for (int f = 0; f < NW; ++f)
 #pragma unroll
       for (int c = 0; c < kPer; ++c) {
-        float v = 0.f;
-        for (int s = 0; s < a.ksplit; ++s)
-          v += __builtin_nontemporal_load(
-              a.part + ((size_t)s * a.num_experts * a.n_tiles + slot) * (NW * kOut) + f * kOut +
-              threadIdx.x + 256 * c);
-        res[f][c] = v;
+        const int o = threadIdx.x + 256 * c;
+        if ((o >> 6) < M) res[f][c] += p[f * kOut + o];
       }
-    if (threadIdx.x == 0) a.cnt[slot] = 0;
   }
-
-  // ---- epilogue
-#pragma unroll
-  for (int c = 0; c < kPer; ++c) {
-    const int o = threadIdx.x + 256 * c;
-    const int m = o >> 6, n = o & 63;
-    if (m >= M) continue;
-    const int i = base + m;
-    const int col = nt * kTileRows + n;
-    if (a.epilogue == MILO_EPI_ROUTE_SCALE) {
-      const int s = a.sorted_pairs[i];
-      ((float*)a.y)[(size_t)s * a.N + col] = res[0][c] * a.slot_w[s];
-    } else {
-      float v = res[0][c];
-      if (NW == 2) v = silu(v) * res[NW - 1][c];
-      ((uint16_t*)a.y)[(size_t)i * a.N + col] = float_to_half_bits(v);
-    }
-  }
+  decode_epilogue<NW, kPer>(a, e, nt, base, M, res);
 }
 
-template <int MT>
+template <int MT, int NW>
 static void launch_mt(const GemmArgs& a, dim3 grid, hipStream_t st) {
-  if (a.n_w == 2)
-    hipLaunchKernelGGL((gemm_decode_kernel<MT, 2>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((gemm_decode_kernel<MT, 1>), grid, dim3(256), 0, st, a);
+  constexpr int depth = (MT == 1 && NW == 1) ? 3 : 2;
+  const int max_kb = (a.kblocks + a.ksplit - 1) / a.ksplit + 1;
+  size_t lds = (size_t)2 * 2 * max_kb * 16 * MT * sizeof(float);
+  const size_t red = (size_t)4 * MT * 16 * 64 * sizeof(float);
+  if (lds < red) lds = red;
+  hipLaunchKernelGGL((gemm_decode_kernel<MT, NW, depth>), grid, dim3(256), lds, st, a);
+  if (a.ksplit > 1)
+    hipLaunchKernelGGL((gemm_decode_reduce<MT, NW>), dim3(grid.x, grid.y), dim3(256), 0, st, a);
 }
 
 GemmArgs make_gemm_args(const milo_gemm_desc* d, const GemmPlan& p, char* ws);
@@ -244,12 +335,11 @@ int32_t launch_gemm_decode(const milo_gemm_desc* d, const GemmPlan& p, char* ws,
   if (p.dec_mt == 0) return MILO_OK;
   GemmArgs a = make_gemm_args(d, p, ws);
   a.part = (float*)(ws + p.off_dec_part);
-  a.cnt = (int32_t*)(ws + p.off_dec_cnt);
   dim3 grid(p.n_tiles, d->num_experts, p.dec_ksplit);
+  const bool two = d->n_w == 2;
   switch (p.dec_mt) {
-    case 1: launch_mt<1>(a, grid, st); break;
-    case 2: launch_mt<2>(a, grid, st); break;
-    case 4: launch_mt<4>(a, grid, st); break;
+    case 1: two ? launch_mt<1, 2>(a, grid, st) : launch_mt<1, 1>(a, grid, st); break;
+    case 2: two ? launch_mt<2, 2>(a, grid, st) : launch_mt<2, 1>(a, grid, st); break;
     default: set_error("internal: bad m-tile count %d", p.dec_mt); return MILO_ERR_ARG;
   }
   return hip_status(hipGetLastError(), "gemm_decode_kernel launch");

@@ -8,10 +8,12 @@
 // matrix cores) and stored as float16 for the GEMM kernels, which add
 // T . U^T as two more matrix-core K-steps.
 //
-// Grid: x = 16-row tiles over all experts (expert by expert), y = K chunks.
-// The four waves of a block split the chunk's 32-wide K steps round robin and
-// are summed in LDS in wave order; K chunks are summed by the last block of a
-// tile to finish, in chunk order (deterministic).
+// Grid: x = 16-row tiles over all experts (expert by expert), y = groups of
+// NRT rank tiles (16 ranks each).  At decode each block takes one rank tile
+// (many small blocks stream V in parallel); at prefill one block takes all
+// rank tiles of its rows (the activation rows are read once).  The four waves
+// of a block split the 32-wide K steps round robin, their partial sums are
+// added in LDS in wave order (deterministic, no cross-block synchronisation).
 #include "milo_internal.hpp"
 
 namespace milo {
@@ -23,10 +25,48 @@ struct LowrankArgs {
   const uint16_t* V[2];
   const int32_t* rank[2];
   uint16_t* T;        // fp16 [P][n_w * rp]
-  float* part;        // fp32 [kchunks][tiles][16][n_w * rp]
-  int32_t* cnt;       // [tiles]
-  int K, gather_div, num_experts, n_w, rp, max_rank, kchunks;
+  float* xsum;        // [expert][group][64 rows]: sum of x over the group
+  float* xoff;        // [expert][group][64 rows]: sum of x * off over the group
+  int K, gather_div, num_experts, n_w, rp, max_rank;
+  int xs_y;           // blockIdx.y of the group-sum blocks (-1: none)
+  int dec_max_rows;   // experts with more rows need no group sums
 };
+
+// Offset (64 or 8) of the "off + q" float16 encoding of the code at position
+// kk (0..127) of a 128-wide K block: code c = 8 (kk div 32) + kk mod 8 of the
+// lane's triplet, pair c div 2.
+__device__ __forceinline__ float code_offset(int kk) {
+  const int c = 8 * (kk >> 5) + (kk & 7);
+  return (float)pair_offset(c >> 1);
+}
+
+// Per (row, 64-wide group): sum of x and sum of x * off, in a fixed order.
+__device__ void group_sums(const LowrankArgs& a, int e, int m0, int M) {
+  if (M > a.dec_max_rows) return;                 // tile-kernel expert
+  const int row = threadIdx.x >> 4;
+  const int m = m0 + row;
+  if (m >= M) return;
+  const int base = a.offsets[e];
+  const int xr = a.gather_div > 0 ? a.sorted_pairs[base + m] / a.gather_div : base + m;
+  const int G = a.K / kGroup;
+  for (int g = threadIdx.x & 15; g < G; g += 16) {
+    const uint16_t* p = a.x + (size_t)xr * a.K + (size_t)g * kGroup;
+    float sx = 0.f, so = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const f16x8 v = *(const f16x8*)(p + 8 * c);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float xv = (float)v[t];
+        sx += xv;
+        so = __builtin_fmaf(xv, code_offset(64 * (g & 1) + 8 * c + t), so);
+      }
+    }
+    const size_t o = ((size_t)e * G + g) * kDecodeMaxRows + m;
+    a.xsum[o] = sx;
+    a.xoff[o] = so;
+  }
+}
 
 // Locate the (expert, first row) of 16-row tile `tile`; returns false past the end.
 __device__ __forceinline__ bool find_tile16(const int32_t* offsets, int num_experts, int tile,
@@ -46,16 +86,20 @@ __device__ __forceinline__ bool find_tile16(const int32_t* offsets, int num_expe
   return false;
 }
 
-template <int NRT>  // rank tiles of 16 columns (n_w * rp / 16)
+template <int NRT>  // rank tiles of 16 columns per block
 __global__ void __launch_bounds__(256) lowrank_kernel(LowrankArgs a) {
   __shared__ float red[4][NRT][64][4];
-  __shared__ int is_last;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e, m0, M;
   if (!find_tile16(a.offsets, a.num_experts, blockIdx.x, &e, &m0, &M)) return;
+  if ((int)blockIdx.y == a.xs_y) {
+    group_sums(a, e, m0, M);
+    return;
+  }
   const int base = a.offsets[e];
   const int RW = a.n_w * a.rp;
   const int tiles_per_w = a.rp / 16;
+  const int tr0 = blockIdx.y * NRT;            // first rank tile of this block
 
   // A operand row of this lane
   const int m = m0 + (lane & 15);
@@ -68,71 +112,64 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowrankArgs a) {
   const uint16_t* vp[NRT];
   bool vok[NRT];
 #pragma unroll
-  for (int tr = 0; tr < NRT; ++tr) {
+  for (int t = 0; t < NRT; ++t) {
+    const int tr = tr0 + t;
     const int f = tr / tiles_per_w;
     const int j = (tr % tiles_per_w) * 16 + (lane & 15);
-    vok[tr] = j < a.rank[f][e];
-    vp[tr] = a.V[f] + ((size_t)e * a.max_rank + (vok[tr] ? j : 0)) * a.K + 8 * (lane >> 4);
+    vok[t] = j < a.rank[f][e];
+    vp[t] = a.V[f] + ((size_t)e * a.max_rank + (vok[t] ? j : 0)) * a.K + 8 * (lane >> 4);
   }
 
   f32x4 acc[NRT];
 #pragma unroll
-  for (int tr = 0; tr < NRT; ++tr) acc[tr] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NRT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // K steps s = wave + 4 i; loads batched four steps at a time
   const int ksteps = a.K / 32;
-  const int s0 = (int)((int64_t)ksteps * blockIdx.y / a.kchunks);
-  const int s1 = (int)((int64_t)ksteps * (blockIdx.y + 1) / a.kchunks);
-  for (int s = s0 + wave; s < s1; s += 4) {
-    f16x8 xa = f16x8{};
-    if (row_ok) xa = *(const f16x8*)(xp + 32 * s);
+  int s = wave;
+  for (; s + 12 < ksteps; s += 16) {
+    f16x8 xa[4], vb[4][NRT];
 #pragma unroll
-    for (int tr = 0; tr < NRT; ++tr) {
-      f16x8 vb = f16x8{};
-      if (vok[tr]) vb = *(const f16x8*)(vp[tr] + 32 * s);
-      acc[tr] = mfma16x16x32(xa, vb, acc[tr]);
+    for (int u = 0; u < 4; ++u) {
+      xa[u] = row_ok ? *(const f16x8*)(xp + 32 * (s + 4 * u)) : f16x8{};
+#pragma unroll
+      for (int t = 0; t < NRT; ++t)
+        vb[u][t] = vok[t] ? *(const f16x8*)(vp[t] + 32 * (s + 4 * u)) : f16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < NRT; ++t) acc[t] = mfma16x16x32(xa[u], vb[u][t], acc[t]);
+  }
+  for (; s < ksteps; s += 4) {
+    const f16x8 xa = row_ok ? *(const f16x8*)(xp + 32 * s) : f16x8{};
+#pragma unroll
+    for (int t = 0; t < NRT; ++t) {
+      const f16x8 vb = vok[t] ? *(const f16x8*)(vp[t] + 32 * s) : f16x8{};
+      acc[t] = mfma16x16x32(xa, vb, acc[t]);
     }
   }
 #pragma unroll
-  for (int tr = 0; tr < NRT; ++tr)
+  for (int t = 0; t < NRT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][tr][lane][r] = acc[tr][r];
+    for (int r = 0; r < 4; ++r) red[wave][t][lane][r] = acc[t][r];
   __syncthreads();
 
-  // thread -> (rank tile, lane, r) outputs: NRT * 256 values over 256 threads
   for (int o = threadIdx.x; o < NRT * 256; o += 256) {
-    const int tr = o >> 8, ln = (o >> 2) & 63, r = o & 3;
-    const float v = red[0][tr][ln][r] + red[1][tr][ln][r] + red[2][tr][ln][r] + red[3][tr][ln][r];
+    const int t = o >> 8, ln = (o >> 2) & 63, r = o & 3;
+    const float v = ((red[0][t][ln][r] + red[1][t][ln][r]) + red[2][t][ln][r]) + red[3][t][ln][r];
     const int row = 4 * (ln >> 4) + r;            // 0..15 within the tile
-    const int col = tr * 16 + (ln & 15);          // 0..RW-1
-    if (a.kchunks == 1) {
-      if (m0 + row < M) a.T[(size_t)(base + m0 + row) * RW + col] = float_to_half_bits(v);
-    } else {
-      a.part[(((size_t)blockIdx.y * gridDim.x + blockIdx.x) * 16 + row) * RW + col] = v;
-    }
-  }
-  if (a.kchunks == 1) return;
-
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&a.cnt[blockIdx.x], 1);
-    is_last = (prev == a.kchunks - 1);
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int o = threadIdx.x; o < 16 * RW; o += 256) {
-    const int row = o / RW, col = o - row * RW;
-    float v = 0.f;
-    for (int c = 0; c < a.kchunks; ++c)
-      v += __builtin_nontemporal_load(&a.part[(((size_t)c * gridDim.x + blockIdx.x) * 16 + row) * RW + col]);
+    const int col = (tr0 + t) * 16 + (ln & 15);   // 0..RW-1
     if (m0 + row < M) a.T[(size_t)(base + m0 + row) * RW + col] = float_to_half_bits(v);
   }
-  if (threadIdx.x == 0) a.cnt[blockIdx.x] = 0;
 }
 
 int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st) {
-  if (p.rp == 0) return MILO_OK;
+  const int nrt = d->n_w * p.rp / 16;                   // rank tiles in total
+  const int per = p.rp ? p.lr_tiles_per_block : 1;      // 1 (decode) or nrt (prefill)
+  const int rank_blocks = p.rp ? nrt / per : 0;
+  const int xs_blocks = p.dec_mt ? 1 : 0;
+  if (rank_blocks + xs_blocks == 0) return MILO_OK;
   LowrankArgs a;
   a.x = d->x;
   a.sorted_pairs = d->sorted_pairs;
@@ -142,23 +179,24 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
     a.rank[f] = d->w[f < d->n_w ? f : 0].rank;
   }
   a.T = (uint16_t*)(ws + p.off_t);
-  a.part = (float*)(ws + p.off_lr_part);
-  a.cnt = (int32_t*)(ws + p.off_lr_cnt);
+  a.xsum = (float*)(ws + p.off_xs);
+  a.xoff = a.xsum + (size_t)d->num_experts * (d->K / kGroup) * kDecodeMaxRows;
   a.K = d->K;
   a.gather_div = d->gather_div;
   a.num_experts = d->num_experts;
   a.n_w = d->n_w;
   a.rp = p.rp;
   a.max_rank = d->max_rank;
-  a.kchunks = p.lr_kchunks;
-  const int nrt = d->n_w * p.rp / 16;
-  dim3 grid(p.lr_tiles, p.lr_kchunks);
-  switch (nrt) {
+  a.xs_y = xs_blocks ? rank_blocks : -1;
+  a.dec_max_rows = p.dec_max_rows;
+  dim3 grid(p.lr_tiles, rank_blocks + xs_blocks);
+  switch (per) {
+    case 1: hipLaunchKernelGGL(lowrank_kernel<1>, grid, dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL(lowrank_kernel<2>, grid, dim3(256), 0, st, a); break;
     case 4: hipLaunchKernelGGL(lowrank_kernel<4>, grid, dim3(256), 0, st, a); break;
     case 8: hipLaunchKernelGGL(lowrank_kernel<8>, grid, dim3(256), 0, st, a); break;
     default:
-      set_error("internal: unsupported rank-tile count %d", nrt);
+      set_error("internal: unsupported rank-tile count %d", per);
       return MILO_ERR_RANK;
   }
   return hip_status(hipGetLastError(), "lowrank_kernel launch");

@@ -23,9 +23,7 @@ constexpr int kTileWords = 768;    // 3 planes x 64 lanes x 4 words
 constexpr int kTileSzWords = 128;  // 64 rows x 2 groups
 constexpr int kGroup = 64;
 constexpr int kMaxRank = 64;
-constexpr int kDecodeMaxRows = 64;  // largest expert row count of the small-M path
-constexpr int kMaxLrCounters = 2048;          // split-K counters of the low-rank pre-pass
-constexpr int kMaxDecCounters = 256 * 1024;   // (expert, n-tile) counters of the small-M kernel
+constexpr int kDecodeMaxRows = 32;  // largest expert row count of the small-M path
 
 // Per-pair constant offsets of the "off + q" float16 encoding produced by the
 // code extraction (see dequant_triplet): pair pi of a triplet holds codes at
@@ -39,8 +37,12 @@ __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// (a & mask) | b as one v_and_or_b32 (the compiler splits it into two ops when
+// both constants are literals).  mask lives in an SGPR, b in a VGPR.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b) {
-  return (a & mask) | b;
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(b));
+  return r;
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
@@ -104,7 +106,7 @@ struct GemmPlan {
   int n_tiles;       // N / 64
   int kblocks;       // K / 128
   int rp;            // compensator rank padded to 32 (0 = no compensator)
-  int lr_kchunks;    // split of K in the low-rank pre-pass
+  int lr_tiles_per_block;  // rank tiles (16 ranks) per pre-pass block
   int lr_tiles;      // grid.x of the low-rank pre-pass (16-row tiles)
   int dec_mt;        // 16-row m-tiles of the small-M kernel (0 = not launched)
   int dec_max_rows;  // experts with at most this many rows use the small-M kernel
@@ -112,7 +114,7 @@ struct GemmPlan {
   int pre_launch;    // launch the tile kernel
   int pre_tiles;     // grid.x bound of the tile kernel
   // workspace carve-up (byte offsets)
-  size_t off_lr_cnt, off_dec_cnt, off_t, off_lr_part, off_dec_part, total;
+  size_t off_t, off_xs, off_dec_part, total;
 };
 int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p);
 int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st);

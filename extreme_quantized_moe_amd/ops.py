@@ -150,12 +150,12 @@ _gemm_ws = {}
 
 
 def _workspace(dev, nbytes):
-    """A zero-filled workspace per device, grown on demand (the library leaves
-    its counters at zero after every call)."""
+    """A scratch workspace per device, grown on demand.  Calls on one stream
+    run in order, so they can share it."""
     key = dev.index
     ws = _gemm_ws.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         _gemm_ws[key] = ws
     return ws
 
@@ -186,16 +186,31 @@ def make_gemm_desc(families, x, offsets, num_pairs, epilogue, y, sorted_pairs=No
 
 def moe_w3a16_lowrank_gemm(families, x, offsets, num_pairs, epilogue, y, sorted_pairs=None,
                            gather_div=0, slot_w=None, y_rows=0, max_rows_per_expert=0,
-                           path=L.PATH_AUTO, workspace=None):
+                           path=L.PATH_AUTO, workspace=None, flags=0):
     """Routed W3A16 + low-rank grouped GEMM (see include/milo.h).  Writes y."""
     _cuda(x, offsets, y, sorted_pairs, slot_w)
     d = make_gemm_desc(families, x, offsets, num_pairs, epilogue, y, sorted_pairs, gather_div,
                        slot_w, y_rows, max_rows_per_expert, path)
+    d.flags = flags
     nbytes = int(L.lib().milo_moe_gemm_workspace_bytes(C.byref(d)))
     ws = workspace if workspace is not None else _workspace(x.device, nbytes)
     check("milo_moe_w3a16_lowrank_gemm", L.lib().milo_moe_w3a16_lowrank_gemm(
         C.byref(d), _p(ws) if nbytes else None, ws.numel() if nbytes else 0, _stream()))
     return y
+
+
+def moe_lowrank_prepass(families, x, offsets, num_pairs, epilogue, y, sorted_pairs=None,
+                        gather_div=0, slot_w=None, y_rows=0, max_rows_per_expert=0,
+                        path=L.PATH_AUTO, workspace=None):
+    """First stage of the GEMM on its own (see include/milo.h); follow with
+    moe_w3a16_lowrank_gemm(..., flags=GEMM_PREPASS_DONE) on the same workspace."""
+    _cuda(x, offsets, y, sorted_pairs, slot_w)
+    d = make_gemm_desc(families, x, offsets, num_pairs, epilogue, y, sorted_pairs, gather_div,
+                       slot_w, y_rows, max_rows_per_expert, path)
+    nbytes = int(L.lib().milo_moe_gemm_workspace_bytes(C.byref(d)))
+    ws = workspace if workspace is not None else _workspace(x.device, nbytes)
+    check("milo_moe_lowrank_prepass", L.lib().milo_moe_lowrank_prepass(
+        C.byref(d), _p(ws) if nbytes else None, ws.numel() if nbytes else 0, _stream()))
 
 
 def moe_combine(y, T, slots, out=None):

@@ -204,7 +204,14 @@ typedef struct milo_gemm_desc {
   int32_t epilogue;             /* MILO_EPI_*                                  */
   void* y;                      /* output, see MILO_EPI_*                      */
   int32_t path;                 /* MILO_PATH_*                                 */
+  int32_t flags;                /* MILO_GEMM_* bits, normally 0                */
 } milo_gemm_desc;
+
+/* desc.flags: the low-rank pre-pass of this descriptor has already been
+   enqueued (by milo_moe_lowrank_prepass, same workspace, same stream, nothing
+   else using the workspace in between); the GEMM call then enqueues only the
+   main kernel(s).  Lets a caller time or schedule the two stages separately. */
+#define MILO_GEMM_PREPASS_DONE 1
 
 /* Workspace bytes milo_moe_w3a16_lowrank_gemm needs for this descriptor. */
 size_t milo_moe_gemm_workspace_bytes(const milo_gemm_desc* desc);
@@ -222,10 +229,9 @@ size_t milo_moe_gemm_workspace_bytes(const milo_gemm_desc* desc);
  * written).  The path (small-M streaming kernel or matrix-core tile kernel)
  * is chosen per expert from its row count on the device unless forced.
  *
- * workspace: milo_moe_gemm_workspace_bytes(desc) bytes, 256-byte aligned.
- *   It MUST be zero-filled before its first use; every call leaves its
- *   synchronisation counters at zero again.  Two calls that overlap in time
- *   must not share a workspace.
+ * workspace: milo_moe_gemm_workspace_bytes(desc) bytes (may be 0), 256-byte
+ *   aligned, scratch only (no initialisation needed, contents undefined after
+ *   the call).  Two calls that overlap in time must not share a workspace.
  * Constraints: N % 64 == 0, K % 128 == 0, N, K <= 65536, 1 <= num_experts
  *   <= 256, num_pairs <= 1048576, x/y/U/V 16-byte aligned; for SWIGLU both
  *   families have the same N, K, max_rank.
@@ -233,6 +239,17 @@ size_t milo_moe_gemm_workspace_bytes(const milo_gemm_desc* desc);
 int32_t milo_moe_w3a16_lowrank_gemm(const milo_gemm_desc* desc,
                                     void* workspace, size_t ws_bytes,
                                     void* stream);
+
+/*
+ * The first stage of milo_moe_w3a16_lowrank_gemm on its own: the per-pair
+ * low-rank products t_i = x_i . V_e^T (fp32 accumulation, stored as fp16 in
+ * the workspace), [talk] MiLo Algorithm (W_out = W_quant + U V).  Follow it
+ * with milo_moe_w3a16_lowrank_gemm on the same descriptor, workspace and
+ * stream with MILO_GEMM_PREPASS_DONE set.  Same validation and workspace rules
+ * as the GEMM call; a no-op when max_rank == 0 or num_pairs == 0.
+ */
+int32_t milo_moe_lowrank_prepass(const milo_gemm_desc* desc, void* workspace,
+                                 size_t ws_bytes, void* stream);
 
 /*
  * Weighted combine: out[t][h] = sum over j = 0..slots-1, in that order, of

@@ -112,12 +112,24 @@ def test_small_moe(path, epi):
     assert_close(got, want, f"small moe {path} {epi}")
 
 
-@pytest.mark.parametrize("T", [1, 7, 33, 64])
-def test_decode_row_counts(T):
+@pytest.mark.parametrize("T,path", [(1, "decode"), (7, "decode"), (16, "decode"), (17, "decode"),
+                                    (32, "decode"), (33, "auto"), (64, "auto")])
+def test_decode_row_counts(T, path):
     m = _m()
     got, want = _moe_case(E=4, S=0, N=128, K=256, ranks=[16, 32, 48, 64], T=T, k=2,
-                          epilogue=m.EPI_SWIGLU, path=PATHS["decode"], seed=T)
-    assert_close(got, want, f"decode T={T}")
+                          epilogue=m.EPI_SWIGLU, path=PATHS[path], seed=T)
+    assert_close(got, want, f"{path} T={T}")
+
+
+@pytest.mark.parametrize("T,epi", [(4, "route"), (16, "swiglu"), (30, "route")])
+def test_decode_split_k(T, epi):
+    """Few experts and a long K: the small-M kernel splits K over blocks and
+    the reduce kernel adds the splits."""
+    m = _m()
+    epilogue = {"swiglu": m.EPI_SWIGLU, "route": m.EPI_ROUTE_SCALE}[epi]
+    got, want = _moe_case(E=2, S=0, N=128, K=4096, ranks=[16, 64], T=T, k=1,
+                          epilogue=epilogue, path=PATHS["decode"], seed=100 + T)
+    assert_close(got, want, f"split-K T={T} {epi}")
 
 
 @pytest.mark.parametrize("T", [100, 300])
