@@ -152,10 +152,17 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
   p->lr_tiles = (P + 15) / 16 + d->num_experts;
   const int nrt = d->n_w * p->rp / 16;
   p->lr_tiles_per_block = rows_bound <= kDecodeMaxRows ? 1 : (nrt > 0 ? nrt : 1);
+  p->lr_kchunks = 1;
+  if (rows_bound <= kDecodeMaxRows) {  // few rows: split K over blocks (~16 steps each)
+    int kc = d->K / 32 / 16;
+    p->lr_kchunks = kc > 16 ? 16 : (kc < 1 ? 1 : kc);
+  }
 
   size_t off = 0;
   p->off_t = off;
   off += round_up((size_t)P * d->n_w * p->rp * 2, 256);
+  p->off_tpart = off;
+  if (p->lr_kchunks > 1 && p->rp) off += round_up((size_t)p->lr_kchunks * P * d->n_w * p->rp * 4, 256);
   p->off_xs = off;
   if (p->dec_mt) off += round_up((size_t)2 * d->num_experts * (d->K / kGroup) * kDecodeMaxRows * 4, 256);
   p->off_dec_part = off;

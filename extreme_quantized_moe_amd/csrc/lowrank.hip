@@ -1,4 +1,5 @@
-// Low-rank pre-pass of the compensated GEMM: T = x_rows(e) . V_e^T per pair.
+// Low-rank pre-pass of the compensated GEMM: T = x_rows(e) . V_e^T per pair,
+// plus the per-(row, group) activation sums the small-M kernel folds with.
 //
 // [talk] = "MiLo: Efficient Quantized MoE Inference with Mixture of Low-Rank
 // Compensators" (MLSys 2025 talk write-up), MiLo Algorithm: the weight is
@@ -9,11 +10,14 @@
 // T . U^T as two more matrix-core K-steps.
 //
 // Grid: x = 16-row tiles over all experts (expert by expert), y = groups of
-// NRT rank tiles (16 ranks each).  At decode each block takes one rank tile
-// (many small blocks stream V in parallel); at prefill one block takes all
-// rank tiles of its rows (the activation rows are read once).  The four waves
-// of a block split the 32-wide K steps round robin, their partial sums are
-// added in LDS in wave order (deterministic, no cross-block synchronisation).
+// NRT rank tiles (16 ranks each) plus, when the small-M kernel runs, one more
+// index for the group sums, z = K chunks.  At decode each block takes one rank
+// tile of one K chunk (many small blocks stream V in parallel); at prefill one
+// block takes every rank tile of its rows over the whole K (the activation
+// rows are read once).  The four waves of a block split the chunk's 32-wide K
+// steps round robin and are added in LDS in wave order.  With several K chunks
+// the chunk sums go to a float32 buffer and lowrank_finalize adds them in
+// chunk order (deterministic; no cross-block synchronisation in a kernel).
 #include "milo_internal.hpp"
 
 namespace milo {
@@ -25,11 +29,13 @@ struct LowrankArgs {
   const uint16_t* V[2];
   const int32_t* rank[2];
   uint16_t* T;        // fp16 [P][n_w * rp]
-  float* xsum;        // [expert][group][64 rows]: sum of x over the group
-  float* xoff;        // [expert][group][64 rows]: sum of x * off over the group
-  int K, gather_div, num_experts, n_w, rp, max_rank;
+  float* part;        // fp32 [kchunks][P][n_w * rp] when kchunks > 1
+  float* xsum;        // [expert][group][32 rows]: sum of x over the group
+  float* xoff;        // [expert][group][32 rows]: sum of x * off over the group
+  int K, gather_div, num_experts, n_w, rp, max_rank, num_pairs;
   int xs_y;           // blockIdx.y of the group-sum blocks (-1: none)
   int dec_max_rows;   // experts with more rows need no group sums
+  int kchunks;
 };
 
 // Offset (64 or 8) of the "off + q" float16 encoding of the code at position
@@ -40,31 +46,36 @@ __device__ __forceinline__ float code_offset(int kk) {
   return (float)pair_offset(c >> 1);
 }
 
-// Per (row, 64-wide group): sum of x and sum of x * off, in a fixed order.
+// Per (row, 64-wide group) of this block's K chunk: sum of x and sum of
+// x * off, each in a fixed order.
 __device__ void group_sums(const LowrankArgs& a, int e, int m0, int M) {
   if (M > a.dec_max_rows) return;                 // tile-kernel expert
-  const int row = threadIdx.x >> 4;
-  const int m = m0 + row;
-  if (m >= M) return;
   const int base = a.offsets[e];
-  const int xr = a.gather_div > 0 ? a.sorted_pairs[base + m] / a.gather_div : base + m;
   const int G = a.K / kGroup;
-  for (int g = threadIdx.x & 15; g < G; g += 16) {
+  const int g0 = (int)((int64_t)G * blockIdx.z / a.kchunks);
+  const int g1 = (int)((int64_t)G * (blockIdx.z + 1) / a.kchunks);
+  const int ng = g1 - g0;
+  for (int o = threadIdx.x; o < 16 * ng; o += blockDim.x) {
+    const int row = o / ng, g = g0 + (o - row * ng);
+    const int m = m0 + row;
+    if (m >= M) continue;
+    const int xr = a.gather_div > 0 ? a.sorted_pairs[base + m] / a.gather_div : base + m;
     const uint16_t* p = a.x + (size_t)xr * a.K + (size_t)g * kGroup;
+    f16x8 v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = *(const f16x8*)(p + 8 * c);
     float sx = 0.f, so = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const f16x8 v = *(const f16x8*)(p + 8 * c);
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float xv = (float)v[t];
+        const float xv = (float)v[c][t];
         sx += xv;
         so = __builtin_fmaf(xv, code_offset(64 * (g & 1) + 8 * c + t), so);
       }
-    }
-    const size_t o = ((size_t)e * G + g) * kDecodeMaxRows + m;
-    a.xsum[o] = sx;
-    a.xoff[o] = so;
+    const size_t oi = ((size_t)e * G + g) * kDecodeMaxRows + m;
+    a.xsum[oi] = sx;
+    a.xoff[oi] = so;
   }
 }
 
@@ -111,12 +122,14 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowrankArgs a) {
   // B operand rows (compensator ranks) of this lane, per rank tile
   const uint16_t* vp[NRT];
   bool vok[NRT];
+  bool any = false;
 #pragma unroll
   for (int t = 0; t < NRT; ++t) {
     const int tr = tr0 + t;
     const int f = tr / tiles_per_w;
     const int j = (tr % tiles_per_w) * 16 + (lane & 15);
     vok[t] = j < a.rank[f][e];
+    any |= (tr % tiles_per_w) * 16 < a.rank[f][e];
     vp[t] = a.V[f] + ((size_t)e * a.max_rank + (vok[t] ? j : 0)) * a.K + 8 * (lane >> 4);
   }
 
@@ -124,29 +137,33 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowrankArgs a) {
 #pragma unroll
   for (int t = 0; t < NRT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K steps s = wave + 4 i; loads batched four steps at a time
+  // this block's K steps [s0, s1); wave takes s0 + wave + 4 i, loads batched by 4
   const int ksteps = a.K / 32;
-  int s = wave;
-  for (; s + 12 < ksteps; s += 16) {
-    f16x8 xa[4], vb[4][NRT];
+  const int s0 = (int)((int64_t)ksteps * blockIdx.z / a.kchunks);
+  const int s1 = (int)((int64_t)ksteps * (blockIdx.z + 1) / a.kchunks);
+  if (any) {
+    int s = s0 + wave;
+    for (; s + 12 < s1; s += 16) {
+      f16x8 xa[4], vb[4][NRT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      xa[u] = row_ok ? *(const f16x8*)(xp + 32 * (s + 4 * u)) : f16x8{};
+      for (int u = 0; u < 4; ++u) {
+        xa[u] = row_ok ? *(const f16x8*)(xp + 32 * (s + 4 * u)) : f16x8{};
 #pragma unroll
-      for (int t = 0; t < NRT; ++t)
-        vb[u][t] = vok[t] ? *(const f16x8*)(vp[t] + 32 * (s + 4 * u)) : f16x8{};
+        for (int t = 0; t < NRT; ++t)
+          vb[u][t] = vok[t] ? *(const f16x8*)(vp[t] + 32 * (s + 4 * u)) : f16x8{};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int t = 0; t < NRT; ++t) acc[t] = mfma16x16x32(xa[u], vb[u][t], acc[t]);
     }
+    for (; s < s1; s += 4) {
+      const f16x8 xa = row_ok ? *(const f16x8*)(xp + 32 * s) : f16x8{};
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int t = 0; t < NRT; ++t) acc[t] = mfma16x16x32(xa[u], vb[u][t], acc[t]);
-  }
-  for (; s < ksteps; s += 4) {
-    const f16x8 xa = row_ok ? *(const f16x8*)(xp + 32 * s) : f16x8{};
-#pragma unroll
-    for (int t = 0; t < NRT; ++t) {
-      const f16x8 vb = vok[t] ? *(const f16x8*)(vp[t] + 32 * s) : f16x8{};
-      acc[t] = mfma16x16x32(xa, vb, acc[t]);
+      for (int t = 0; t < NRT; ++t) {
+        const f16x8 vb = vok[t] ? *(const f16x8*)(vp[t] + 32 * s) : f16x8{};
+        acc[t] = mfma16x16x32(xa, vb, acc[t]);
+      }
     }
   }
 #pragma unroll
@@ -160,7 +177,23 @@ __global__ void __launch_bounds__(256) lowrank_kernel(LowrankArgs a) {
     const float v = ((red[0][t][ln][r] + red[1][t][ln][r]) + red[2][t][ln][r]) + red[3][t][ln][r];
     const int row = 4 * (ln >> 4) + r;            // 0..15 within the tile
     const int col = (tr0 + t) * 16 + (ln & 15);   // 0..RW-1
-    if (m0 + row < M) a.T[(size_t)(base + m0 + row) * RW + col] = float_to_half_bits(v);
+    if (m0 + row >= M) continue;
+    const size_t i = (size_t)(base + m0 + row) * RW + col;
+    if (a.kchunks == 1)
+      a.T[i] = float_to_half_bits(v);
+    else
+      a.part[(size_t)blockIdx.z * a.num_pairs * RW + i] = v;
+  }
+}
+
+// T = fp16(sum of the K-chunk partial products, in chunk order)
+__global__ void __launch_bounds__(256) lowrank_finalize(const float* __restrict__ part, int kchunks,
+                                                        size_t n, uint16_t* __restrict__ T) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    float v = 0.f;
+    for (int c = 0; c < kchunks; ++c) v += part[(size_t)c * n + i];
+    T[i] = float_to_half_bits(v);
   }
 }
 
@@ -179,6 +212,7 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
     a.rank[f] = d->w[f < d->n_w ? f : 0].rank;
   }
   a.T = (uint16_t*)(ws + p.off_t);
+  a.part = (float*)(ws + p.off_tpart);
   a.xsum = (float*)(ws + p.off_xs);
   a.xoff = a.xsum + (size_t)d->num_experts * (d->K / kGroup) * kDecodeMaxRows;
   a.K = d->K;
@@ -187,9 +221,11 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
   a.n_w = d->n_w;
   a.rp = p.rp;
   a.max_rank = d->max_rank;
+  a.num_pairs = d->num_pairs;
   a.xs_y = xs_blocks ? rank_blocks : -1;
   a.dec_max_rows = p.dec_max_rows;
-  dim3 grid(p.lr_tiles, rank_blocks + xs_blocks);
+  a.kchunks = p.lr_kchunks;
+  dim3 grid(p.lr_tiles, rank_blocks + xs_blocks, p.lr_kchunks);
   switch (per) {
     case 1: hipLaunchKernelGGL(lowrank_kernel<1>, grid, dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL(lowrank_kernel<2>, grid, dim3(256), 0, st, a); break;
@@ -199,7 +235,14 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
       set_error("internal: unsupported rank-tile count %d", per);
       return MILO_ERR_RANK;
   }
-  return hip_status(hipGetLastError(), "lowrank_kernel launch");
+  int32_t rc = hip_status(hipGetLastError(), "lowrank_kernel launch");
+  if (rc != MILO_OK || p.lr_kchunks == 1 || p.rp == 0) return rc;
+  const size_t n = (size_t)d->num_pairs * d->n_w * p.rp;
+  size_t g = (n + 255) / 256;
+  if (g > 4096) g = 4096;
+  hipLaunchKernelGGL(lowrank_finalize, dim3((unsigned)g), dim3(256), 0, st, (const float*)a.part,
+                     p.lr_kchunks, n, a.T);
+  return hip_status(hipGetLastError(), "lowrank_finalize launch");
 }
 
 }  // namespace milo

@@ -20,6 +20,8 @@ namespace milo {
 constexpr int kRouteBlock = 256;
 constexpr int kMaxExperts = 256;
 constexpr int kBitWords = kRouteBlock / 32;
+constexpr int kMaxK = 8;
+constexpr int kMaxSlots = 16;
 
 __device__ __forceinline__ int slot_expert(const int32_t* ids_row, int j, int k, int E) {
   return j < k ? ids_row[j] : E + (j - k);
@@ -55,55 +57,82 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
   for (int x = tid; x < kMaxExperts * kBitWords; x += kRouteBlock) (&bits[0][0])[x] = 0u;
   __syncthreads();
 
-  int my_ids[16];
+  // per-thread arrays are indexed only by unrolled loop counters (registers)
+  int my_ids[kMaxSlots];
+  int rank[kMaxSlots];
+#pragma unroll
+  for (int j = 0; j < kMaxSlots; ++j) {
+    my_ids[j] = 0;
+    rank[j] = 0;
+  }
   if (t < T) {
     const float* row = logits + (size_t)t * E;
-    uint32_t taken[kMaxExperts / 32];
+    // k passes; pass j picks the largest logit (lowest id on ties) among the
+    // experts not picked by passes 0..j-1
+    float bv[kMaxK];
+    int bi[kMaxK];
+    float mx = -INFINITY;
+    for (int e = 0; e < E; ++e) mx = fmaxf(mx, row[e]);
 #pragma unroll
-    for (int x = 0; x < kMaxExperts / 32; ++x) taken[x] = 0u;
-    float mx = row[0];
-    for (int e = 1; e < E; ++e) mx = fmaxf(mx, row[e]);
+    for (int j = 0; j < kMaxK; ++j) {
+      bv[j] = -INFINITY;
+      bi[j] = -1;
+      if (j < k) {
+        for (int e = 0; e < E; ++e) {
+          bool taken = false;
+#pragma unroll
+          for (int jj = 0; jj < j; ++jj) taken |= (bi[jj] == e);
+          const float v = row[e];
+          if (!taken && (bi[j] < 0 || v > bv[j])) {
+            bv[j] = v;
+            bi[j] = e;
+          }
+        }
+      }
+    }
     float den = 0.f;
     for (int e = 0; e < E; ++e) den += expf(row[e] - mx);
-    float sel[8];
+    float sel[kMaxK];
     float selsum = 0.f;
-    for (int j = 0; j < k; ++j) {
-      int best = -1;
-      float bv = 0.f;
-      for (int e = 0; e < E; ++e) {
-        if ((taken[e >> 5] >> (e & 31)) & 1u) continue;
-        const float v = row[e];
-        if (best < 0 || v > bv) { best = e; bv = v; }
-      }
-      taken[best >> 5] |= 1u << (best & 31);
-      my_ids[j] = best;
-      sel[j] = expf(bv - mx);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      sel[j] = j < k ? expf(bv[j] - mx) : 0.f;
       selsum += sel[j];
     }
-    for (int j = 0; j < k; ++j) {
-      const float w = renorm ? sel[j] / selsum : sel[j] / den;
-      ids[(size_t)t * k + j] = my_ids[j];
-      topw[(size_t)t * k + j] = w;
-      slot_w[(size_t)t * slots + j] = w;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k) {
+        const float w = renorm ? sel[j] / selsum : sel[j] / den;
+        ids[(size_t)t * k + j] = bi[j];
+        topw[(size_t)t * k + j] = w;
+        slot_w[(size_t)t * slots + j] = w;
+        my_ids[j] = bi[j];
+      }
     }
-    for (int j = k; j < slots; ++j) {
-      my_ids[j] = E + (j - k);
-      slot_w[(size_t)t * slots + j] = 1.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxSlots; ++j) {
+      if (j >= k && j < slots) {
+        my_ids[j] = E + (j - k);
+        slot_w[(size_t)t * slots + j] = 1.0f;
+      }
     }
-    for (int j = 0; j < slots; ++j)
-      atomicOr(&bits[my_ids[j]][tid >> 5], 1u << (tid & 31));
+#pragma unroll
+    for (int j = 0; j < kMaxSlots; ++j)
+      if (j < slots) atomicOr(&bits[my_ids[j]][tid >> 5], 1u << (tid & 31));
   }
   __syncthreads();
 
   // stable rank of each slot among earlier tokens of this block with the same expert
-  int rank[16];
   if (t < T) {
-    for (int j = 0; j < slots; ++j) {
-      const uint32_t* row = bits[my_ids[j]];
-      int c = 0;
-      for (int w = 0; w < (tid >> 5); ++w) c += __popc(row[w]);
-      c += __popc(row[tid >> 5] & ((1u << (tid & 31)) - 1u));
-      rank[j] = c;
+#pragma unroll
+    for (int j = 0; j < kMaxSlots; ++j) {
+      if (j < slots) {
+        const uint32_t* brow = bits[my_ids[j]];
+        int c = 0;
+        for (int w = 0; w < (tid >> 5); ++w) c += __popc(brow[w]);
+        c += __popc(brow[tid >> 5] & ((1u << (tid & 31)) - 1u));
+        rank[j] = c;
+      }
     }
   }
   int count = 0;
@@ -119,17 +148,23 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
     __syncthreads();
     if (tid < ET) offsets[tid] = scan_lds[tid];
     if (t < T) {
-      for (int j = 0; j < slots; ++j) {
-        const int s = t * slots + j;
-        const int pos = scan_lds[my_ids[j]] + rank[j];
-        sorted_pairs[pos] = s;
-        pair_pos[s] = pos;
+#pragma unroll
+      for (int j = 0; j < kMaxSlots; ++j) {
+        if (j < slots) {
+          const int s = t * slots + j;
+          const int pos = scan_lds[my_ids[j]] + rank[j];
+          sorted_pairs[pos] = s;
+          pair_pos[s] = pos;
+        }
       }
     }
   } else {
     if (tid < ET) block_counts[(size_t)blockIdx.x * ET + tid] = count;
-    if (t < T)
-      for (int j = 0; j < slots; ++j) pair_pos[t * slots + j] = rank[j];
+    if (t < T) {
+#pragma unroll
+      for (int j = 0; j < kMaxSlots; ++j)
+        if (j < slots) pair_pos[t * slots + j] = rank[j];
+    }
   }
 }
 
