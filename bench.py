@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="only measure plain device read (sum) and copy bandwidth on 4 GiB")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times "
                          "(calibrates HBM byte counters against a known size)")
@@ -227,6 +229,23 @@ def main():
     from synth import configs as SC
 
     torch.cuda.set_device(0)
+    if args.hbm_probe:
+        n = 4 << 30
+        x = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        y = torch.empty_like(x)
+        out = {}
+        for name, fn, nbytes in (("read_sum", lambda: x.sum(), n), ("copy", lambda: y.copy_(x), 2 * n)):
+            fn()
+            torch.cuda.synchronize()
+            s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s_.record()
+            for _ in range(10):
+                fn()
+            e_.record()
+            torch.cuda.synchronize()
+            out[name + "_GBps"] = round(10 * nbytes / (s_.elapsed_time(e_) * 1e-3) / 1e9, 1)
+        print(json.dumps({"hbm_probe_bytes": n, **out}))
+        return
     if args.copy_probe_mb:
         n = args.copy_probe_mb << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
