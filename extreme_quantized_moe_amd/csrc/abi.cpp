@@ -55,9 +55,6 @@ GemmArgs make_gemm_args(const milo_gemm_desc* d, const GemmPlan& p, char* ws) {
   a.K = d->K;
   a.kblocks = p.kblocks;
   a.n_tiles = p.n_tiles;
-  a.groups = d->K / kGroup;
-  a.xsum = (const float*)(ws + p.off_xs);
-  a.xoff = a.xsum + (size_t)d->num_experts * a.groups * kDecodeMaxRows;
   a.gather_div = d->gather_div;
   a.num_experts = d->num_experts;
   a.n_w = d->n_w;
@@ -138,33 +135,30 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
   p->pre_tiles = (P + 127) / 128 + d->num_experts;
 
   if (p->dec_mt) {
-    // split K only when the (expert, n-tile) blocks cannot fill the chip;
-    // splits are summed by a separate reduce kernel
+    // persistent grid: two blocks per CU for one m-tile, one for two; split K
+    // only when the (expert, n-tile) items cannot fill that grid, and keep at
+    // least four K blocks per split (one per wave)
+    const int slots = p->dec_mt == 1 ? 512 : 256;
     const int active = d->num_experts < P ? d->num_experts : P;
-    const int blocks = active * p->n_tiles;
-    int ks = blocks >= 384 ? 1 : (512 + blocks - 1) / blocks;
-    int ks_max = p->kblocks / 8;
+    const int items = active * p->n_tiles;
+    int ks = items >= slots ? 1 : (slots + items - 1) / items;
+    int ks_max = p->kblocks / 4;
     if (ks_max < 1) ks_max = 1;
     if (ks > ks_max) ks = ks_max;
-    if (ks < 1) ks = 1;
     p->dec_ksplit = ks;
+    p->dec_blocks = items * ks < slots ? items * ks : slots;
   }
   p->lr_tiles = (P + 15) / 16 + d->num_experts;
   const int nrt = d->n_w * p->rp / 16;
   p->lr_tiles_per_block = rows_bound <= kDecodeMaxRows ? 1 : (nrt > 0 ? nrt : 1);
-  p->lr_kchunks = 1;
-  if (rows_bound <= kDecodeMaxRows) {  // few rows: split K over blocks (~16 steps each)
-    int kc = d->K / 32 / 16;
-    p->lr_kchunks = kc > 16 ? 16 : (kc < 1 ? 1 : kc);
-  }
 
   size_t off = 0;
   p->off_t = off;
   off += round_up((size_t)P * d->n_w * p->rp * 2, 256);
-  p->off_tpart = off;
-  if (p->lr_kchunks > 1 && p->rp) off += round_up((size_t)p->lr_kchunks * P * d->n_w * p->rp * 4, 256);
-  p->off_xs = off;
-  if (p->dec_mt) off += round_up((size_t)2 * d->num_experts * (d->K / kGroup) * kDecodeMaxRows * 4, 256);
+  p->off_xg = off;
+  if (p->dec_mt && d->gather_div > 0) off += round_up((size_t)P * d->K * 2, 256);
+  p->off_pw = off;
+  if (p->dec_mt && d->epilogue == MILO_EPI_ROUTE_SCALE) off += round_up((size_t)P * 4, 256);
   p->off_dec_part = off;
   if (p->dec_ksplit > 1)
     off += round_up((size_t)p->dec_ksplit * d->num_experts * p->n_tiles * d->n_w * p->dec_mt * 16 * 64 * 4, 256);

@@ -17,10 +17,9 @@ struct GemmArgs {
   const uint16_t* T;       // fp16 [P][n_w * rp] low-rank pre-pass output
   void* y;
   float* part;             // split-K partial sums
-  const float* xsum;       // per (expert, group, row <= 64): sum of x over the group
-  const float* xoff;       // ... and sum of x * off over the group
+  const float* pw;         // per pair (sorted order): route weight (small-M path)
   int64_t words_per_expert, sz_per_expert;
-  int N, K, kblocks, n_tiles, groups, gather_div, num_experts, n_w, rp, max_rank;
+  int N, K, kblocks, n_tiles, gather_div, num_experts, n_w, rp, max_rank;
   int epilogue, ksplit, dec_max_rows, pre_min_rows;
 };
 

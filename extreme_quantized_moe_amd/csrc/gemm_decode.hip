@@ -6,172 +6,231 @@
 // copy of the weights in memory), and asynchronous global loads to hide
 // memory latency.  MiLo Algorithm: W_out = W_quant + U V.
 //
-// At decode an expert sees a handful of rows, so the kernel streams the
-// packed weights once from HBM: block (n-tile of 64 output features, expert,
-// K split) = 4 waves, wave w takes the 128-wide K blocks w, w+4, ... of the
-// block's range.  Per K block a wave issues three 16-byte loads per lane for
-// the 64 x 128 codes (one per plane of layout v1), two for the scale/zero
-// words, four per 16-row m-tile for the activation fragments and four per
-// m-tile for the per-group activation sums; these loads run DEPTH-1 K blocks
-// ahead of the block being consumed (a register ring).
+// At decode an expert sees a handful of rows and the layer is a stream of
+// packed weights.  Work items are (expert, 64-row n-tile, K split) over the
+// experts with rows; a persistent grid of blocks takes items round robin.
+// The four waves of a block split each item's 128-wide K blocks (wave w:
+// blocks w, w+4, ...); each wave runs one continuous stream of K blocks across
+// all of its items, with the loads of the next DEPTH-1 K blocks in flight in a
+// register ring while the current one is consumed, so item boundaries do not
+// drain the pipeline.  Every load in the stream is issued unconditionally
+// (past the end a wave re-reads its last block), so the compiler's wait counts
+// stay exact.
 //
-// Dequantization is folded out of the inner product.  The extraction turns a
-// pair of int3 codes into two exact float16 values off + q (off = 64 or 8,
-// one v_and_or_b32 per pair), and the matrix cores compute, per 64-wide group
-// g, P = sum_k x_k (off_k + q_k) starting from the accumulator value
-// -(sum_k x_k off_k) - z sum_k x_k (both sums precomputed per row and group by
-// the pre-pass), so that P = sum_k x_k (q_k - z) up to fp32 rounding; then
-// y += s P in fp32.  No weight is rounded to float16.  The expert's rows are
-// the A operand (16 per m-tile, rows beyond the expert's count are zero) and
-// the codes the B operand.  Waves are summed in LDS in wave order.  With one
-// K split the block applies the epilogue itself; with several, each split
-// stores its sum and gemm_decode_reduce adds the splits in split order and
-// applies the epilogue (no cross-block synchronisation inside a kernel).  The
-// low-rank term is added by wave 0 of split 0.
+// Dequantization is folded out of the inner product.  One v_and_or_b32 turns
+// a pair of int3 codes into two exact fp16 values off + q (off = 64 or 8);
+// per 64-wide group the matrix cores compute P = sum_k x_k (off_k + q_k) from
+// an accumulator preset to -(sum_k x_k off_k) - z (sum_k x_k), so that
+// P = sum_k x_k (q_k - z), and y += s P in fp32.  The two activation sums are
+// themselves matrix-core products of the activation fragments with constant
+// fragments (all ones, and the offsets), so no weight is ever rounded to fp16
+// and no extra data is loaded.  The expert's rows are the A operand (16 per
+// m-tile; rows past the expert's count are zero), the codes the B operand.
+//
+// Item end: the low-rank term (x V^T) U^T is added by wave f for weight family
+// f (its T and U fragments were loaded when the item started), the waves are
+// summed in LDS in wave order, and the epilogue stores fp16 (NONE / SWIGLU) or
+// scales by the pair's route weight and scatters fp32 (ROUTE_SCALE).  With
+// several K splits each split stores its sum and gemm_decode_reduce adds the
+// splits in split order (no cross-block synchronisation inside a kernel).
 #include "gemm_common.hpp"
 
 namespace milo {
 
-struct WTile {
-  u32x4 q[3];
-  u32x4 z[2];
-};
+constexpr int kMaxE = 256;
 
 template <int MT, int NW>
 struct Stage {
-  WTile w[NW];
-  f16x8 x[MT][4];
+  u32x4 q[NW][3];    // three planes of the 64 x 128 code tile
+  u32x4 z[NW][2];    // eight scale/zero words of this lane's rows
+  f16x8 x[MT][4];    // activation fragments of the four 32-wide K steps
 };
 
-__device__ __forceinline__ void load_wtile(WTile& t, const uint32_t* tp, const uint32_t* sp, int lane) {
-  t.q[0] = *(const u32x4*)(tp + 4 * lane);
-  t.q[1] = *(const u32x4*)(tp + 256 + 4 * lane);
-  t.q[2] = *(const u32x4*)(tp + 512 + 4 * lane);
-  const uint32_t* s = sp + 8 * (lane & 15);
-  t.z[0] = *(const u32x4*)(s);
-  t.z[1] = *(const u32x4*)(s + 4);
+struct Item {
+  int e, nt, ks, base, M, kbA, kbB;
+};
+
+struct Cursor {
+  int it;            // item index
+  int kb;            // K block of this wave in the item
+  bool valid;
+  Item item;
+};
+
+struct DecShared {
+  int off[kMaxE + 1];
+  int act[kMaxE];
+  int rank[2][kMaxE];
+  int nact;
+};
+
+// fp16 constant fragments: all ones, and the per-slot offset of step `step`
+__device__ __forceinline__ f16x8 ones_frag() {
+  const u32x4 u = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+  return __builtin_bit_cast(f16x8, u);
+}
+__device__ __forceinline__ f16x8 offset_frag(int step) {
+  u32x4 u;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) u[v] = pair_offset(4 * step + v) == 64 ? 0x54005400u : 0x48004800u;
+  return __builtin_bit_cast(f16x8, u);
 }
 
-// sz word for row group i and group g of the tile: index 2 i + g of the lane's 8
-__device__ __forceinline__ uint32_t sz_word(const WTile& t, int i, int g) {
-  const int idx = 2 * i + g;
-  return idx < 4 ? t.z[0][idx] : t.z[1][idx - 4];
-}
+template <int MT, int NW, int EPI>
+struct Dec {
+  const GemmArgs& a;
+  const DecShared& sh;
+  int lane, wave, total;
 
-template <int MT>
-__device__ __forceinline__ void consume_tile(const WTile& t, const f16x8 (&xa)[MT][4],
-                                             const f32x4 (&xs)[2][MT], const f32x4 (&xo)[2][MT],
-                                             f32x4 (&acc)[MT][4]) {
+  __device__ __forceinline__ Dec(const GemmArgs& a_, const DecShared& sh_, int total_)
+      : a(a_), sh(sh_), lane(threadIdx.x & 63), wave(threadIdx.x >> 6), total(total_) {}
+
+  __device__ __forceinline__ void enter(Cursor& c, int it) const {
+    if (it >= total) {
+      c.valid = false;          // keep the last item and K block for dummy loads
+      return;
+    }
+    // all item fields are wave-uniform: keep them in scalar registers
+    const int per_e = a.n_tiles * a.ksplit;
+    const int ai = it / per_e;
+    const int r = it - ai * per_e;
+    Item& m = c.item;
+    m.e = __builtin_amdgcn_readfirstlane(sh.act[ai]);
+    m.nt = r / a.ksplit;
+    m.ks = r - m.nt * a.ksplit;
+    m.base = __builtin_amdgcn_readfirstlane(sh.off[m.e]);
+    m.M = __builtin_amdgcn_readfirstlane(sh.off[m.e + 1]) - m.base;
+    m.kbA = (int)((int64_t)a.kblocks * m.ks / a.ksplit);
+    m.kbB = (int)((int64_t)a.kblocks * (m.ks + 1) / a.ksplit);
+    c.it = it;
+    c.kb = m.kbA + __builtin_amdgcn_readfirstlane(wave);
+    c.valid = true;
+  }
+  __device__ __forceinline__ bool last(const Cursor& c) const { return c.kb + 4 >= c.item.kbB; }
+  __device__ __forceinline__ void next(Cursor& c) const {
+    if (!c.valid) return;
+    if (!last(c)) c.kb += 4;
+    else enter(c, c.it + gridDim.x);
+  }
+
+  // A wave whose first K block lies past the item's range (K splits of fewer
+  // than four blocks) gets one null element: real codes of the item's first
+  // block with zero activations, which adds exactly zero.
+  __device__ __forceinline__ void load(Stage<MT, NW>& S, const Cursor& c) const {
+    const Item& m = c.item;
+    const bool live = c.kb < m.kbB;
+    const int kb = live ? c.kb : m.kbA;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t h[16];
-    extract_triplet(t.q[0][i], t.q[1][i], t.q[2][i], h);
+    for (int f = 0; f < NW; ++f) {
+      const uint32_t* tp = a.packed[f] + m.e * a.words_per_expert +
+                           ((size_t)m.nt * a.kblocks + kb) * kTileWords + 4 * lane;
+      S.q[f][0] = *(const u32x4*)(tp);
+      S.q[f][1] = *(const u32x4*)(tp + 256);
+      S.q[f][2] = *(const u32x4*)(tp + 512);
+      const uint32_t* sp = a.sz[f] + m.e * a.sz_per_expert +
+                           ((size_t)m.nt * a.kblocks + kb) * kTileSzWords + 8 * (lane & 15);
+      S.z[f][0] = *(const u32x4*)(sp);
+      S.z[f][1] = *(const u32x4*)(sp + 4);
+    }
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const uint32_t w = sz_word(t, i, g);
-      const float s = half_bits_to_float(w & 0xFFFFu);
-      const float z = half_bits_to_float(w >> 16);
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = mt * 16 + (lane & 15);
+      const bool ok = live && row < m.M;
+      const uint16_t* xp =
+          a.x + (size_t)(m.base + (row < m.M ? row : 0)) * a.K + (size_t)kb * kTileK + 8 * (lane >> 4);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 p;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = __builtin_fmaf(-z, xs[g][mt][r], -xo[g][mt][r]);
-#pragma unroll
-        for (int ss = 0; ss < 2; ++ss) {
-          const int step = 2 * g + ss;
-          const u32x4 u = {h[4 * step], h[4 * step + 1], h[4 * step + 2], h[4 * step + 3]};
-          p = mfma16x16x32(xa[mt][step], __builtin_bit_cast(f16x8, u), p);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[mt][i][r] = __builtin_fmaf(s, p[r], acc[mt][i][r]);
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 v = *(const f16x8*)(xp + 32 * s);
+        S.x[mt][s] = ok ? v : f16x8{};
       }
     }
   }
-}
 
-template <int MT, int NW>
-struct DecodeCtx {
-  const uint32_t* tbase[NW];
-  const uint32_t* sbase[NW];
-  const uint16_t* xp[MT];
-  const float* lds_xs;    // [local group][16 MT rows], then xo at + lds_half
-  int lds_half;
-  int g0;                 // first group of the block's K range
-  bool xok[MT];
-  int lane;
-
-  __device__ __forceinline__ void load(Stage<MT, NW>& S, int kb) const {
-#pragma unroll
-    for (int f = 0; f < NW; ++f)
-      load_wtile(S.w[f], tbase[f] + (size_t)kb * kTileWords, sbase[f] + (size_t)kb * kTileSzWords, lane);
+  __device__ __forceinline__ void consume(const Stage<MT, NW>& S, f32x4 (&acc)[NW][MT][4]) const {
+    const f16x8 one = ones_frag();
+    // activation sums per group: xs = sum x, xo = sum x * off (rows of this lane)
+    f32x4 xs[MT][2], xo[MT][2];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        S.x[mt][s] = xok[mt] ? *(const f16x8*)(xp[mt] + (size_t)kb * kTileK + 32 * s) : f16x8{};
-  }
-  __device__ __forceinline__ void consume(const Stage<MT, NW>& S, int kb, f32x4 (&acc)[NW][MT][4]) const {
-    f32x4 xs[2][MT], xo[2][MT];
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const float* q = lds_xs + (2 * kb + g - g0) * (16 * MT) + mt * 16 + 4 * (lane >> 4);
-        xs[g][mt] = *(const f32x4*)q;
-        xo[g][mt] = *(const f32x4*)(q + lds_half);
+      for (int g = 0; g < 2; ++g) {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        xs[mt][g] = mfma16x16x32(S.x[mt][2 * g], one, zero);
+        xs[mt][g] = mfma16x16x32(S.x[mt][2 * g + 1], one, xs[mt][g]);
+        xo[mt][g] = mfma16x16x32(S.x[mt][2 * g], offset_frag(2 * g), zero);
+        xo[mt][g] = mfma16x16x32(S.x[mt][2 * g + 1], offset_frag(2 * g + 1), xo[mt][g]);
       }
 #pragma unroll
-    for (int f = 0; f < NW; ++f) consume_tile<MT>(S.w[f], S.x, xs, xo, acc[f]);
+    for (int f = 0; f < NW; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t h[16];
+        extract_triplet(S.q[f][0][i], S.q[f][1][i], S.q[f][2][i], h);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int idx = 2 * i + g;
+          const uint32_t w = idx < 4 ? S.z[f][0][idx] : S.z[f][1][idx - 4];
+          const float sc = half_bits_to_float(w & 0xFFFFu);
+          const float zp = half_bits_to_float(w >> 16);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            f32x4 p;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = __builtin_fmaf(-zp, xs[mt][g][r], -xo[mt][g][r]);
+#pragma unroll
+            for (int ss = 0; ss < 2; ++ss) {
+              const int step = 2 * g + ss;
+              const u32x4 u = {h[4 * step], h[4 * step + 1], h[4 * step + 2], h[4 * step + 3]};
+              p = mfma16x16x32(S.x[mt][step], __builtin_bit_cast(f16x8, u), p);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[f][mt][i][r] = __builtin_fmaf(sc, p[r], acc[f][mt][i][r]);
+          }
+        }
+      }
   }
 };
 
-// Final values -> outputs.  res[f][c] holds output (m, n) = (o >> 6, o & 63)
-// with o = threadIdx.x + 256 c of the 64-wide n-tile nt of expert e.
-template <int NW, int KPER>
-__device__ __forceinline__ void decode_epilogue(const GemmArgs& a, int e, int nt, int base, int M,
-                                                const float (&res)[NW][KPER]) {
-#pragma unroll
-  for (int c = 0; c < KPER; ++c) {
-    const int o = threadIdx.x + 256 * c;
-    const int m = o >> 6, n = o & 63;
-    if (m >= M) continue;
-    const int i = base + m;
-    const int col = nt * kTileRows + n;
-    if (a.epilogue == MILO_EPI_ROUTE_SCALE) {
-      const int s = a.sorted_pairs[i];
-      ((float*)a.y)[(size_t)s * a.N + col] = res[0][c] * a.slot_w[s];
-    } else {
-      float v = res[0][c];
-      if (NW == 2) v = silu(v) * res[NW - 1][c];
-      ((uint16_t*)a.y)[(size_t)i * a.N + col] = float_to_half_bits(v);
-    }
-  }
-}
+// Per-item values loaded when an item starts and used at its end.
+template <int MT>
+struct ItemLate {
+  f16x8 t[MT][2];     // low-rank T fragments (rows x 32 ranks) of family `wave`
+  f16x8 u[4][2];      // U fragments (64 n rows x 32 ranks) of family `wave`
+  int32_t sp[MT * 4]; // ROUTE_SCALE: slot index of each output row of this thread
+  float pw[MT * 4];   // ROUTE_SCALE: route weight of those rows
+};
 
-template <int MT, int NW, int DEPTH>
+template <int MT, int NW, int EPI, int DEPTH>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 2 : 1, MT == 1 ? 2 : 1)))
 gemm_decode_kernel(GemmArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nt = blockIdx.x, e = blockIdx.y, ks = blockIdx.z;
-  const int base = a.offsets[e];
-  const int M = a.offsets[e + 1] - base;
-  if (M == 0 || M > a.dec_max_rows) return;
+  __shared__ DecShared sh;
+  constexpr int kOut = MT * 16 * 64;       // outputs per family per item
+  constexpr int kPer = kOut / 256;         // per thread
+  __shared__ float red[4][NW][kOut];
 
-  DecodeCtx<MT, NW> cx;
-  cx.lane = lane;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + (lane & 15);
-    cx.xok[mt] = m < M;
-    int xr = 0;
-    if (cx.xok[mt]) xr = a.gather_div > 0 ? a.sorted_pairs[base + m] / a.gather_div : base + m;
-    cx.xp[mt] = a.x + (size_t)xr * a.K + 8 * (lane >> 4);
+  // ---- experts with rows for this path, and their ranks
+  for (int e = threadIdx.x; e <= a.num_experts; e += 256) sh.off[e] = a.offsets[e];
+  for (int e = threadIdx.x; e < a.num_experts; e += 256) {
+    sh.rank[0][e] = a.rp ? a.rank[0][e] : 0;
+    sh.rank[1][e] = a.rp ? a.rank[NW - 1][e] : 0;
   }
-#pragma unroll
-  for (int f = 0; f < NW; ++f) {
-    cx.tbase[f] = a.packed[f] + e * a.words_per_expert + (size_t)nt * a.kblocks * kTileWords;
-    cx.sbase[f] = a.sz[f] + e * a.sz_per_expert + (size_t)nt * a.kblocks * kTileSzWords;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int e = 0; e < a.num_experts; ++e) {
+      const int M = sh.off[e + 1] - sh.off[e];
+      if (M > 0 && M <= a.dec_max_rows) sh.act[n++] = e;
+    }
+    sh.nact = n;
   }
+  __syncthreads();
+  const int total = __builtin_amdgcn_readfirstlane(sh.nact) * a.n_tiles * a.ksplit;
+  if ((int)blockIdx.x >= total) return;
+
+  Dec<MT, NW, EPI> D(a, sh, total);
+  const int lane = D.lane, wave = D.wave;
+  const int RW = a.n_w * a.rp;
+  const int lrf = wave < NW ? wave : 0;   // weight family whose low-rank term this wave adds
 
   f32x4 acc[NW][MT][4];
 #pragma unroll
@@ -181,117 +240,137 @@ gemm_decode_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[f][mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K range of this block and the K blocks of this wave: kbw + 4 j, j < cnt
-  const int kbA = (int)((int64_t)a.kblocks * ks / a.ksplit);
-  const int kbB = (int)((int64_t)a.kblocks * (ks + 1) / a.ksplit);
-  const int kb0 = kbA + wave;
-  const int kb1 = kbB;
-  const int cnt = kb0 < kb1 ? (kb1 - kb0 + 3) / 4 : 0;
-
-  // group sums of the block's rows over its K range -> LDS
-  extern __shared__ __align__(16) float smem[];
-  const int ngr = 2 * (kbB - kbA);
-  cx.lds_xs = smem;
-  cx.lds_half = ngr * 16 * MT;
-  cx.g0 = 2 * kbA;
-  for (int o = threadIdx.x; o < ngr * 16 * MT; o += 256) {
-    const int gl = o / (16 * MT), m = o - gl * (16 * MT);
-    const size_t src = ((size_t)e * a.groups + cx.g0 + gl) * kDecodeMaxRows + m;
-    smem[o] = a.xsum[src];
-    smem[cx.lds_half + o] = a.xoff[src];
-  }
-  __syncthreads();
-
-  Stage<MT, NW> ring[DEPTH];
+  // item-start loads: low-rank fragments (every wave loads, waves >= NW
+  // ignore them) and the epilogue's row metadata.  Addresses are clamped to
+  // valid memory and masked values replaced, so every load is issued.
+  ItemLate<MT> late;
+  auto load_late = [&](const Item& m) {
+    if (a.rp > 0) {
+      const int rk = sh.rank[lrf][m.e];
 #pragma unroll
-  for (int d = 0; d < DEPTH - 1; ++d)
-    if (d < cnt) cx.load(ring[d], kb0 + 4 * d);
-  int j = 0;
-  // K block of ring entry consumed at step (j + d): kb0 + 4 (j + d)
-  // steady state: every prefetch in range, so loads are unconditional and
-  // each consume waits only for the batch issued DEPTH-1 steps earlier
-  for (; j + 2 * DEPTH - 1 <= cnt; j += DEPTH) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      cx.load(ring[(d + DEPTH - 1) % DEPTH], kb0 + 4 * (j + d + DEPTH - 1));
-      cx.consume(ring[d], kb0 + 4 * (j + d), acc);
-    }
-  }
-  // tail: at most 2 DEPTH - 2 blocks left
-#pragma unroll
-  for (int t = 0; t < 2; ++t, j += DEPTH) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int jn = j + d + DEPTH - 1;
-      if (jn < cnt) cx.load(ring[(d + DEPTH - 1) % DEPTH], kb0 + 4 * jn);
-      if (j + d < cnt) cx.consume(ring[d], kb0 + 4 * (j + d), acc);
-    }
-  }
-
-  // low-rank term (x V^T) U^T: two more K steps per 32 ranks, added once
-  if (wave == 0 && ks == 0 && a.rp > 0) {
-    const int RW = a.n_w * a.rp;
-#pragma unroll
-    for (int f = 0; f < NW; ++f) {
-      const int rk = a.rank[f][e];
-      for (int s2 = 0; s2 < a.rp / 32; ++s2) {
+      for (int s2 = 0; s2 < 2; ++s2) {
         const int j0 = 32 * s2 + 8 * (lane >> 4);
-        f16x8 ta[MT];
+        const bool jok = j0 < rk;
+        const int jc = jok ? j0 : 0;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const int m = mt * 16 + (lane & 15);
-          ta[mt] = m < M ? *(const f16x8*)(a.T + (size_t)(base + m) * RW + f * a.rp + j0) : f16x8{};
+          const int row = mt * 16 + (lane & 15);
+          const bool ok = jok && row < m.M;
+          const f16x8 v = *(const f16x8*)(a.T + (size_t)(m.base + (row < m.M ? row : 0)) * RW + lrf * a.rp + jc);
+          late.t[mt][s2] = ok ? v : f16x8{};
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int n = nt * kTileRows + 16 * i + (lane & 15);
-          f16x8 ub = f16x8{};
-          if (j0 < rk) ub = *(const f16x8*)(a.U[f] + ((size_t)e * a.N + n) * a.max_rank + j0);
+          const int n = m.nt * kTileRows + 16 * i + (lane & 15);
+          const f16x8 v = *(const f16x8*)(a.U[lrf] + ((size_t)m.e * a.N + n) * a.max_rank + jc);
+          late.u[i][s2] = jok ? v : f16x8{};
+        }
+      }
+    }
+    if (EPI == MILO_EPI_ROUTE_SCALE) {
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[f][mt][i] = mfma16x16x32(ta[mt], ub, acc[f][mt][i]);
+      for (int c = 0; c < kPer; ++c) {
+        const int row = (threadIdx.x + 256 * c) >> 6;
+        const int i = m.base + (row < m.M ? row : 0);
+        late.sp[c] = a.sorted_pairs[i];
+        late.pw[c] = a.pw[i];
+      }
+    }
+  };
+
+  auto finish_item = [&](const Item& m) {
+    // low-rank term of family `wave` (added once: by the first K split)
+    if (wave < NW && a.rp > 0 && m.ks == 0) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        if (32 * s2 >= a.rp) break;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int f = 0; f < NW; ++f)
+              if (f == wave) acc[f][mt][i] = mfma16x16x32(late.t[mt][s2], late.u[i][s2], acc[f][mt][i]);
+      }
+    }
+    __syncthreads();   // previous item's readers of red are done
+#pragma unroll
+    for (int f = 0; f < NW; ++f)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = mt * 16 + 4 * (lane >> 4) + r, n = 16 * i + (lane & 15);
+            red[wave][f][row * 64 + n] = acc[f][mt][i][r];
+          }
+          acc[f][mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    __syncthreads();
+    float res[NW][kPer];
+#pragma unroll
+    for (int f = 0; f < NW; ++f)
+#pragma unroll
+      for (int c = 0; c < kPer; ++c) {
+        const int o = threadIdx.x + 256 * c;
+        res[f][c] = ((red[0][f][o] + red[1][f][o]) + red[2][f][o]) + red[3][f][o];
+      }
+    if (a.ksplit > 1) {
+      float* mine = a.part + (((size_t)m.ks * a.num_experts + m.e) * a.n_tiles + m.nt) * (NW * kOut);
+#pragma unroll
+      for (int f = 0; f < NW; ++f)
+#pragma unroll
+        for (int c = 0; c < kPer; ++c) mine[f * kOut + threadIdx.x + 256 * c] = res[f][c];
+      return;
+    }
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const int o = threadIdx.x + 256 * c;
+      const int row = o >> 6, n = o & 63;
+      if (row >= m.M) continue;
+      const int col = m.nt * kTileRows + n;
+      if (EPI == MILO_EPI_ROUTE_SCALE) {
+        ((float*)a.y)[(size_t)late.sp[c] * a.N + col] = res[0][c] * late.pw[c];
+      } else {
+        float v = res[0][c];
+        if (EPI == MILO_EPI_SWIGLU) v = silu(v) * res[NW - 1][c];
+        ((uint16_t*)a.y)[(size_t)(m.base + row) * a.N + col] = float_to_half_bits(v);
+      }
+    }
+  };
+
+  Cursor pf, cs;
+  D.enter(pf, blockIdx.x);
+  cs = pf;
+  load_late(cs.item);
+  Stage<MT, NW> ring[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH - 1; ++d) {
+    D.load(ring[d], pf);
+    D.next(pf);
+  }
+  while (cs.valid) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      if (cs.valid) {
+        D.load(ring[(d + DEPTH - 1) % DEPTH], pf);
+        D.next(pf);
+        D.consume(ring[d], acc);
+        if (D.last(cs)) {
+          finish_item(cs.item);
+          D.next(cs);
+          if (cs.valid) load_late(cs.item);
+        } else {
+          D.next(cs);
         }
       }
     }
   }
-
-  // ---- cross-wave reduction (wave order), one weight family at a time
-  constexpr int kOut = MT * 16 * 64;       // outputs per family per block
-  constexpr int kPer = kOut / 256;         // per thread
-  float (*red)[kOut] = (float (*)[kOut])smem;   // reuses the group-sum LDS
-  float res[NW][kPer];
-#pragma unroll
-  for (int f = 0; f < NW; ++f) {
-    __syncthreads();
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mt * 16 + 4 * (lane >> 4) + r, n = 16 * i + (lane & 15);
-          red[wave][m * 64 + n] = acc[f][mt][i][r];
-        }
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < kPer; ++c) {
-      const int o = threadIdx.x + 256 * c;
-      res[f][c] = ((red[0][o] + red[1][o]) + red[2][o]) + red[3][o];
-    }
-  }
-
-  if (a.ksplit > 1) {  // partial sums for gemm_decode_reduce
-    float* mine = a.part + (((size_t)ks * a.num_experts + e) * a.n_tiles + nt) * (NW * kOut);
-#pragma unroll
-    for (int f = 0; f < NW; ++f)
-#pragma unroll
-      for (int c = 0; c < kPer; ++c) mine[f * kOut + threadIdx.x + 256 * c] = res[f][c];
-    return;
-  }
-  decode_epilogue<NW, kPer>(a, e, nt, base, M, res);
 }
 
 // Sum of the K splits in split order, then the epilogue.
-template <int MT, int NW>
+template <int MT, int NW, int EPI>
 __global__ void __launch_bounds__(256) gemm_decode_reduce(GemmArgs a) {
   const int nt = blockIdx.x, e = blockIdx.y;
   const int base = a.offsets[e];
@@ -314,19 +393,40 @@ __global__ void __launch_bounds__(256) gemm_decode_reduce(GemmArgs a) {
         if ((o >> 6) < M) res[f][c] += p[f * kOut + o];
       }
   }
-  decode_epilogue<NW, kPer>(a, e, nt, base, M, res);
+#pragma unroll
+  for (int c = 0; c < kPer; ++c) {
+    const int o = threadIdx.x + 256 * c;
+    const int row = o >> 6, n = o & 63;
+    if (row >= M) continue;
+    const int i = base + row;
+    const int col = nt * kTileRows + n;
+    if (EPI == MILO_EPI_ROUTE_SCALE) {
+      const int s = a.sorted_pairs[i];
+      ((float*)a.y)[(size_t)s * a.N + col] = res[0][c] * a.pw[i];
+    } else {
+      float v = res[0][c];
+      if (EPI == MILO_EPI_SWIGLU) v = silu(v) * res[NW - 1][c];
+      ((uint16_t*)a.y)[(size_t)i * a.N + col] = float_to_half_bits(v);
+    }
+  }
 }
 
-template <int MT, int NW>
-static void launch_mt(const GemmArgs& a, dim3 grid, hipStream_t st) {
+template <int MT, int NW, int EPI>
+static void launch_one(const GemmArgs& a, int blocks, int num_experts, hipStream_t st) {
   constexpr int depth = (MT == 1 && NW == 1) ? 3 : 2;
-  const int max_kb = (a.kblocks + a.ksplit - 1) / a.ksplit + 1;
-  size_t lds = (size_t)2 * 2 * max_kb * 16 * MT * sizeof(float);
-  const size_t red = (size_t)4 * MT * 16 * 64 * sizeof(float);
-  if (lds < red) lds = red;
-  hipLaunchKernelGGL((gemm_decode_kernel<MT, NW, depth>), grid, dim3(256), lds, st, a);
+  hipLaunchKernelGGL((gemm_decode_kernel<MT, NW, EPI, depth>), dim3(blocks), dim3(256), 0, st, a);
   if (a.ksplit > 1)
-    hipLaunchKernelGGL((gemm_decode_reduce<MT, NW>), dim3(grid.x, grid.y), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_decode_reduce<MT, NW, EPI>), dim3(a.n_tiles, num_experts), dim3(256), 0,
+                       st, a);
+}
+
+template <int MT>
+static void launch_mt(const GemmArgs& a, int epi, int blocks, int num_experts, hipStream_t st) {
+  switch (epi) {
+    case MILO_EPI_SWIGLU: launch_one<MT, 2, MILO_EPI_SWIGLU>(a, blocks, num_experts, st); break;
+    case MILO_EPI_ROUTE_SCALE: launch_one<MT, 1, MILO_EPI_ROUTE_SCALE>(a, blocks, num_experts, st); break;
+    default: launch_one<MT, 1, MILO_EPI_NONE>(a, blocks, num_experts, st); break;
+  }
 }
 
 GemmArgs make_gemm_args(const milo_gemm_desc* d, const GemmPlan& p, char* ws);
@@ -335,11 +435,11 @@ int32_t launch_gemm_decode(const milo_gemm_desc* d, const GemmPlan& p, char* ws,
   if (p.dec_mt == 0) return MILO_OK;
   GemmArgs a = make_gemm_args(d, p, ws);
   a.part = (float*)(ws + p.off_dec_part);
-  dim3 grid(p.n_tiles, d->num_experts, p.dec_ksplit);
-  const bool two = d->n_w == 2;
+  if (d->gather_div > 0) a.x = (const uint16_t*)(ws + p.off_xg);   // pair-ordered rows
+  a.pw = (const float*)(ws + p.off_pw);
   switch (p.dec_mt) {
-    case 1: two ? launch_mt<1, 2>(a, grid, st) : launch_mt<1, 1>(a, grid, st); break;
-    case 2: two ? launch_mt<2, 2>(a, grid, st) : launch_mt<2, 1>(a, grid, st); break;
+    case 1: launch_mt<1>(a, d->epilogue, p.dec_blocks, d->num_experts, st); break;
+    case 2: launch_mt<2>(a, d->epilogue, p.dec_blocks, d->num_experts, st); break;
     default: set_error("internal: bad m-tile count %d", p.dec_mt); return MILO_ERR_ARG;
   }
   return hip_status(hipGetLastError(), "gemm_decode_kernel launch");

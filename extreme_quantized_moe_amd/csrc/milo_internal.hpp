@@ -107,15 +107,15 @@ struct GemmPlan {
   int kblocks;       // K / 128
   int rp;            // compensator rank padded to 32 (0 = no compensator)
   int lr_tiles_per_block;  // rank tiles (16 ranks) per pre-pass block
-  int lr_kchunks;          // K chunks of the pre-pass (partials added by a finalize kernel)
   int lr_tiles;      // grid.x of the low-rank pre-pass (16-row tiles)
   int dec_mt;        // 16-row m-tiles of the small-M kernel (0 = not launched)
   int dec_max_rows;  // experts with at most this many rows use the small-M kernel
   int dec_ksplit;    // split-K factor of the small-M kernel
+  int dec_blocks;    // persistent grid of the small-M kernel
   int pre_launch;    // launch the tile kernel
   int pre_tiles;     // grid.x bound of the tile kernel
   // workspace carve-up (byte offsets)
-  size_t off_t, off_tpart, off_xs, off_dec_part, total;
+  size_t off_t, off_xg, off_pw, off_dec_part, total;
 };
 int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p);
 int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st);
