@@ -142,10 +142,10 @@ class Layer:
         wsp, wsb = p(self.ws), self.ws.numel()
         chk("prepass13", lib.milo_moe_lowrank_prepass(C.byref(self.d13), wsp, wsb, stream))
         if ev13 is not None:
-            ev13[0].record()
+            TIMER.record(ev13[0], stream)
         chk("gemm13", lib.milo_moe_w3a16_lowrank_gemm(C.byref(self.d13), wsp, wsb, stream))
         if ev13 is not None:
-            ev13[1].record()
+            TIMER.record(ev13[1], stream)
         chk("prepass2", lib.milo_moe_lowrank_prepass(C.byref(self.d2), wsp, wsb, stream))
         chk("gemm2", lib.milo_moe_w3a16_lowrank_gemm(C.byref(self.d2), wsp, wsb, stream))
         chk("combine", lib.milo_moe_combine(p(self.Y), cfg.T, self.slots, cfg.H, p(self.out), stream))
@@ -215,6 +215,42 @@ def cpu_baseline(cfg, layer, offsets, budget_s):
                   f"pairs) in {t_route + t_exp:.1f} s, scaled x{scale:.2f} by pairs to the whole layer",
         "layer_seconds": layer_s,
     }
+
+
+class HipTimer:
+    """HIP timing events on the library's stream.  They are created with
+    hipEventDisableSystemFence: a default event ends with a system-scope
+    release (an L2 writeback) that costs several microseconds between the
+    kernels it brackets; a timing-only event needs no such fence, and the
+    device-wide synchronize before the read-out orders everything."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import torch
+        path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        self.h = C.CDLL(path if os.path.exists(path) else "libamdhip64.so.7")
+        self.h.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+        self.h.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        self.h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+
+    def event(self):
+        e = C.c_void_p()
+        rc = self.h.hipEventCreateWithFlags(C.byref(e), self.DISABLE_SYSTEM_FENCE)
+        assert rc == 0, f"hipEventCreateWithFlags: {rc}"
+        return e
+
+    def record(self, e, stream):
+        rc = self.h.hipEventRecord(e, C.c_void_p(stream))
+        assert rc == 0, f"hipEventRecord: {rc}"
+
+    def ms(self, a, b):
+        f = C.c_float()
+        rc = self.h.hipEventElapsedTime(C.byref(f), a, b)
+        assert rc == 0, f"hipEventElapsedTime: {rc}"
+        return f.value
+
+
+TIMER = None
 
 
 def main():
@@ -287,20 +323,21 @@ def main():
     for i in range(args.warmup):
         run_step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    global TIMER
+    TIMER = HipTimer()
+    evs = [(TIMER.event(), TIMER.event()) for _ in range(args.steps)]
+    start, stop = TIMER.event(), TIMER.event()
     torch.cuda.synchronize()
     t_host = time.perf_counter()
-    start.record()
+    TIMER.record(start, stream)
     for i in range(args.steps):
         run_step(i, evs[i])
-    stop.record()
+    TIMER.record(stop, stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
-    ms_total = start.elapsed_time(stop)
+    ms_total = TIMER.ms(start, stop)
     ms_step = ms_total / args.steps
-    k13_us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1000.0
+    k13_us = sum(TIMER.ms(a, b) for a, b in evs) / len(evs) * 1000.0
 
     # work accounting (after the timed region)
     works = []

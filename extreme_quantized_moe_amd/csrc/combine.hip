@@ -16,11 +16,16 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     const int64_t t = i / hq;
     const int h4 = (int)(i - t * hq);
     const float4* src = (const float4*)(y + (size_t)t * slots * H) + h4;
-    float4 acc = src[0];
-    for (int j = 1; j < slots; ++j) {
-      const float4 v = src[(size_t)j * hq];
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
+    float4 v[16];                         // all slot loads issued before the sum
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < slots) v[j] = src[(size_t)j * hq];
+    float4 acc = v[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j)
+      if (j < slots) {
+        acc.x += v[j].x; acc.y += v[j].y; acc.z += v[j].z; acc.w += v[j].w;
+      }
     uint2 o;
     o.x = (uint32_t)float_to_half_bits(acc.x) | ((uint32_t)float_to_half_bits(acc.y) << 16);
     o.y = (uint32_t)float_to_half_bits(acc.z) | ((uint32_t)float_to_half_bits(acc.w) << 16);

@@ -10,12 +10,16 @@
 // matrix cores) and stored as float16 for the GEMM kernels, which add
 // T . U^T as two more matrix-core K-steps.
 //
-// Grid: x = 16-row tiles over all experts (expert by expert); y = groups of
-// NRT rank tiles (16 ranks each), plus one "aux" index for the gather / pair
-// weights.  At decode a block is 16 waves on one rank tile (the waves split
-// the 32-wide K steps round robin, many blocks stream V in parallel); at
-// prefill it is 4 waves on every rank tile of its rows (rows read once).
-// Wave partial sums are added in LDS in wave order (deterministic).
+// Grid: x = 16-row tiles over all experts (expert by expert); y = compensator
+// ranks (decode) or groups of NRT rank tiles of 16 ranks (prefill), plus one
+// "aux" index for the gather / pair weights.
+// At decode (at most 32 rows per expert) a block computes one rank j of T for
+// its rows as plain dot products: the 256 threads read V row j in consecutive
+// 16-byte chunks (fully coalesced) and multiply with the same chunks of each
+// row; the per-thread partial sums are added in LDS in a fixed tree order.
+// At prefill a block is 4 waves on every rank tile of its rows on the matrix
+// cores (the activation rows are read once); wave partial sums are added in
+// LDS in wave order.
 #include "milo_internal.hpp"
 
 namespace milo {
@@ -62,12 +66,94 @@ __device__ void prepass_aux(const PrepassArgs& a, int e, int m0, int M) {
     a.pw[i] = a.slot_w[a.sorted_pairs[i]];
   }
   if (!a.xg || M > a.dec_max_rows) return;
+  // copy the tile's rows in pair order, eight 16-byte chunks in flight per thread
   const int chunks = a.K / 8;                     // 16-byte chunks per row
-  for (int o = threadIdx.x; o < rows * chunks; o += blockDim.x) {
-    const int r = o / chunks, c = o - r * chunks;
+  const int n = rows * chunks;
+  for (int o0 = threadIdx.x; o0 < n; o0 += 8 * blockDim.x) {
+    u32x4 v[8];
+    size_t dst[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int o = o0 + u * blockDim.x;
+      dst[u] = 0;
+      if (o < n) {
+        const int r = o / chunks, c = o - r * chunks;
+        const int i = base + m0 + r;
+        const int xr = a.sorted_pairs[i] / a.gather_div;
+        v[u] = *(const u32x4*)(a.x + (size_t)xr * a.K + 8 * c);
+        dst[u] = (size_t)i * a.K + 8 * c;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (o0 + u * blockDim.x < n) *(u32x4*)(a.xg + dst[u]) = v[u];
+  }
+}
+
+// Decode form: block (16-row tile, rank j over all families), 512 threads.
+// The rows of the tile are rounded up to R2 (a power of two) and each row gets
+// 512 / R2 consecutive threads, which stride over the 16-byte chunks of V row j
+// and of the token row, eight chunks per batch of loads.  The partial sums of a
+// row are reduced in a fixed order: a butterfly inside each wave, then the
+// waves of that row in ascending order.
+constexpr int kDotThreads = 512;
+constexpr int kDotBatch = 8;
+
+__global__ void __launch_bounds__(kDotThreads) prepass_dot_kernel(PrepassArgs a) {
+  __shared__ float part[kDotThreads / 64];
+  int e, m0, M;
+  if (!find_tile16(a.offsets, a.num_experts, blockIdx.x, &e, &m0, &M)) return;
+  if ((int)blockIdx.y == a.aux_y) {
+    prepass_aux(a, e, m0, M);
+    return;
+  }
+  const int base = a.offsets[e];
+  const int RW = a.n_w * a.rp;
+  const int f = blockIdx.y / a.rp, j = blockIdx.y - f * a.rp;
+  const int rows = (M - m0) < 16 ? (M - m0) : 16;
+  const int tid = threadIdx.x;
+  uint16_t* tout = a.T + (size_t)(base + m0) * RW + f * a.rp + j;
+  if (j >= a.rank[f][e]) {                        // beyond the expert's rank: T = 0
+    if (tid < rows) tout[(size_t)tid * RW] = 0;
+    return;
+  }
+  const int R2 = rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : 16;
+  const int G = kDotThreads / R2;                 // threads per row, 32 .. 512
+  const int r = tid / G, g = tid - r * G;
+  const int chunks = a.K / 8;
+  float acc = 0.f;
+  if (r < rows) {
     const int i = base + m0 + r;
-    const int xr = a.sorted_pairs[i] / a.gather_div;
-    *(u32x4*)(a.xg + (size_t)i * a.K + 8 * c) = *(const u32x4*)(a.x + (size_t)xr * a.K + 8 * c);
+    const int xr = a.gather_div > 0 ? a.sorted_pairs[i] / a.gather_div : i;
+    const uint16_t* xp = a.x + (size_t)xr * a.K;
+    const uint16_t* vp = a.V[f] + ((size_t)e * a.max_rank + j) * a.K;
+    for (int c0 = g; c0 < chunks; c0 += kDotBatch * G) {
+      f16x8 v[kDotBatch], xv[kDotBatch];
+#pragma unroll
+      for (int u = 0; u < kDotBatch; ++u) {
+        const int c = c0 + G * u;
+        v[u] = c < chunks ? *(const f16x8*)(vp + 8 * c) : f16x8{};
+        xv[u] = c < chunks ? *(const f16x8*)(xp + 8 * c) : f16x8{};
+      }
+#pragma unroll
+      for (int u = 0; u < kDotBatch; ++u)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc = __builtin_fmaf((float)xv[u][t], (float)v[u][t], acc);
+    }
+  }
+  const int W = G < 64 ? G : 64;
+  for (int o = W >> 1; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+  if (G < 64) {
+    if (g == 0 && r < rows) tout[(size_t)r * RW] = float_to_half_bits(acc);
+    return;
+  }
+  if ((tid & 63) == 0) part[tid >> 6] = acc;
+  __syncthreads();
+  const int wpr = G >> 6;                         // waves per row
+  if (tid < rows) {
+    float sum = 0.f;
+    for (int w = 0; w < wpr; ++w) sum += part[tid * wpr + w];
+    tout[(size_t)tid * RW] = float_to_half_bits(sum);
   }
 }
 
@@ -111,31 +197,25 @@ __global__ void __launch_bounds__(64 * NWAVES) prepass_kernel(PrepassArgs a) {
 #pragma unroll
   for (int t = 0; t < NRT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K steps s = wave + NWAVES i; loads batched UNR steps at a time
+  // K steps s = wave + NWAVES i, in batches of UNR steps whose loads are all
+  // issued before the first product (steps past the end are skipped)
   const int ksteps = a.K / 32;
   if (any) {
-    int s = wave;
-    for (; s + (UNR - 1) * NWAVES < ksteps; s += UNR * NWAVES) {
+    for (int s0 = wave; s0 < ksteps; s0 += UNR * NWAVES) {
       f16x8 xa[UNR], vb[UNR][NRT];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        xa[u] = row_ok ? *(const f16x8*)(xp + 32 * (s + NWAVES * u)) : f16x8{};
+        const int s = s0 + NWAVES * u;
+        const bool in = s < ksteps;
+        xa[u] = (in && row_ok) ? *(const f16x8*)(xp + 32 * s) : f16x8{};
 #pragma unroll
         for (int t = 0; t < NRT; ++t)
-          vb[u][t] = vok[t] ? *(const f16x8*)(vp[t] + 32 * (s + NWAVES * u)) : f16x8{};
+          vb[u][t] = (in && vok[t]) ? *(const f16x8*)(vp[t] + 32 * s) : f16x8{};
       }
 #pragma unroll
       for (int u = 0; u < UNR; ++u)
 #pragma unroll
         for (int t = 0; t < NRT; ++t) acc[t] = mfma16x16x32(xa[u], vb[u][t], acc[t]);
-    }
-    for (; s < ksteps; s += NWAVES) {
-      const f16x8 xa = row_ok ? *(const f16x8*)(xp + 32 * s) : f16x8{};
-#pragma unroll
-      for (int t = 0; t < NRT; ++t) {
-        const f16x8 vb = vok[t] ? *(const f16x8*)(vp[t] + 32 * s) : f16x8{};
-        acc[t] = mfma16x16x32(xa, vb, acc[t]);
-      }
     }
   }
 #pragma unroll
@@ -183,10 +263,13 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
   a.max_rank = d->max_rank;
   a.aux_y = aux_blocks ? rank_blocks : -1;
   a.dec_max_rows = p.dec_max_rows;
-  dim3 grid(p.lr_tiles, rank_blocks + aux_blocks);
-  if (per == 1) {
-    hipLaunchKernelGGL((prepass_kernel<1, 16, 8>), grid, dim3(1024), 0, st, a);
+  if (per == 1) {                                   // decode: one block per rank
+    const int rank_rows = p.rp ? d->n_w * p.rp : 0;
+    a.aux_y = aux_blocks ? rank_rows : -1;
+    dim3 grid(p.lr_tiles, rank_rows + aux_blocks);
+    hipLaunchKernelGGL(prepass_dot_kernel, grid, dim3(kDotThreads), 0, st, a);
   } else {
+    dim3 grid(p.lr_tiles, rank_blocks + aux_blocks);
     switch (per) {
       case 2: hipLaunchKernelGGL((prepass_kernel<2, 4, 4>), grid, dim3(256), 0, st, a); break;
       case 4: hipLaunchKernelGGL((prepass_kernel<4, 4, 4>), grid, dim3(256), 0, st, a); break;

@@ -21,6 +21,7 @@ constexpr int kRouteBlock = 256;
 constexpr int kMaxExperts = 256;
 constexpr int kBitWords = kRouteBlock / 32;
 constexpr int kMaxK = 8;
+constexpr int kLdsExperts = 64;   // logits of up to 64 experts are staged in LDS
 constexpr int kMaxSlots = 16;
 
 __device__ __forceinline__ int slot_expert(const int32_t* ids_row, int j, int k, int E) {
@@ -51,10 +52,26 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
            int32_t* __restrict__ offsets, int32_t* __restrict__ block_counts) {
   __shared__ uint32_t bits[kMaxExperts][kBitWords];
   __shared__ int scan_lds[kRouteBlock];
+  __shared__ float lg_lds[kRouteBlock * kLdsExperts];
   const int tid = threadIdx.x;
   const int t = blockIdx.x * kRouteBlock + tid;
   const int ET = E + S, slots = k + S;
   for (int x = tid; x < kMaxExperts * kBitWords; x += kRouteBlock) (&bits[0][0])[x] = 0u;
+  // stage the block's logits in LDS with coalesced loads, all issued at once
+  const bool staged = E <= kLdsExperts;
+  if (staged) {
+    const int t0 = blockIdx.x * kRouteBlock;
+    const int ntok = (T - t0) < kRouteBlock ? (T - t0) : kRouteBlock;
+    const int n = ntok * E;
+    const float* src = logits + (size_t)t0 * E;
+    float v[kLdsExperts];
+#pragma unroll
+    for (int u = 0; u < kLdsExperts; ++u)
+      if (tid + kRouteBlock * u < n) v[u] = src[tid + kRouteBlock * u];
+#pragma unroll
+    for (int u = 0; u < kLdsExperts; ++u)
+      if (tid + kRouteBlock * u < n) lg_lds[tid + kRouteBlock * u] = v[u];
+  }
   __syncthreads();
 
   // per-thread arrays are indexed only by unrolled loop counters (registers)
@@ -66,7 +83,7 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
     rank[j] = 0;
   }
   if (t < T) {
-    const float* row = logits + (size_t)t * E;
+    const float* row = staged ? lg_lds + tid * E : logits + (size_t)t * E;
     // k passes; pass j picks the largest logit (lowest id on ties) among the
     // experts not picked by passes 0..j-1
     float bv[kMaxK];
