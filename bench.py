@@ -77,7 +77,7 @@ def src_hash(files):
 class Layer:
     """One MoE layer's device weights, buffers and prebuilt call descriptors."""
 
-    def __init__(self, m, cfg, layer_idx, X, logits, path, ws):
+    def __init__(self, m, cfg, layer_idx, X, logits, path):
         import synth
         import torch
         L = m._lib
@@ -124,8 +124,9 @@ class Layer:
         lib = L.lib()
         need = max(lib.milo_moe_gemm_workspace_bytes(C.byref(self.d13)),
                    lib.milo_moe_gemm_workspace_bytes(C.byref(self.d2)))
-        assert need > 0 and ws.numel() >= need, (need, ws.numel())
-        self.ws = ws
+        assert need > 0, need
+        self.ws_need = need
+        self.ws = None            # shared workspace, attached once all layers exist
         self.P, self.T, self.slots = P, T, slots
 
     def step(self, stream, ev13=None):
@@ -304,11 +305,13 @@ def main():
     X = synth.gen_tokens(cfg, 0, device="cuda")
     t0 = time.time()
     layers = []
-    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
     for i in range(nsets):
         logits = synth.gen_logits(cfg, i if stack else 0, device="cuda")
-        layers.append(Layer(m, cfg, i if stack else 0, X, logits, path, ws) if (stack or i == 0)
-                      else Layer(m, cfg, 100 + i, X, logits, path, ws))
+        layers.append(Layer(m, cfg, i if stack else 0, X, logits, path) if (stack or i == 0)
+                      else Layer(m, cfg, 100 + i, X, logits, path))
+    ws = torch.zeros(max(lay.ws_need for lay in layers), dtype=torch.uint8, device="cuda")
+    for lay in layers:
+        lay.ws = ws
     torch.cuda.synchronize()
     log(f"weights ready in {time.time() - t0:.1f} s")
     stream = torch.cuda.current_stream().cuda_stream

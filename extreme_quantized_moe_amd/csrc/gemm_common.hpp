@@ -21,7 +21,11 @@ struct GemmArgs {
   int64_t words_per_expert, sz_per_expert;
   int N, K, kblocks, n_tiles, gather_div, num_experts, n_w, rp, max_rank;
   int epilogue, ksplit, dec_max_rows, pre_min_rows;
+  int m_lo, m_hi;          // row-count range of the experts a decode launch handles
 };
+
+struct GemmPlan;
+GemmArgs make_gemm_args(const milo_gemm_desc* d, const GemmPlan& p, char* ws);
 
 // Per-(row, group) dequantization constants: d = h * s + c_off for h = off + q.
 struct GroupConst {
@@ -52,5 +56,48 @@ __device__ __forceinline__ f16x8 dequant_step(const uint32_t h[16], int step, co
 }
 
 __device__ __forceinline__ float silu(float u) { return u / (1.f + expf(-u)); }
+
+// Sum of the K splits of a decode launch in split order, then the epilogue.
+// Partial sums are [split][expert][n-tile][family][ROWS x 64].
+template <int ROWS, int NW, int EPI>
+__global__ void __launch_bounds__(256) gemm_split_reduce(GemmArgs a) {
+  const int nt = blockIdx.x, e = blockIdx.y;
+  const int base = a.offsets[e];
+  const int M = a.offsets[e + 1] - base;
+  if (M < a.m_lo || M > a.m_hi) return;
+  constexpr int kOut = ROWS * 64;
+  constexpr int kPer = kOut / 256;
+  float res[NW][kPer];
+#pragma unroll
+  for (int f = 0; f < NW; ++f)
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) res[f][c] = 0.f;
+  for (int s = 0; s < a.ksplit; ++s) {
+    const float* p = a.part + (((size_t)s * a.num_experts + e) * a.n_tiles + nt) * (NW * kOut);
+#pragma unroll
+    for (int f = 0; f < NW; ++f)
+#pragma unroll
+      for (int c = 0; c < kPer; ++c) {
+        const int o = threadIdx.x + 256 * c;
+        if ((o >> 6) < M) res[f][c] += p[f * kOut + o];
+      }
+  }
+#pragma unroll
+  for (int c = 0; c < kPer; ++c) {
+    const int o = threadIdx.x + 256 * c;
+    const int row = o >> 6, n = o & 63;
+    if (row >= M) continue;
+    const int i = base + row;
+    const int col = nt * kTileRows + n;
+    if (EPI == MILO_EPI_ROUTE_SCALE) {
+      const int s = a.sorted_pairs[i];
+      ((float*)a.y)[(size_t)s * a.N + col] = res[0][c] * a.pw[i];
+    } else {
+      float v = res[0][c];
+      if (EPI == MILO_EPI_SWIGLU) v = silu(v) * res[NW - 1][c];
+      ((uint16_t*)a.y)[(size_t)i * a.N + col] = float_to_half_bits(v);
+    }
+  }
+}
 
 }  // namespace milo

@@ -81,9 +81,11 @@ struct Dec {
   const GemmArgs& a;
   const DecShared& sh;
   int lane, wave, total;
+  CodeConsts kc;
 
   __device__ __forceinline__ Dec(const GemmArgs& a_, const DecShared& sh_, int total_)
-      : a(a_), sh(sh_), lane(threadIdx.x & 63), wave(threadIdx.x >> 6), total(total_) {}
+      : a(a_), sh(sh_), lane(threadIdx.x & 63), wave(threadIdx.x >> 6), total(total_),
+        kc(make_code_consts()) {}
 
   __device__ __forceinline__ void enter(Cursor& c, int it) const {
     if (it >= total) {
@@ -165,7 +167,7 @@ struct Dec {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t h[16];
-        extract_triplet(S.q[f][0][i], S.q[f][1][i], S.q[f][2][i], h);
+        extract_triplet(S.q[f][0][i], S.q[f][1][i], S.q[f][2][i], h, kc);
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
           const int idx = 2 * i + g;
@@ -219,7 +221,7 @@ gemm_decode_kernel(GemmArgs a) {
     int n = 0;
     for (int e = 0; e < a.num_experts; ++e) {
       const int M = sh.off[e + 1] - sh.off[e];
-      if (M > 0 && M <= a.dec_max_rows) sh.act[n++] = e;
+      if (M >= a.m_lo && M <= a.m_hi) sh.act[n++] = e;
     }
     sh.nact = n;
   }
@@ -369,54 +371,12 @@ gemm_decode_kernel(GemmArgs a) {
   }
 }
 
-// Sum of the K splits in split order, then the epilogue.
-template <int MT, int NW, int EPI>
-__global__ void __launch_bounds__(256) gemm_decode_reduce(GemmArgs a) {
-  const int nt = blockIdx.x, e = blockIdx.y;
-  const int base = a.offsets[e];
-  const int M = a.offsets[e + 1] - base;
-  if (M == 0 || M > a.dec_max_rows) return;
-  constexpr int kOut = MT * 16 * 64;
-  constexpr int kPer = kOut / 256;
-  float res[NW][kPer];
-#pragma unroll
-  for (int f = 0; f < NW; ++f)
-#pragma unroll
-    for (int c = 0; c < kPer; ++c) res[f][c] = 0.f;
-  for (int s = 0; s < a.ksplit; ++s) {
-    const float* p = a.part + (((size_t)s * a.num_experts + e) * a.n_tiles + nt) * (NW * kOut);
-#pragma unroll
-    for (int f = 0; f < NW; ++f)
-#pragma unroll
-      for (int c = 0; c < kPer; ++c) {
-        const int o = threadIdx.x + 256 * c;
-        if ((o >> 6) < M) res[f][c] += p[f * kOut + o];
-      }
-  }
-#pragma unroll
-  for (int c = 0; c < kPer; ++c) {
-    const int o = threadIdx.x + 256 * c;
-    const int row = o >> 6, n = o & 63;
-    if (row >= M) continue;
-    const int i = base + row;
-    const int col = nt * kTileRows + n;
-    if (EPI == MILO_EPI_ROUTE_SCALE) {
-      const int s = a.sorted_pairs[i];
-      ((float*)a.y)[(size_t)s * a.N + col] = res[0][c] * a.pw[i];
-    } else {
-      float v = res[0][c];
-      if (EPI == MILO_EPI_SWIGLU) v = silu(v) * res[NW - 1][c];
-      ((uint16_t*)a.y)[(size_t)i * a.N + col] = float_to_half_bits(v);
-    }
-  }
-}
-
 template <int MT, int NW, int EPI>
 static void launch_one(const GemmArgs& a, int blocks, int num_experts, hipStream_t st) {
   constexpr int depth = (MT == 1 && NW == 1) ? 3 : 2;
   hipLaunchKernelGGL((gemm_decode_kernel<MT, NW, EPI, depth>), dim3(blocks), dim3(256), 0, st, a);
   if (a.ksplit > 1)
-    hipLaunchKernelGGL((gemm_decode_reduce<MT, NW, EPI>), dim3(a.n_tiles, num_experts), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_split_reduce<16 * MT, NW, EPI>), dim3(a.n_tiles, num_experts), dim3(256), 0,
                        st, a);
 }
 
@@ -429,14 +389,14 @@ static void launch_mt(const GemmArgs& a, int epi, int blocks, int num_experts, h
   }
 }
 
-GemmArgs make_gemm_args(const milo_gemm_desc* d, const GemmPlan& p, char* ws);
-
 int32_t launch_gemm_decode(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st) {
   if (p.dec_mt == 0) return MILO_OK;
   GemmArgs a = make_gemm_args(d, p, ws);
   a.part = (float*)(ws + p.off_dec_part);
   if (d->gather_div > 0) a.x = (const uint16_t*)(ws + p.off_xg);   // pair-ordered rows
   a.pw = (const float*)(ws + p.off_pw);
+  a.m_lo = 1;
+  a.m_hi = p.dec_max_rows;
   switch (p.dec_mt) {
     case 1: launch_mt<1>(a, d->epilogue, p.dec_blocks, d->num_experts, st); break;
     case 2: launch_mt<2>(a, d->epilogue, p.dec_blocks, d->num_experts, st); break;

@@ -50,6 +50,7 @@ template <int NW>
 __global__ void __launch_bounds__(256) gemm_prefill_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
+  const CodeConsts kc = make_code_consts();
   int e, m0, M;
   if (!find_tile128(a.offsets, a.num_experts, a.pre_min_rows, blockIdx.x, &e, &m0, &M)) return;
   const int base = a.offsets[e];
@@ -117,7 +118,7 @@ __global__ void __launch_bounds__(256) gemm_prefill_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t h[16];
-        extract_triplet(wq[0][i], wq[1][i], wq[2][i], h);
+        extract_triplet(wq[0][i], wq[1][i], wq[2][i], h, kc);
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
           const int idx = 2 * i + g;
@@ -222,7 +223,6 @@ __global__ void __launch_bounds__(256) gemm_prefill_kernel(GemmArgs a) {
     }
 }
 
-GemmArgs make_gemm_args(const milo_gemm_desc* d, const GemmPlan& p, char* ws);
 
 int32_t launch_gemm_prefill(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st) {
   if (!p.pre_launch) return MILO_OK;

@@ -37,12 +37,34 @@ __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// (a & mask) | b as one v_and_or_b32 (the compiler splits it into two ops when
-// both constants are literals).  mask lives in an SGPR, b in a VGPR.
+// Masks and float16 magic words of the code extraction, held in registers.
+// They are produced by inline asm so that the compiler cannot fold them back
+// into literals (gfx9 VOP3 encodings take no literal, and two literal
+// operands would split every v_and_or_b32 into two instructions).  Only
+// these definitions are asm: every extraction op is ordinary code, so the
+// compiler's hazard tracking sees the VALU writes that feed the matrix cores
+// (a matrix instruction reads its sources a fixed number of wait states after
+// a VALU write, and the compiler cannot insert them for results of inline asm).
+struct CodeConsts {
+  uint32_t lo, hi, b4, b5, b6;   // SGPR masks
+  uint32_t m64, m8;              // VGPR magic words: float16 64.0 / 8.0 in both halves
+};
+
+__device__ __forceinline__ CodeConsts make_code_consts() {
+  CodeConsts k;
+  asm volatile("s_mov_b32 %0, 0x00700070" : "=s"(k.lo));   // bits 4..6 of each half
+  asm volatile("s_mov_b32 %0, 0x03800380" : "=s"(k.hi));   // bits 7..9 of each half
+  asm volatile("s_mov_b32 %0, 0x00100010" : "=s"(k.b4));
+  asm volatile("s_mov_b32 %0, 0x00200020" : "=s"(k.b5));
+  asm volatile("s_mov_b32 %0, 0x00400040" : "=s"(k.b6));
+  asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(k.m64));
+  asm volatile("v_mov_b32 %0, 0x48004800" : "=v"(k.m8));
+  return k;
+}
+
+// (a & mask) | b: one v_and_or_b32 with mask in an SGPR and b in a VGPR.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(b));
-  return r;
+  return (a & mask) | b;
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
@@ -56,25 +78,21 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float v) {
 // Extract the 16 code pairs of one layout-v1 triplet (words w0, w1, w2) into
 // float16x2 words holding (off + q_even, off + q_odd) with off = pair_offset.
 __device__ __forceinline__ void extract_triplet(uint32_t w0, uint32_t w1, uint32_t w2,
-                                                uint32_t out[16]) {
-  const uint32_t M64 = 0x54005400u;  // float16 64.0 in both halves
-  const uint32_t M8 = 0x48004800u;   // float16 8.0 in both halves
-  const uint32_t LO = 0x00700070u;   // bits 4..6 of each half
-  const uint32_t HI = 0x03800380u;   // bits 7..9 of each half
+                                                uint32_t out[16], const CodeConsts& k) {
   uint32_t w[3] = {w0, w1, w2};
 #pragma unroll
   for (int p = 0; p < 3; ++p) {
     uint32_t a = w[p];
     uint32_t sh = a >> 6;
-    out[5 * p + 0] = and_or(a << 3, LO, M64);   // bits 1..3  -> 4..6
-    out[5 * p + 1] = and_or(a, LO, M64);        // bits 4..6
-    out[5 * p + 2] = and_or(a, HI, M8);         // bits 7..9
-    out[5 * p + 3] = and_or(sh, LO, M64);       // bits 10..12 -> 4..6
-    out[5 * p + 4] = and_or(sh, HI, M8);        // bits 13..15 -> 7..9
+    out[5 * p + 0] = and_or(a << 3, k.lo, k.m64);   // bits 1..3  -> 4..6
+    out[5 * p + 1] = and_or(a, k.lo, k.m64);        // bits 4..6
+    out[5 * p + 2] = and_or(a, k.hi, k.m8);         // bits 7..9
+    out[5 * p + 3] = and_or(sh, k.lo, k.m64);       // bits 10..12 -> 4..6
+    out[5 * p + 4] = and_or(sh, k.hi, k.m8);        // bits 13..15 -> 7..9
   }
-  uint32_t s = and_or(w0 << 4, 0x00100010u, M64);
-  s = and_or(w1 << 5, 0x00200020u, s);
-  out[15] = and_or(w2 << 6, 0x00400040u, s);
+  uint32_t s = and_or(w0 << 4, k.b4, k.m64);
+  s = and_or(w1 << 5, k.b5, s);
+  out[15] = and_or(w2 << 6, k.b6, s);
 }
 
 // (off + q) -> (q - z) * s as float16, computed as fma(h, s, -(off + z) s) in
