@@ -135,10 +135,10 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
   p->pre_tiles = (P + 127) / 128 + d->num_experts;
 
   if (p->dec_mt) {
-    // persistent grid: two blocks per CU for one m-tile, one for two; split K
+    // persistent grid: two blocks per CU; split K
     // only when the (expert, n-tile) items cannot fill that grid, and keep at
     // least four K blocks per split (one per wave)
-    const int slots = p->dec_mt == 1 ? 512 : 256;
+    const int slots = 512;
     const int active = d->num_experts < P ? d->num_experts : P;
     const int items = active * p->n_tiles;
     int ks = items >= slots ? 1 : (slots + items - 1) / items;

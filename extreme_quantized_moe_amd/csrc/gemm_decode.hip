@@ -9,11 +9,15 @@
 // At decode an expert sees a handful of rows and the layer is a stream of
 // packed weights.  Work items are (expert, 64-row n-tile, K split) over the
 // experts with rows; a persistent grid of blocks takes items round robin.
-// The four waves of a block split each item's 128-wide K blocks (wave w:
-// blocks w, w+4, ...); each wave runs one continuous stream of K blocks across
-// all of its items, with the loads of the next DEPTH-1 K blocks in flight in a
-// register ring while the current one is consumed, so item boundaries do not
-// drain the pipeline.  Every load in the stream is issued unconditionally
+// An item covers MP 16-row m-tiles of the expert's rows (MP = 1: up to 16
+// rows, MP = 2: up to 32).  The four waves of a block split the item: wave w
+// takes m-tile w / KW and every KW-th 128-wide K block from w % KW on
+// (KW = 4 / MP), so every wave holds one m-tile's registers and the waves of
+// different m-tiles read the same code tiles at about the same time (the
+// second read is served by the caches).  Each wave runs one continuous stream
+// of K blocks across all of its items, with the loads of the next DEPTH-1 K
+// blocks in flight in a register ring while the current one is consumed, so
+// item boundaries do not drain the pipeline.  Every load in the stream is issued unconditionally
 // (past the end a wave re-reads its last block), so the compiler's wait counts
 // stay exact.
 //
@@ -27,9 +31,9 @@
 // and no extra data is loaded.  The expert's rows are the A operand (16 per
 // m-tile; rows past the expert's count are zero), the codes the B operand.
 //
-// Item end: the low-rank term (x V^T) U^T is added by wave f for weight family
-// f (its T and U fragments were loaded when the item started), the waves are
-// summed in LDS in wave order, and the epilogue stores fp16 (NONE / SWIGLU) or
+// Item end: the low-rank term (x V^T) U^T of each m-tile is added by the
+// wave with w % KW = f for weight family f (its T and U fragments were loaded
+// when the item started), the waves are summed in LDS in wave order, and the epilogue stores fp16 (NONE / SWIGLU) or
 // scales by the pair's route weight and scatters fp32 (ROUTE_SCALE).  With
 // several K splits each split stores its sum and gemm_decode_reduce adds the
 // splits in split order (no cross-block synchronisation inside a kernel).
@@ -39,11 +43,11 @@ namespace milo {
 
 constexpr int kMaxE = 256;
 
-template <int MT, int NW>
+template <int NW>
 struct Stage {
   u32x4 q[NW][3];    // three planes of the 64 x 128 code tile
   u32x4 z[NW][2];    // eight scale/zero words of this lane's rows
-  f16x8 x[MT][4];    // activation fragments of the four 32-wide K steps
+  f16x8 x[4];        // activation fragments of the four 32-wide K steps
 };
 
 struct Item {
@@ -76,15 +80,18 @@ __device__ __forceinline__ f16x8 offset_frag(int step) {
   return __builtin_bit_cast(f16x8, u);
 }
 
-template <int MT, int NW, int EPI>
+template <int MP, int NW, int EPI>
 struct Dec {
+  static constexpr int KW = 4 / MP;   // waves per m-tile (they split the K blocks)
   const GemmArgs& a;
   const DecShared& sh;
-  int lane, wave, total;
+  int lane, wave, kw, mtile, total;
   CodeConsts kc;
 
   __device__ __forceinline__ Dec(const GemmArgs& a_, const DecShared& sh_, int total_)
-      : a(a_), sh(sh_), lane(threadIdx.x & 63), wave(threadIdx.x >> 6), total(total_),
+      : a(a_), sh(sh_), lane(threadIdx.x & 63), wave(threadIdx.x >> 6),
+        kw(__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) % KW)),
+        mtile(__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) / KW)), total(total_),
         kc(make_code_consts()) {}
 
   __device__ __forceinline__ void enter(Cursor& c, int it) const {
@@ -105,20 +112,20 @@ struct Dec {
     m.kbA = (int)((int64_t)a.kblocks * m.ks / a.ksplit);
     m.kbB = (int)((int64_t)a.kblocks * (m.ks + 1) / a.ksplit);
     c.it = it;
-    c.kb = m.kbA + __builtin_amdgcn_readfirstlane(wave);
+    c.kb = m.kbA + kw;
     c.valid = true;
   }
-  __device__ __forceinline__ bool last(const Cursor& c) const { return c.kb + 4 >= c.item.kbB; }
+  __device__ __forceinline__ bool last(const Cursor& c) const { return c.kb + KW >= c.item.kbB; }
   __device__ __forceinline__ void next(Cursor& c) const {
     if (!c.valid) return;
-    if (!last(c)) c.kb += 4;
+    if (!last(c)) c.kb += KW;
     else enter(c, c.it + gridDim.x);
   }
 
   // A wave whose first K block lies past the item's range (K splits of fewer
   // than four blocks) gets one null element: real codes of the item's first
   // block with zero activations, which adds exactly zero.
-  __device__ __forceinline__ void load(Stage<MT, NW>& S, const Cursor& c) const {
+  __device__ __forceinline__ void load(Stage<NW>& S, const Cursor& c) const {
     const Item& m = c.item;
     const bool live = c.kb < m.kbB;
     const int kb = live ? c.kb : m.kbA;
@@ -134,34 +141,29 @@ struct Dec {
       S.z[f][0] = *(const u32x4*)(sp);
       S.z[f][1] = *(const u32x4*)(sp + 4);
     }
+    const int row = mtile * 16 + (lane & 15);
+    const bool ok = live && row < m.M;
+    const uint16_t* xp =
+        a.x + (size_t)(m.base + (row < m.M ? row : 0)) * a.K + (size_t)kb * kTileK + 8 * (lane >> 4);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int row = mt * 16 + (lane & 15);
-      const bool ok = live && row < m.M;
-      const uint16_t* xp =
-          a.x + (size_t)(m.base + (row < m.M ? row : 0)) * a.K + (size_t)kb * kTileK + 8 * (lane >> 4);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const f16x8 v = *(const f16x8*)(xp + 32 * s);
-        S.x[mt][s] = ok ? v : f16x8{};
-      }
+    for (int s = 0; s < 4; ++s) {
+      const f16x8 v = *(const f16x8*)(xp + 32 * s);
+      S.x[s] = ok ? v : f16x8{};
     }
   }
 
-  __device__ __forceinline__ void consume(const Stage<MT, NW>& S, f32x4 (&acc)[NW][MT][4]) const {
+  __device__ __forceinline__ void consume(const Stage<NW>& S, f32x4 (&acc)[NW][4]) const {
     const f16x8 one = ones_frag();
     // activation sums per group: xs = sum x, xo = sum x * off (rows of this lane)
-    f32x4 xs[MT][2], xo[MT][2];
+    f32x4 xs[2], xo[2];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        xs[mt][g] = mfma16x16x32(S.x[mt][2 * g], one, zero);
-        xs[mt][g] = mfma16x16x32(S.x[mt][2 * g + 1], one, xs[mt][g]);
-        xo[mt][g] = mfma16x16x32(S.x[mt][2 * g], offset_frag(2 * g), zero);
-        xo[mt][g] = mfma16x16x32(S.x[mt][2 * g + 1], offset_frag(2 * g + 1), xo[mt][g]);
-      }
+    for (int g = 0; g < 2; ++g) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      xs[g] = mfma16x16x32(S.x[2 * g], one, zero);
+      xs[g] = mfma16x16x32(S.x[2 * g + 1], one, xs[g]);
+      xo[g] = mfma16x16x32(S.x[2 * g], offset_frag(2 * g), zero);
+      xo[g] = mfma16x16x32(S.x[2 * g + 1], offset_frag(2 * g + 1), xo[g]);
+    }
 #pragma unroll
     for (int f = 0; f < NW; ++f)
 #pragma unroll
@@ -174,41 +176,41 @@ struct Dec {
           const uint32_t w = idx < 4 ? S.z[f][0][idx] : S.z[f][1][idx - 4];
           const float sc = half_bits_to_float(w & 0xFFFFu);
           const float zp = half_bits_to_float(w >> 16);
+          f32x4 p;
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            f32x4 p;
+          for (int r = 0; r < 4; ++r) p[r] = __builtin_fmaf(-zp, xs[g][r], -xo[g][r]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = __builtin_fmaf(-zp, xs[mt][g][r], -xo[mt][g][r]);
-#pragma unroll
-            for (int ss = 0; ss < 2; ++ss) {
-              const int step = 2 * g + ss;
-              const u32x4 u = {h[4 * step], h[4 * step + 1], h[4 * step + 2], h[4 * step + 3]};
-              p = mfma16x16x32(S.x[mt][step], __builtin_bit_cast(f16x8, u), p);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[f][mt][i][r] = __builtin_fmaf(sc, p[r], acc[f][mt][i][r]);
+          for (int ss = 0; ss < 2; ++ss) {
+            const int step = 2 * g + ss;
+            const u32x4 u = {h[4 * step], h[4 * step + 1], h[4 * step + 2], h[4 * step + 3]};
+            p = mfma16x16x32(S.x[step], __builtin_bit_cast(f16x8, u), p);
           }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[f][i][r] = __builtin_fmaf(sc, p[r], acc[f][i][r]);
         }
       }
   }
 };
 
 // Per-item values loaded when an item starts and used at its end.
-template <int MT>
+template <int MP>
 struct ItemLate {
-  f16x8 t[MT][2];     // low-rank T fragments (rows x 32 ranks) of family `wave`
-  f16x8 u[4][2];      // U fragments (64 n rows x 32 ranks) of family `wave`
-  int32_t sp[MT * 4]; // ROUTE_SCALE: slot index of each output row of this thread
-  float pw[MT * 4];   // ROUTE_SCALE: route weight of those rows
+  f16x8 t[2];         // low-rank T fragments (rows of this wave's m-tile x 32 ranks)
+  f16x8 u[4][2];      // U fragments (64 n rows x 32 ranks) of this wave's family
+  int32_t sp[MP * 4]; // ROUTE_SCALE: slot index of each output row of this thread
+  float pw[MP * 4];   // ROUTE_SCALE: route weight of those rows
 };
 
-template <int MT, int NW, int EPI, int DEPTH>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 2 : 1, MT == 1 ? 2 : 1)))
+template <int MP, int NW, int EPI, int DEPTH>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_decode_kernel(GemmArgs a) {
+  using DecT = Dec<MP, NW, EPI>;
+  constexpr int KW = DecT::KW;
   __shared__ DecShared sh;
-  constexpr int kOut = MT * 16 * 64;       // outputs per family per item
+  constexpr int kTile = 16 * 64;           // outputs of one m-tile per family
+  constexpr int kOut = MP * kTile;         // outputs per family per item
   constexpr int kPer = kOut / 256;         // per thread
-  __shared__ float red[4][NW][kOut];
+  __shared__ float red[4][NW][kTile];      // wave partials of their own m-tile
 
   // ---- experts with rows for this path, and their ranks
   for (int e = threadIdx.x; e <= a.num_experts; e += 256) sh.off[e] = a.offsets[e];
@@ -229,23 +231,21 @@ gemm_decode_kernel(GemmArgs a) {
   const int total = __builtin_amdgcn_readfirstlane(sh.nact) * a.n_tiles * a.ksplit;
   if ((int)blockIdx.x >= total) return;
 
-  Dec<MT, NW, EPI> D(a, sh, total);
-  const int lane = D.lane, wave = D.wave;
+  DecT D(a, sh, total);
+  const int lane = D.lane, wave = D.wave, kw = D.kw, mtile = D.mtile;
   const int RW = a.n_w * a.rp;
-  const int lrf = wave < NW ? wave : 0;   // weight family whose low-rank term this wave adds
+  const int lrf = kw < NW ? kw : 0;       // weight family whose low-rank term this wave adds
 
-  f32x4 acc[NW][MT][4];
+  f32x4 acc[NW][4];
 #pragma unroll
   for (int f = 0; f < NW; ++f)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[f][mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) acc[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // item-start loads: low-rank fragments (every wave loads, waves >= NW
-  // ignore them) and the epilogue's row metadata.  Addresses are clamped to
-  // valid memory and masked values replaced, so every load is issued.
-  ItemLate<MT> late;
+  // item-start loads: low-rank fragments (every wave loads, waves that add no
+  // low-rank term ignore them) and the epilogue's row metadata.  Addresses are
+  // clamped to valid memory and masked values replaced, so every load is issued.
+  ItemLate<MP> late;
   auto load_late = [&](const Item& m) {
     if (a.rp > 0) {
       const int rk = sh.rank[lrf][m.e];
@@ -254,18 +254,15 @@ gemm_decode_kernel(GemmArgs a) {
         const int j0 = 32 * s2 + 8 * (lane >> 4);
         const bool jok = j0 < rk;
         const int jc = jok ? j0 : 0;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int row = mt * 16 + (lane & 15);
-          const bool ok = jok && row < m.M;
-          const f16x8 v = *(const f16x8*)(a.T + (size_t)(m.base + (row < m.M ? row : 0)) * RW + lrf * a.rp + jc);
-          late.t[mt][s2] = ok ? v : f16x8{};
-        }
+        const int row = mtile * 16 + (lane & 15);
+        const bool ok = jok && row < m.M;
+        const f16x8 v = *(const f16x8*)(a.T + (size_t)(m.base + (row < m.M ? row : 0)) * RW + lrf * a.rp + jc);
+        late.t[s2] = ok ? v : f16x8{};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int n = m.nt * kTileRows + 16 * i + (lane & 15);
-          const f16x8 v = *(const f16x8*)(a.U[lrf] + ((size_t)m.e * a.N + n) * a.max_rank + jc);
-          late.u[i][s2] = jok ? v : f16x8{};
+          const f16x8 u = *(const f16x8*)(a.U[lrf] + ((size_t)m.e * a.N + n) * a.max_rank + jc);
+          late.u[i][s2] = jok ? u : f16x8{};
         }
       }
     }
@@ -281,34 +278,30 @@ gemm_decode_kernel(GemmArgs a) {
   };
 
   auto finish_item = [&](const Item& m) {
-    // low-rank term of family `wave` (added once: by the first K split)
-    if (wave < NW && a.rp > 0 && m.ks == 0) {
+    // low-rank term of family kw for this wave's m-tile (added once: by the first K split)
+    if (kw < NW && a.rp > 0 && m.ks == 0) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         if (32 * s2 >= a.rp) break;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int f = 0; f < NW; ++f)
-              if (f == wave) acc[f][mt][i] = mfma16x16x32(late.t[mt][s2], late.u[i][s2], acc[f][mt][i]);
+          for (int f = 0; f < NW; ++f)
+            if (f == kw) acc[f][i] = mfma16x16x32(late.t[s2], late.u[i][s2], acc[f][i]);
       }
     }
     __syncthreads();   // previous item's readers of red are done
 #pragma unroll
     for (int f = 0; f < NW; ++f)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = mt * 16 + 4 * (lane >> 4) + r, n = 16 * i + (lane & 15);
-            red[wave][f][row * 64 + n] = acc[f][mt][i][r];
-          }
-          acc[f][mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < 4; ++r) {
+          const int row = 4 * (lane >> 4) + r, n = 16 * i + (lane & 15);
+          red[wave][f][row * 64 + n] = acc[f][i][r];
         }
+        acc[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     __syncthreads();
     float res[NW][kPer];
 #pragma unroll
@@ -316,7 +309,11 @@ gemm_decode_kernel(GemmArgs a) {
 #pragma unroll
       for (int c = 0; c < kPer; ++c) {
         const int o = threadIdx.x + 256 * c;
-        res[f][c] = ((red[0][f][o] + red[1][f][o]) + red[2][f][o]) + red[3][f][o];
+        const int mt = o / kTile, ol = o - mt * kTile;   // m-tile and offset within it
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < KW; ++w) v += red[mt * KW + w][f][ol];
+        res[f][c] = v;
       }
     if (a.ksplit > 1) {
       float* mine = a.part + (((size_t)m.ks * a.num_experts + m.e) * a.n_tiles + m.nt) * (NW * kOut);
@@ -346,7 +343,7 @@ gemm_decode_kernel(GemmArgs a) {
   D.enter(pf, blockIdx.x);
   cs = pf;
   load_late(cs.item);
-  Stage<MT, NW> ring[DEPTH];
+  Stage<NW> ring[DEPTH];
 #pragma unroll
   for (int d = 0; d < DEPTH - 1; ++d) {
     D.load(ring[d], pf);
@@ -371,21 +368,21 @@ gemm_decode_kernel(GemmArgs a) {
   }
 }
 
-template <int MT, int NW, int EPI>
+template <int MP, int NW, int EPI>
 static void launch_one(const GemmArgs& a, int blocks, int num_experts, hipStream_t st) {
-  constexpr int depth = (MT == 1 && NW == 1) ? 3 : 2;
-  hipLaunchKernelGGL((gemm_decode_kernel<MT, NW, EPI, depth>), dim3(blocks), dim3(256), 0, st, a);
+  constexpr int depth = NW == 1 ? 3 : 2;
+  hipLaunchKernelGGL((gemm_decode_kernel<MP, NW, EPI, depth>), dim3(blocks), dim3(256), 0, st, a);
   if (a.ksplit > 1)
-    hipLaunchKernelGGL((gemm_split_reduce<16 * MT, NW, EPI>), dim3(a.n_tiles, num_experts), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_split_reduce<16 * MP, NW, EPI>), dim3(a.n_tiles, num_experts), dim3(256), 0,
                        st, a);
 }
 
-template <int MT>
+template <int MP>
 static void launch_mt(const GemmArgs& a, int epi, int blocks, int num_experts, hipStream_t st) {
   switch (epi) {
-    case MILO_EPI_SWIGLU: launch_one<MT, 2, MILO_EPI_SWIGLU>(a, blocks, num_experts, st); break;
-    case MILO_EPI_ROUTE_SCALE: launch_one<MT, 1, MILO_EPI_ROUTE_SCALE>(a, blocks, num_experts, st); break;
-    default: launch_one<MT, 1, MILO_EPI_NONE>(a, blocks, num_experts, st); break;
+    case MILO_EPI_SWIGLU: launch_one<MP, 2, MILO_EPI_SWIGLU>(a, blocks, num_experts, st); break;
+    case MILO_EPI_ROUTE_SCALE: launch_one<MP, 1, MILO_EPI_ROUTE_SCALE>(a, blocks, num_experts, st); break;
+    default: launch_one<MP, 1, MILO_EPI_NONE>(a, blocks, num_experts, st); break;
   }
 }
 

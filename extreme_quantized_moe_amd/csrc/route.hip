@@ -21,11 +21,76 @@ constexpr int kRouteBlock = 256;
 constexpr int kMaxExperts = 256;
 constexpr int kBitWords = kRouteBlock / 32;
 constexpr int kMaxK = 8;
-constexpr int kLdsExperts = 64;   // logits of up to 64 experts are staged in LDS
 constexpr int kMaxSlots = 16;
 
 __device__ __forceinline__ int slot_expert(const int32_t* ids_row, int j, int k, int E) {
   return j < k ? ids_row[j] : E + (j - k);
+}
+
+// Top-k of one token's logits: k passes, pass j picks the largest logit (lowest
+// id on ties) among the experts not picked before; also the row maximum and
+// the softmax denominator.  Up to 64 experts the row is held in registers
+// (NE >= E; all loads issued at once); beyond that it is re-read per pass.
+template <int NE>
+__device__ __forceinline__ void topk_regs(const float* row, int E, int k, float (&bv)[kMaxK],
+                                          int (&bi)[kMaxK], float& mx, float& den) {
+  float v[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) v[e] = e < E ? row[e] : -INFINITY;
+  mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+    if (e < E) mx = fmaxf(mx, v[e]);
+  uint64_t taken = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    bv[j] = -INFINITY;
+    bi[j] = -1;
+    if (j < k) {
+      float best = -INFINITY;
+      int bidx = -1;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const bool ok = e < E && !((taken >> e) & 1ull);
+        if (ok && (bidx < 0 || v[e] > best)) {
+          best = v[e];
+          bidx = e;
+        }
+      }
+      bv[j] = best;
+      bi[j] = bidx;
+      taken |= 1ull << bidx;
+    }
+  }
+  den = 0.f;
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+    if (e < E) den += expf(v[e] - mx);
+}
+
+__device__ __forceinline__ void topk_loop(const float* row, int E, int k, float (&bv)[kMaxK],
+                                       int (&bi)[kMaxK], float& mx, float& den) {
+  mx = -INFINITY;
+  for (int e = 0; e < E; ++e) mx = fmaxf(mx, row[e]);
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    bv[j] = -INFINITY;
+    bi[j] = -1;
+    if (j < k) {
+      for (int e = 0; e < E; ++e) {
+        bool taken = false;
+#pragma unroll
+        for (int jj = 0; jj < j; ++jj) taken |= (bi[jj] == e);
+        const float v = row[e];
+        if (!taken && (bi[j] < 0 || v > bv[j])) {
+          bv[j] = v;
+          bi[j] = e;
+        }
+      }
+    }
+  }
+  den = 0.f;
+  for (int e = 0; e < E; ++e) den += expf(row[e] - mx);
 }
 
 // Block-wide exclusive scan of one int per thread (blockDim == 256).
@@ -52,26 +117,10 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
            int32_t* __restrict__ offsets, int32_t* __restrict__ block_counts) {
   __shared__ uint32_t bits[kMaxExperts][kBitWords];
   __shared__ int scan_lds[kRouteBlock];
-  __shared__ float lg_lds[kRouteBlock * kLdsExperts];
   const int tid = threadIdx.x;
   const int t = blockIdx.x * kRouteBlock + tid;
   const int ET = E + S, slots = k + S;
   for (int x = tid; x < kMaxExperts * kBitWords; x += kRouteBlock) (&bits[0][0])[x] = 0u;
-  // stage the block's logits in LDS with coalesced loads, all issued at once
-  const bool staged = E <= kLdsExperts;
-  if (staged) {
-    const int t0 = blockIdx.x * kRouteBlock;
-    const int ntok = (T - t0) < kRouteBlock ? (T - t0) : kRouteBlock;
-    const int n = ntok * E;
-    const float* src = logits + (size_t)t0 * E;
-    float v[kLdsExperts];
-#pragma unroll
-    for (int u = 0; u < kLdsExperts; ++u)
-      if (tid + kRouteBlock * u < n) v[u] = src[tid + kRouteBlock * u];
-#pragma unroll
-    for (int u = 0; u < kLdsExperts; ++u)
-      if (tid + kRouteBlock * u < n) lg_lds[tid + kRouteBlock * u] = v[u];
-  }
   __syncthreads();
 
   // per-thread arrays are indexed only by unrolled loop counters (registers)
@@ -83,32 +132,15 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
     rank[j] = 0;
   }
   if (t < T) {
-    const float* row = staged ? lg_lds + tid * E : logits + (size_t)t * E;
-    // k passes; pass j picks the largest logit (lowest id on ties) among the
-    // experts not picked by passes 0..j-1
+    const float* row = logits + (size_t)t * E;
     float bv[kMaxK];
     int bi[kMaxK];
-    float mx = -INFINITY;
-    for (int e = 0; e < E; ++e) mx = fmaxf(mx, row[e]);
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      bv[j] = -INFINITY;
-      bi[j] = -1;
-      if (j < k) {
-        for (int e = 0; e < E; ++e) {
-          bool taken = false;
-#pragma unroll
-          for (int jj = 0; jj < j; ++jj) taken |= (bi[jj] == e);
-          const float v = row[e];
-          if (!taken && (bi[j] < 0 || v > bv[j])) {
-            bv[j] = v;
-            bi[j] = e;
-          }
-        }
-      }
-    }
-    float den = 0.f;
-    for (int e = 0; e < E; ++e) den += expf(row[e] - mx);
+    float mx, den;
+    if (E <= 8) topk_regs<8>(row, E, k, bv, bi, mx, den);
+    else if (E <= 16) topk_regs<16>(row, E, k, bv, bi, mx, den);
+    else if (E <= 32) topk_regs<32>(row, E, k, bv, bi, mx, den);
+    else if (E <= 64) topk_regs<64>(row, E, k, bv, bi, mx, den);
+    else topk_loop(row, E, k, bv, bi, mx, den);
     float sel[kMaxK];
     float selsum = 0.f;
 #pragma unroll
