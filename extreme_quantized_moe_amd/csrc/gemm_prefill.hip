@@ -26,33 +26,13 @@ constexpr int kMT = kBM / 16;            // m-tiles per wave
 constexpr int kXStride = kTileK + 8;     // LDS row stride in halves (272 B)
 constexpr int kXBuf = kBM * kXStride;    // halves per buffer
 
-// (expert, first row, rows) of the `tile`-th 128-row tile among the experts
-// with more than min_rows rows.
-__device__ __forceinline__ bool find_tile128(const int32_t* offsets, int num_experts, int min_rows,
-                                             int tile, int* e_out, int* m0_out, int* rows_out) {
-  int cum = 0;
-  for (int e = 0; e < num_experts; ++e) {
-    const int m = offsets[e + 1] - offsets[e];
-    if (m <= min_rows) continue;
-    const int nt = (m + kBM - 1) / kBM;
-    if (tile < cum + nt) {
-      *e_out = e;
-      *m0_out = (tile - cum) * kBM;
-      *rows_out = m;
-      return true;
-    }
-    cum += nt;
-  }
-  return false;
-}
-
 template <int NW>
 __global__ void __launch_bounds__(256) gemm_prefill_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
   const CodeConsts kc = make_code_consts();
   int e, m0, M;
-  if (!find_tile128(a.offsets, a.num_experts, a.pre_min_rows, blockIdx.x, &e, &m0, &M)) return;
+  if (!find_row_tile(a.offsets, a.num_experts, a.pre_min_rows, kBM, blockIdx.x, &e, &m0, &M)) return;
   const int base = a.offsets[e];
   const int f = (NW == 2) ? (wave & 1) : 0;
   const int nt = (NW == 2) ? (2 * blockIdx.y + (wave >> 1)) : (4 * blockIdx.y + wave);

@@ -39,22 +39,9 @@ struct PrepassArgs {
   int dec_max_rows;   // experts with more rows are not gathered
 };
 
-// Locate the (expert, first row) of 16-row tile `tile`; returns false past the end.
 __device__ __forceinline__ bool find_tile16(const int32_t* offsets, int num_experts, int tile,
                                             int* e_out, int* m0_out, int* rows_out) {
-  int cum = 0;
-  for (int e = 0; e < num_experts; ++e) {
-    const int m = offsets[e + 1] - offsets[e];
-    const int nt = (m + 15) >> 4;
-    if (tile < cum + nt) {
-      *e_out = e;
-      *m0_out = (tile - cum) * 16;
-      *rows_out = m;
-      return true;
-    }
-    cum += nt;
-  }
-  return false;
+  return find_row_tile(offsets, num_experts, 0, 16, tile, e_out, m0_out, rows_out);
 }
 
 // Gathered rows (pair order) and pair weights of one 16-row tile.

@@ -105,6 +105,53 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t h, float s, float c) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Locate the (expert, first row, expert rows) of row tile `tile` when the
+// experts with more than `min_rows` rows are cut into tiles of `rows_per_tile`
+// rows, expert by expert.  Block-uniform result; returns false past the last
+// tile.  The first wave reads the expert offsets (all loads issued at once),
+// scans the per-expert tile counts with lane shuffles and the lane holding the
+// tile publishes it through LDS.  Every thread of the block must call it.
+__device__ __forceinline__ bool find_row_tile(const int32_t* __restrict__ offsets, int num_experts,
+                                              int min_rows, int rows_per_tile, int tile,
+                                              int* e_out, int* m0_out, int* rows_out) {
+  __shared__ int res[3];
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int m[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {          // up to 256 experts
+      const int e = 64 * c + lane;
+      m[c] = e < num_experts ? offsets[e + 1] - offsets[e] : 0;
+    }
+    if (lane == 0) res[0] = -1;
+    int before = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (64 * c >= num_experts) break;
+      const int nt = m[c] > min_rows ? (m[c] + rows_per_tile - 1) / rows_per_tile : 0;
+      int incl = nt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+      }
+      const int first = before + incl - nt;
+      if (nt > 0 && tile >= first && tile < first + nt) {
+        res[0] = 64 * c + lane;
+        res[1] = (tile - first) * rows_per_tile;
+        res[2] = m[c];
+      }
+      before += __shfl(incl, 63);
+    }
+  }
+  __syncthreads();
+  const int e = res[0];
+  *e_out = e;
+  *m0_out = res[1];
+  *rows_out = res[2];
+  return e >= 0;
+}
+
 // ---------------------------------------------------------------- host side
 void set_error(const char* fmt, ...);
 int32_t hip_status(hipError_t e, const char* what);
