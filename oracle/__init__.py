@@ -34,6 +34,18 @@ from .layout import (  # noqa: F401
     unpack_sz_v1,
 )
 from .route import route_ref  # noqa: F401
+from .compensator import (  # noqa: F401
+    quantize_compensator,
+    dequant_compensator,
+    pack_lr_v,
+    unpack_lr_v,
+    pack_lr_u,
+    unpack_lr_u,
+    lr_v_words,
+    lr_v_sz_words,
+    lr_u_words,
+    lr_u_sz_words,
+)
 from .moe import (  # noqa: F401
     linear_ref,
     quantize_expert,

@@ -42,11 +42,16 @@ def silu(u):
     return u / (1.0 + np.exp(-u))
 
 
-def quantize_expert(exp, group=64):
+def quantize_expert(exp, group=64, lr_format="fp16"):
     """fp32 expert weights -> dict with (codes, scale, zero) per matrix plus the
-    compensators unchanged."""
+    compensators: unchanged (lr_format "fp16"), or quantized to int3 and
+    dequantized again (lr_format "int3", oracle.compensator: [talk] MiLo
+    Algorithm, last step -- the factors themselves are stored as int3)."""
+    from .compensator import dequant_compensator, quantize_compensator
     out = {}
     for n in ("W1", "W3", "W2"):
+        if n not in exp:
+            continue
         W = exp[n]
         W = W.numpy() if hasattr(W, "numpy") else np.asarray(W)
         out[n] = quantize_rtn_int3(W, group)
@@ -54,6 +59,12 @@ def quantize_expert(exp, group=64):
         if n in exp:
             v = exp[n]
             out[n] = v.numpy() if hasattr(v, "numpy") else np.asarray(v)
+    if lr_format == "int3":
+        for a, b in (("A1", "B1"), ("A3", "B3"), ("A2", "B2")):
+            if a in out and b in out:
+                out[a], out[b] = dequant_compensator(quantize_compensator(out[a], out[b]))
+    elif lr_format != "fp16":
+        raise ValueError(f"unknown compensator format {lr_format!r}")
     return out
 
 
