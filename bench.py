@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
+    ap.add_argument("--lr", default="fp16", choices=["fp16", "int3"],
+                    help="storage of the compensator factors U, V")
     ap.add_argument("--hbm-probe", action="store_true",
                     help="only measure plain device read (sum) and copy bandwidth on 4 GiB")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -77,11 +79,12 @@ def src_hash(files):
 class Layer:
     """One MoE layer's device weights, buffers and prebuilt call descriptors."""
 
-    def __init__(self, m, cfg, layer_idx, X, logits, path):
+    def __init__(self, m, cfg, layer_idx, X, logits, path, lr_format="fp16"):
         import synth
         import torch
         L = m._lib
         self.m, self.cfg = m, cfg
+        self.lr_format = lr_format
         self.ranks = synth.gen_ranks(cfg, layer_idx)
         ET = cfg.E + cfg.S
         fam = {}
@@ -92,7 +95,7 @@ class Layer:
                 Ws.append(d[n])
                 As.append(d[a])
                 Bs.append(d[b])
-            fam[n] = m.Family.from_dense(Ws, As, Bs, max_rank=max(self.ranks))
+            fam[n] = m.Family.from_dense(Ws, As, Bs, max_rank=max(self.ranks), lr_format=lr_format)
             del Ws
         self.fam = fam
         T, slots = cfg.T, cfg.slots
@@ -159,6 +162,11 @@ class Layer:
         b13 = b2 = 0
         f13 = f2 = 0
         touched = 0
+        q3 = self.lr_format == "int3"
+        # compensator factor bytes: fp16, or int3 codes + fp16 scale/zero words
+        # (U: one group per output row; V: groups of 64 along the input)
+        u_bytes = (lambda n, r: n * r * 3 // 8 + (4 * n if r else 0)) if q3 else (lambda n, r: n * r * 2)
+        v_bytes = (lambda r, k: r * k * 3 // 8 + r * (k // 64) * 4) if q3 else (lambda r, k: r * k * 2)
         for e, M in enumerate(rows):
             if M == 0:
                 continue
@@ -166,12 +174,12 @@ class Layer:
             r = self.ranks[e]
             # gate/up kernel: W1, W3 packed + scale/zero + U (N x r) per matrix,
             # gathered X rows, T rows, G written
-            b13 += 2 * (3 * F * H // 8 + F * H // 16 + F * r * 2) + M * H * 2 + M * 2 * r * 2 + M * F * 2
-            b2 += (3 * H * F // 8 + H * F // 16 + H * r * 2) + M * F * 2 + M * r * 2 + M * H * 4
+            b13 += 2 * (3 * F * H // 8 + F * H // 16 + u_bytes(F, r)) + M * H * 2 + M * 2 * r * 2 + M * F * 2
+            b2 += (3 * H * F // 8 + H * F // 16 + u_bytes(H, r)) + M * F * 2 + M * r * 2 + M * H * 4
             f13 += 2 * M * 2 * F * H + 2 * M * 2 * r * (H + F)
             f2 += 2 * M * H * F + 2 * M * r * (H + F)
-        # pre-pass reads of V (V1, V3: r x H; V2: r x F; fp16) for touched experts
-        vbytes = sum((2 * r * H + r * F) * 2 for e, r in enumerate(self.ranks) if rows[e])
+        # pre-pass reads of V (V1, V3: r x H; V2: r x F) for touched experts
+        vbytes = sum(2 * v_bytes(r, H) + v_bytes(r, F) for e, r in enumerate(self.ranks) if rows[e])
         layer_bytes = b13 + b2 + vbytes + cfg.T * H * 2 * 2 + cfg.T * cfg.E * 4
         return {"rows": rows, "touched": touched, "bytes13": b13, "bytes2": b2, "flops13": f13,
                 "flops2": f2, "layer_bytes": layer_bytes, "layer_flops": f13 + f2}
@@ -195,7 +203,8 @@ def cpu_baseline(cfg, layer, offsets, budget_s):
     done, t_exp, pairs_done = [], 0.0, 0
     for e in touched:
         exp = synth.gen_expert(cfg, 0, e, layer.ranks[e], device="cuda")
-        qe = oracle.quantize_expert({k: v.cpu() for k, v in exp.items()})   # offline, untimed
+        qe = oracle.quantize_expert({k: v.cpu() for k, v in exp.items()},
+                                    lr_format=layer.lr_format)              # offline, untimed
         seg = sp[off[e]:off[e + 1]]
         rows = X[seg // cfg.slots]
         t1 = time.perf_counter()
@@ -307,8 +316,8 @@ def main():
     layers = []
     for i in range(nsets):
         logits = synth.gen_logits(cfg, i if stack else 0, device="cuda")
-        layers.append(Layer(m, cfg, i if stack else 0, X, logits, path) if (stack or i == 0)
-                      else Layer(m, cfg, 100 + i, X, logits, path))
+        layers.append(Layer(m, cfg, i if stack else 0, X, logits, path, args.lr) if (stack or i == 0)
+                      else Layer(m, cfg, 100 + i, X, logits, path, args.lr))
     ws = torch.zeros(max(lay.ws_need for lay in layers), dtype=torch.uint8, device="cuda")
     for lay in layers:
         lay.ws = ws
@@ -369,7 +378,7 @@ def main():
     else:
         achieved = k_bytes / (k13_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(args.config, cfg.T)}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(args.config, cfg.T, args.lr)}
     roof.update({"kernel": kname, "alg_bytes_per_launch": int(k_bytes), "alg_flops_per_launch": int(k_flops),
                  "avg_launch_us": round(k13_us, 2)})
     res = {
@@ -395,6 +404,7 @@ def main():
             "achieved_TFLOPs_step": round(layer_flops / (ms_step * 1e-3) / 1e12, 2),
             "host_seconds_timed": round(t_host, 3),
             "path": args.path,
+            "compensator_factors": args.lr,
         },
         "roofline": roof,
     }
@@ -406,7 +416,7 @@ def main():
     print(json.dumps(res))
 
 
-def traffic_for(config, T):
+def traffic_for(config, T, lr="fp16"):
     """Measured HBM traffic of the dominant kernel from a committed rocprofv3
     counter summary, if it was taken on the current kernel source."""
     f = os.path.join(ROOT, "profiles", "traffic.json")
@@ -414,7 +424,7 @@ def traffic_for(config, T):
         return None
     try:
         d = json.load(open(f))
-        ent = d.get(f"{config}_T{T}")
+        ent = d.get(f"{config}_T{T}" + ("" if lr == "fp16" else f"_{lr}"))
         if not ent or ent.get("src_hash") != src_hash(ent.get("src_files", [])):
             return None
         return ent.get("bytes_per_launch")

@@ -5,13 +5,13 @@ is the ctypes binding.  Importing it loads the library and raises if it has
 not been built: there is no CPU or PyTorch fallback.
 """
 from ._lib import (  # noqa: F401
-    EPI_NONE, EPI_ROUTE_SCALE, EPI_SWIGLU, GEMM_PREPASS_DONE, PATH_AUTO, PATH_DECODE, PATH_PREFILL,
-    LIB_PATH, MiloError, lib,
+    EPI_NONE, EPI_ROUTE_SCALE, EPI_SWIGLU, GEMM_PREPASS_DONE, LR_FP16, LR_INT3, PATH_AUTO, PATH_DECODE,
+    PATH_PREFILL, LIB_PATH, MiloError, lib,
 )
 
 lib()  # fail loudly at import if libmilo.so is missing
 
 from .ops import (  # noqa: E402,F401
-    Family, MoELayer, moe_combine, moe_lowrank_prepass, moe_w3a16_lowrank_gemm, pack_int3, packed_words,
-    quantize_rtn_int3, route_sort, sz_words,
+    Family, MoELayer, lr_words, moe_combine, moe_lowrank_prepass, moe_w3a16_lowrank_gemm, pack_int3,
+    pack_lr_int3, packed_words, quantize_rtn_int3, route_sort, sz_words,
 )

@@ -11,11 +11,14 @@ STATUS_NAMES = {0: "MILO_OK", 1: "MILO_ERR_NULL", 2: "MILO_ERR_SHAPE", 3: "MILO_
 EPI_NONE, EPI_SWIGLU, EPI_ROUTE_SCALE = 0, 1, 2
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 GEMM_PREPASS_DONE = 1
+LR_FP16, LR_INT3 = 0, 1
 
 
 class MiloWeights(C.Structure):
     _fields_ = [("packed", C.c_void_p), ("sz", C.c_void_p), ("U", C.c_void_p),
-                ("V", C.c_void_p), ("rank", C.c_void_p)]
+                ("V", C.c_void_p), ("rank", C.c_void_p), ("lr_format", C.c_int32),
+                ("Uq", C.c_void_p), ("Usz", C.c_void_p), ("Vq", C.c_void_p),
+                ("Vsz", C.c_void_p)]
 
 
 class MiloGemmDesc(C.Structure):
@@ -59,7 +62,13 @@ def lib():
         "milo_packed_words": (i64, [i64, i64]),
         "milo_sz_words": (i64, [i64, i64]),
         "milo_quantize_rtn_int3": (i32, [vp, i64, i64, vp, vp, vp, vp]),
+        "milo_quantize_rtn_int3_grouped": (i32, [vp, i64, i64, i32, vp, vp, vp, vp]),
         "milo_pack_int3": (i32, [vp, vp, vp, i64, i64, vp, vp, vp]),
+        "milo_lr_v_words": (i64, [i32, i64]),
+        "milo_lr_v_sz_words": (i64, [i32, i64]),
+        "milo_lr_u_words": (i64, [i64, i32]),
+        "milo_lr_u_sz_words": (i64, [i64]),
+        "milo_pack_lr_int3": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
         "milo_route_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "milo_route_sort": (i32, [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "milo_moe_gemm_workspace_bytes": (sz, [C.POINTER(MiloGemmDesc)]),

@@ -45,8 +45,12 @@ GemmArgs make_gemm_args(const milo_gemm_desc* d, const GemmPlan& p, char* ws) {
     a.packed[f] = w.packed;
     a.sz[f] = w.sz;
     a.U[f] = w.U;
+    a.Uq[f] = w.Uq;
+    a.Usz[f] = w.Usz;
     a.rank[f] = w.rank;
   }
+  a.lrq = d->w[0].lr_format == MILO_LR_INT3 ? 1 : 0;
+  a.uq_per_expert = d->max_rank ? milo_lr_u_words(d->N, d->max_rank) : 0;
   a.T = (const uint16_t*)(ws + p.off_t);
   a.y = d->y;
   a.words_per_expert = milo_packed_words(d->N, d->K);
@@ -94,9 +98,17 @@ static int32_t validate_gemm(const milo_gemm_desc* d) {
   for (int f = 0; f < d->n_w; ++f) {
     const milo_weights& w = d->w[f];
     if (!w.packed || !w.sz) MILO_FAIL(MILO_ERR_NULL, "w[%d].packed / sz is NULL", f);
-    if (d->max_rank > 0 && (!w.U || !w.V || !w.rank))
-      MILO_FAIL(MILO_ERR_NULL, "w[%d].U / V / rank is NULL with max_rank > 0", f);
-    if (!aligned(w.packed, 16) || !aligned(w.sz, 16) || !aligned(w.U, 16) || !aligned(w.V, 16))
+    if (w.lr_format != MILO_LR_FP16 && w.lr_format != MILO_LR_INT3)
+      MILO_FAIL(MILO_ERR_ARG, "w[%d].lr_format=%d unknown", f, w.lr_format);
+    if (w.lr_format != d->w[0].lr_format)
+      MILO_FAIL(MILO_ERR_ARG, "both weight families need the same lr_format");
+    if (d->max_rank > 0 && !w.rank) MILO_FAIL(MILO_ERR_NULL, "w[%d].rank is NULL with max_rank > 0", f);
+    if (d->max_rank > 0 && w.lr_format == MILO_LR_FP16 && (!w.U || !w.V))
+      MILO_FAIL(MILO_ERR_NULL, "w[%d].U / V is NULL with max_rank > 0", f);
+    if (d->max_rank > 0 && w.lr_format == MILO_LR_INT3 && (!w.Uq || !w.Usz || !w.Vq || !w.Vsz))
+      MILO_FAIL(MILO_ERR_NULL, "w[%d].Uq / Usz / Vq / Vsz is NULL with max_rank > 0 (int3 factors)", f);
+    if (!aligned(w.packed, 16) || !aligned(w.sz, 16) || !aligned(w.U, 16) || !aligned(w.V, 16) ||
+        !aligned(w.Uq, 16) || !aligned(w.Usz, 16) || !aligned(w.Vq, 16) || !aligned(w.Vsz, 16))
       MILO_FAIL(MILO_ERR_ALIGN, "w[%d] pointers must be 16-byte aligned", f);
     if (w.rank && !aligned(w.rank, 4)) MILO_FAIL(MILO_ERR_ALIGN, "w[%d].rank must be 4-byte aligned", f);
   }
@@ -194,16 +206,49 @@ const char* milo_last_error(void) { return g_err; }
 int64_t milo_packed_words(int64_t rows, int64_t K) { return 3 * rows * K / 32; }
 int64_t milo_sz_words(int64_t rows, int64_t K) { return rows * K / 64; }
 
-int32_t milo_quantize_rtn_int3(const float* W, int64_t rows, int64_t K, uint8_t* codes,
-                               uint16_t* scale, uint16_t* zero, void* stream) {
+int32_t milo_quantize_rtn_int3_grouped(const float* W, int64_t rows, int64_t K, int32_t group,
+                                       uint8_t* codes, uint16_t* scale, uint16_t* zero, void* stream) {
   g_err[0] = 0;
   if (!W || !codes || !scale || !zero) MILO_FAIL(MILO_ERR_NULL, "W, codes, scale, zero are required");
-  if (rows < 1 || K < 64 || K % 64 || rows > (1ll << 31) || K > (1ll << 31))
-    MILO_FAIL(MILO_ERR_SHAPE, "rows=%lld K=%lld: need rows >= 1, K >= 64, K %% 64 == 0",
-              (long long)rows, (long long)K);
+  if (group < 1 || group > 64) MILO_FAIL(MILO_ERR_SHAPE, "group=%d outside 1..64", group);
+  if (rows < 1 || K < group || K % group || rows > (1ll << 31) || K > (1ll << 31))
+    MILO_FAIL(MILO_ERR_SHAPE, "rows=%lld K=%lld: need rows >= 1, K >= group, K %% group == 0 (group %d)",
+              (long long)rows, (long long)K, group);
   if (!aligned(W, 4) || !aligned(scale, 2) || !aligned(zero, 2))
     MILO_FAIL(MILO_ERR_ALIGN, "W must be 4-byte and scale/zero 2-byte aligned");
-  return launch_quantize(W, rows, K, codes, scale, zero, (hipStream_t)stream);
+  return launch_quantize(W, rows, K, group, codes, scale, zero, (hipStream_t)stream);
+}
+
+int32_t milo_quantize_rtn_int3(const float* W, int64_t rows, int64_t K, uint8_t* codes,
+                               uint16_t* scale, uint16_t* zero, void* stream) {
+  return milo_quantize_rtn_int3_grouped(W, rows, K, kGroup, codes, scale, zero, stream);
+}
+
+int64_t milo_lr_v_words(int32_t max_rank, int64_t K) { return 3 * (int64_t)max_rank * K / 32; }
+int64_t milo_lr_v_sz_words(int32_t max_rank, int64_t K) { return (int64_t)max_rank * K / 64; }
+int64_t milo_lr_u_words(int64_t N, int32_t max_rank) { return 3 * N * (int64_t)round_up(max_rank, 32) / 32; }
+int64_t milo_lr_u_sz_words(int64_t N) { return N; }
+
+int32_t milo_pack_lr_int3(const uint8_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
+                          const uint8_t* u_codes, const uint16_t* u_scale, const uint16_t* u_zero,
+                          int64_t N, int64_t K, int32_t rank, int32_t max_rank, uint32_t* vq,
+                          uint32_t* vsz, uint32_t* uq, uint32_t* usz, void* stream) {
+  g_err[0] = 0;
+  if (!vq || !vsz || !uq || !usz) MILO_FAIL(MILO_ERR_NULL, "vq, vsz, uq, usz are required");
+  if (rank > 0 && (!v_codes || !v_scale || !v_zero || !u_codes || !u_scale || !u_zero))
+    MILO_FAIL(MILO_ERR_NULL, "codes, scales and zeros of both factors are required when rank > 0");
+  if (N <= 0 || K <= 0 || N % 64 || K % 128 || N > 65536 || K > 65536)
+    MILO_FAIL(MILO_ERR_SHAPE, "N=%lld K=%lld: need N %% 64 == 0, K %% 128 == 0, both in 1..65536",
+              (long long)N, (long long)K);
+  if (max_rank < 8 || max_rank > kMaxRank || max_rank % 8 || rank < 0 || rank > max_rank || rank % 8)
+    MILO_FAIL(MILO_ERR_RANK, "rank=%d max_rank=%d: need 0 <= rank <= max_rank, 8 <= max_rank <= 64, "
+              "multiples of 8", rank, max_rank);
+  if (!aligned(vq, 16) || !aligned(vsz, 16) || !aligned(uq, 16) || !aligned(usz, 16))
+    MILO_FAIL(MILO_ERR_ALIGN, "vq, vsz, uq, usz must be 16-byte aligned");
+  if (!aligned(v_scale, 2) || !aligned(v_zero, 2) || !aligned(u_scale, 2) || !aligned(u_zero, 2))
+    MILO_FAIL(MILO_ERR_ALIGN, "scales and zeros must be 2-byte aligned");
+  return launch_pack_lr(v_codes, v_scale, v_zero, u_codes, u_scale, u_zero, N, K, rank, max_rank, vq,
+                        vsz, uq, usz, (hipStream_t)stream);
 }
 
 int32_t milo_pack_int3(const uint8_t* codes, const uint16_t* scale, const uint16_t* zero,

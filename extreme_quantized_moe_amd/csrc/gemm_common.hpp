@@ -13,12 +13,15 @@ struct GemmArgs {
   const uint32_t* packed[2];
   const uint32_t* sz[2];
   const uint16_t* U[2];
+  const uint32_t* Uq[2];   // int3 compensator: U layout codes and row scale/zero
+  const uint32_t* Usz[2];
   const int32_t* rank[2];
   const uint16_t* T;       // fp16 [P][n_w * rp] low-rank pre-pass output
   void* y;
   float* part;             // split-K partial sums
   const float* pw;         // per pair (sorted order): route weight (small-M path)
-  int64_t words_per_expert, sz_per_expert;
+  int64_t words_per_expert, sz_per_expert, uq_per_expert;
+  int lrq;                 // compensator factors are int3
   int N, K, kblocks, n_tiles, gather_div, num_experts, n_w, rp, max_rank;
   int epilogue, ksplit, dec_max_rows, pre_min_rows;
   int m_lo, m_hi;          // row-count range of the experts a decode launch handles

@@ -32,9 +32,12 @@
 // m-tile; rows past the expert's count are zero), the codes the B operand.
 //
 // Item end: the low-rank term (x V^T) U^T of each m-tile is added by the
-// wave with w % KW = f for weight family f (its T and U fragments were loaded
-// when the item started), the waves are summed in LDS in wave order, and the epilogue stores fp16 (NONE / SWIGLU) or
-// scales by the pair's route weight and scatters fp32 (ROUTE_SCALE).  With
+// waves of that m-tile, split by weight family and 32-rank step (their T and
+// U fragments were loaded when the item started; int3 U tiles are extracted
+// and dequantized here),
+// the waves are summed in LDS in wave order, and the epilogue stores fp16
+// (NONE / SWIGLU) or scales by the pair's route weight and scatters fp32
+// (ROUTE_SCALE).  With
 // several K splits each split stores its sum and gemm_decode_reduce adds the
 // splits in split order (no cross-block synchronisation inside a kernel).
 #include "gemm_common.hpp"
@@ -192,16 +195,30 @@ struct Dec {
   }
 };
 
+// U operand of the low-rank term of one item (the NS rank steps of 32 that
+// this wave adds): fp16 fragments (64 n rows x 32 ranks per step), or with
+// int3 factors the lane's triplet of each 32-rank U tile plus the scale/zero
+// words of its four rows (dequantized at the item's end).
+template <bool LRQ, int NS>
+struct LateU {
+  f16x8 u[4][NS];
+};
+template <int NS>
+struct LateU<true, NS> {
+  uint32_t q[NS][3];
+  u32x4 sz;
+};
+
 // Per-item values loaded when an item starts and used at its end.
-template <int MP>
+template <int MP, bool LRQ, int NS>
 struct ItemLate {
-  f16x8 t[2];         // low-rank T fragments (rows of this wave's m-tile x 32 ranks)
-  f16x8 u[4][2];      // U fragments (64 n rows x 32 ranks) of this wave's family
+  f16x8 t[NS];        // low-rank T fragments (rows of this wave's m-tile x 32 ranks)
+  LateU<LRQ, NS> lu;  // U operand of this wave's family
   int32_t sp[MP * 4]; // ROUTE_SCALE: slot index of each output row of this thread
   float pw[MP * 4];   // ROUTE_SCALE: route weight of those rows
 };
 
-template <int MP, int NW, int EPI, int DEPTH>
+template <int MP, int NW, int EPI, int DEPTH, bool LRQ>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_decode_kernel(GemmArgs a) {
   using DecT = Dec<MP, NW, EPI>;
@@ -234,7 +251,13 @@ gemm_decode_kernel(GemmArgs a) {
   DecT D(a, sh, total);
   const int lane = D.lane, wave = D.wave, kw = D.kw, mtile = D.mtile;
   const int RW = a.n_w * a.rp;
-  const int lrf = kw < NW ? kw : 0;       // weight family whose low-rank term this wave adds
+  // low-rank work of this wave: family kw mod NW, rank steps (32 ranks each)
+  // kw / NW + l LRW for l < NS, so the waves of an m-tile share the item-end
+  // work (steps past the padded rank are skipped)
+  constexpr int LRW = KW / NW;
+  constexpr int NS = LRW >= 2 ? 1 : 2;
+  const int lrf = kw % NW;
+  const int s2_0 = kw / NW;
 
   f32x4 acc[NW][4];
 #pragma unroll
@@ -245,26 +268,39 @@ gemm_decode_kernel(GemmArgs a) {
   // item-start loads: low-rank fragments (every wave loads, waves that add no
   // low-rank term ignore them) and the epilogue's row metadata.  Addresses are
   // clamped to valid memory and masked values replaced, so every load is issued.
-  ItemLate<MP> late;
+  ItemLate<MP, LRQ, NS> late;
   auto load_late = [&](const Item& m) {
     if (a.rp > 0) {
       const int rk = sh.rank[lrf][m.e];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
+      for (int l = 0; l < NS; ++l) {
+        const int s2 = s2_0 + l * LRW;
         const int j0 = 32 * s2 + 8 * (lane >> 4);
         const bool jok = j0 < rk;
         const int jc = jok ? j0 : 0;
         const int row = mtile * 16 + (lane & 15);
         const bool ok = jok && row < m.M;
         const f16x8 v = *(const f16x8*)(a.T + (size_t)(m.base + (row < m.M ? row : 0)) * RW + lrf * a.rp + jc);
-        late.t[s2] = ok ? v : f16x8{};
+        late.t[l] = ok ? v : f16x8{};    // ranks >= rank: zero, so U's padding adds nothing
+        if constexpr (LRQ) {
+          // 32-rank tile s2 if the expert has ranks there, else tile 0 (valid memory, unused)
+          const int jt = 32 * s2 < rk ? s2 : 0;
+          const uint32_t* up = a.Uq[lrf] + m.e * a.uq_per_expert +
+                               ((size_t)m.nt * (a.rp / 32) + jt) * 192 + lane;
+          late.lu.q[l][0] = up[0];
+          late.lu.q[l][1] = up[64];
+          late.lu.q[l][2] = up[128];
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = m.nt * kTileRows + 16 * i + (lane & 15);
-          const f16x8 u = *(const f16x8*)(a.U[lrf] + ((size_t)m.e * a.N + n) * a.max_rank + jc);
-          late.u[i][s2] = jok ? u : f16x8{};
+          for (int i = 0; i < 4; ++i) {
+            const int n = m.nt * kTileRows + 16 * i + (lane & 15);
+            const f16x8 u = *(const f16x8*)(a.U[lrf] + ((size_t)m.e * a.N + n) * a.max_rank + jc);
+            late.lu.u[i][l] = jok ? u : f16x8{};
+          }
         }
       }
+      if constexpr (LRQ)
+        late.lu.sz = *(const u32x4*)(a.Usz[lrf] + (size_t)m.e * a.N + m.nt * kTileRows + 4 * (lane & 15));
     }
     if (EPI == MILO_EPI_ROUTE_SCALE) {
 #pragma unroll
@@ -278,16 +314,30 @@ gemm_decode_kernel(GemmArgs a) {
   };
 
   auto finish_item = [&](const Item& m) {
-    // low-rank term of family kw for this wave's m-tile (added once: by the first K split)
-    if (kw < NW && a.rp > 0 && m.ks == 0) {
+    // low-rank term of family lrf, rank steps s2_0 + l LRW, for this wave's
+    // m-tile (added once: by the first K split)
+    if (a.rp > 0 && m.ks == 0) {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
+      for (int l = 0; l < NS; ++l) {
+        const int s2 = s2_0 + l * LRW;
         if (32 * s2 >= a.rp) break;
+        if constexpr (LRQ) {
+          uint32_t h[16];
+          extract_triplet(late.lu.q[l][0], late.lu.q[l][1], late.lu.q[l][2], h, D.kc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) {
+            const f16x8 ub = dequant_step(h, i, group_const(late.lu.sz[i]));
 #pragma unroll
-          for (int f = 0; f < NW; ++f)
-            if (f == kw) acc[f][i] = mfma16x16x32(late.t[s2], late.u[i][s2], acc[f][i]);
+            for (int f = 0; f < NW; ++f)
+              if (f == lrf) acc[f][i] = mfma16x16x32(late.t[l], ub, acc[f][i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int f = 0; f < NW; ++f)
+              if (f == lrf) acc[f][i] = mfma16x16x32(late.t[l], late.lu.u[i][l], acc[f][i]);
+        }
       }
     }
     __syncthreads();   // previous item's readers of red are done
@@ -371,7 +421,10 @@ gemm_decode_kernel(GemmArgs a) {
 template <int MP, int NW, int EPI>
 static void launch_one(const GemmArgs& a, int blocks, int num_experts, hipStream_t st) {
   constexpr int depth = NW == 1 ? 3 : 2;
-  hipLaunchKernelGGL((gemm_decode_kernel<MP, NW, EPI, depth>), dim3(blocks), dim3(256), 0, st, a);
+  if (a.lrq)
+    hipLaunchKernelGGL((gemm_decode_kernel<MP, NW, EPI, depth, true>), dim3(blocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_decode_kernel<MP, NW, EPI, depth, false>), dim3(blocks), dim3(256), 0, st, a);
   if (a.ksplit > 1)
     hipLaunchKernelGGL((gemm_split_reduce<16 * MP, NW, EPI>), dim3(a.n_tiles, num_experts), dim3(256), 0,
                        st, a);

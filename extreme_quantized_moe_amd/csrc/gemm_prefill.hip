@@ -26,7 +26,7 @@ constexpr int kMT = kBM / 16;            // m-tiles per wave
 constexpr int kXStride = kTileK + 8;     // LDS row stride in halves (272 B)
 constexpr int kXBuf = kBM * kXStride;    // halves per buffer
 
-template <int NW>
+template <int NW, bool LRQ>
 __global__ void __launch_bounds__(256) gemm_prefill_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
@@ -128,17 +128,28 @@ __global__ void __launch_bounds__(256) gemm_prefill_kernel(GemmArgs a) {
     __syncthreads();
   }
 
-  // ---- low-rank term: (x V^T) U^T as extra K steps
+  // ---- low-rank term: (x V^T) U^T as extra K steps (int3 U: the lane's
+  // triplet of each 32-rank U tile is its B operand for the four row groups)
   if (wave_on && a.rp > 0) {
     const int RW = a.n_w * a.rp;
     const int rk = a.rank[f][e];
+    u32x4 usz = {0u, 0u, 0u, 0u};
+    if constexpr (LRQ) usz = *(const u32x4*)(a.Usz[f] + (size_t)e * a.N + nt * kTileRows + 4 * (lane & 15));
     for (int s2 = 0; s2 < a.rp / 32; ++s2) {
       const int j0 = 32 * s2 + 8 * (lane >> 4);
       f16x8 ub[4];
+      if constexpr (LRQ) {
+        const uint32_t* up = a.Uq[f] + e * a.uq_per_expert + ((size_t)nt * (a.rp / 32) + s2) * 192 + lane;
+        uint32_t h[16];
+        extract_triplet(up[0], up[64], up[128], h, kc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = nt * kTileRows + 16 * i + (lane & 15);
-        ub[i] = j0 < rk ? *(const f16x8*)(a.U[f] + ((size_t)e * a.N + n) * a.max_rank + j0) : f16x8{};
+        for (int i = 0; i < 4; ++i) ub[i] = j0 < rk ? dequant_step(h, i, group_const(usz[i])) : f16x8{};
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = nt * kTileRows + 16 * i + (lane & 15);
+          ub[i] = j0 < rk ? *(const f16x8*)(a.U[f] + ((size_t)e * a.N + n) * a.max_rank + j0) : f16x8{};
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
@@ -210,10 +221,12 @@ int32_t launch_gemm_prefill(const milo_gemm_desc* d, const GemmPlan& p, char* ws
   const size_t lds_bytes = 2 * kXBuf * sizeof(uint16_t);   // >= 2 x 128 x 64 fp32 for SWIGLU
   if (d->n_w == 2) {
     dim3 grid(p.pre_tiles, (p.n_tiles + 1) / 2);
-    hipLaunchKernelGGL(gemm_prefill_kernel<2>, grid, dim3(256), lds_bytes, st, a);
+    if (a.lrq) hipLaunchKernelGGL((gemm_prefill_kernel<2, true>), grid, dim3(256), lds_bytes, st, a);
+    else hipLaunchKernelGGL((gemm_prefill_kernel<2, false>), grid, dim3(256), lds_bytes, st, a);
   } else {
     dim3 grid(p.pre_tiles, (p.n_tiles + 3) / 4);
-    hipLaunchKernelGGL(gemm_prefill_kernel<1>, grid, dim3(256), lds_bytes, st, a);
+    if (a.lrq) hipLaunchKernelGGL((gemm_prefill_kernel<1, true>), grid, dim3(256), lds_bytes, st, a);
+    else hipLaunchKernelGGL((gemm_prefill_kernel<1, false>), grid, dim3(256), lds_bytes, st, a);
   }
   return hip_status(hipGetLastError(), "gemm_prefill_kernel launch");
 }

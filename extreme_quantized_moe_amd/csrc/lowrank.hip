@@ -11,16 +11,18 @@
 // T . U^T as two more matrix-core K-steps.
 //
 // Grid: x = 16-row tiles over all experts (expert by expert); y = compensator
-// ranks (decode) or groups of NRT rank tiles of 16 ranks (prefill), plus one
-// "aux" index for the gather / pair weights.
-// At decode (at most 32 rows per expert) a block computes one rank j of T for
-// its rows as plain dot products: the 256 threads read V row j in consecutive
-// 16-byte chunks (fully coalesced) and multiply with the same chunks of each
-// row; the per-thread partial sums are added in LDS in a fixed tree order.
-// At prefill a block is 4 waves on every rank tile of its rows on the matrix
-// cores (the activation rows are read once); wave partial sums are added in
-// LDS in wave order.
-#include "milo_internal.hpp"
+// ranks or groups of them (decode) or groups of NRT rank tiles of 16 ranks
+// (prefill), plus one "aux" index for the gather / pair weights.
+// At decode (at most 32 rows per expert) a block computes one rank (fp16 V)
+// or four ranks (int3 V) of T for its rows as plain dot products over
+// coalesced chunks of the V rows and the activation rows; per-thread partial
+// sums are added in a fixed tree order.  At prefill a block is 4 waves on
+// every rank tile of its rows on the matrix cores (the activation rows are
+// read once); wave partial sums are added in LDS in wave order.  int3 factors
+// ([talk] MiLo Algorithm, last step: U and V stored as int3) are dequantized
+// in registers: folded into the dot products at decode, to fp16 matrix-core
+// operands at prefill.
+#include "gemm_common.hpp"
 
 namespace milo {
 
@@ -30,6 +32,9 @@ struct PrepassArgs {
   const int32_t* offsets;
   const float* slot_w;
   const uint16_t* V[2];
+  const uint32_t* Vq[2];    // int3 factors: V layout codes and scale/zero
+  const uint32_t* Vsz[2];
+  int64_t vq_per_expert, vsz_per_expert;
   const int32_t* rank[2];
   uint16_t* T;        // fp16 [P][n_w * rp]
   uint16_t* xg;       // fp16 [P][K]: row of each pair (small-M experts), or null
@@ -77,13 +82,14 @@ __device__ void prepass_aux(const PrepassArgs& a, int e, int m0, int M) {
   }
 }
 
-// Decode form: block (16-row tile, rank j over all families), 512 threads.
+constexpr int kDotThreads = 512;
+
+// Decode form, fp16 V: block (16-row tile, rank j over all families), 512 threads.
 // The rows of the tile are rounded up to R2 (a power of two) and each row gets
 // 512 / R2 consecutive threads, which stride over the 16-byte chunks of V row j
 // and of the token row, eight chunks per batch of loads.  The partial sums of a
 // row are reduced in a fixed order: a butterfly inside each wave, then the
 // waves of that row in ascending order.
-constexpr int kDotThreads = 512;
 constexpr int kDotBatch = 8;
 
 __global__ void __launch_bounds__(kDotThreads) prepass_dot_kernel(PrepassArgs a) {
@@ -142,6 +148,167 @@ __global__ void __launch_bounds__(kDotThreads) prepass_dot_kernel(PrepassArgs a)
     for (int w = 0; w < wpr; ++w) sum += part[tid * wpr + w];
     tout[(size_t)tid * RW] = float_to_half_bits(sum);
   }
+}
+
+// Decode form, int3 V: block = (16-row tile, NJ consecutive ranks of one family),
+// 512 threads.  The rows of the tile are rounded up to R2 (a power of two) and
+// each row gets 512 / R2 consecutive threads, which stride over the row's K
+// (16-byte chunks of fp16 V, or 32-column triplets of int3 V), reading each
+// activation chunk once for the NJ ranks.  The partial sums of a (row, rank)
+// are reduced in a fixed order: a butterfly inside each wave, then the waves
+// of that row in ascending order.  Ranks at or beyond the expert's rank give
+// T = 0 (their V rows are not read).
+
+template <int NJ>
+__device__ __forceinline__ void dot_reduce_store(float (&acc)[NJ], int G, int rows, uint16_t* tout,
+                                                 int RW, float* part) {
+  const int tid = threadIdx.x, r = tid / G, g = tid - r * G;
+  const int W = G < 64 ? G : 64;
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj)
+    for (int o = W >> 1; o >= 1; o >>= 1) acc[jj] += __shfl_xor(acc[jj], o);
+  if (G < 64) {
+    if (g == 0 && r < rows)
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) tout[(size_t)r * RW + jj] = float_to_half_bits(acc[jj]);
+    return;
+  }
+  if ((tid & 63) == 0)
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) part[jj * (kDotThreads / 64) + (tid >> 6)] = acc[jj];
+  __syncthreads();
+  const int wpr = G >> 6;                         // waves per row
+  if (tid < rows * NJ) {
+    const int rr = tid / NJ, jj = tid - rr * NJ;
+    float sum = 0.f;
+    for (int w = 0; w < wpr; ++w) sum += part[jj * (kDotThreads / 64) + rr * wpr + w];
+    tout[(size_t)rr * RW + jj] = float_to_half_bits(sum);
+  }
+}
+
+// Common prologue of the decode forms: tile lookup, aux blocks, and the
+// block's (family, first rank, rows).  Returns false if the block is done.
+struct DotBlock {
+  int e, m0, M, base, RW, f, j0, rk, rows, R2, G, r, g;
+  uint16_t* tout;
+};
+
+template <int NJ>
+__device__ __forceinline__ bool dot_block(const PrepassArgs& a, DotBlock& b) {
+  if (!find_tile16(a.offsets, a.num_experts, blockIdx.x, &b.e, &b.m0, &b.M)) return false;
+  if ((int)blockIdx.y == a.aux_y) {
+    prepass_aux(a, b.e, b.m0, b.M);
+    return false;
+  }
+  b.base = a.offsets[b.e];
+  b.RW = a.n_w * a.rp;
+  const int y0 = blockIdx.y * NJ;
+  b.f = y0 / a.rp;
+  b.j0 = y0 - b.f * a.rp;
+  b.rows = (b.M - b.m0) < 16 ? (b.M - b.m0) : 16;
+  b.tout = a.T + (size_t)(b.base + b.m0) * b.RW + b.f * a.rp + b.j0;
+  b.rk = a.rank[b.f][b.e];
+  const int tid = threadIdx.x;
+  if (b.j0 >= b.rk) {                             // beyond the expert's rank: T = 0
+    if (tid < b.rows * NJ) b.tout[(size_t)(tid / NJ) * b.RW + tid % NJ] = 0;
+    return false;
+  }
+  b.R2 = b.rows <= 1 ? 1 : b.rows <= 2 ? 2 : b.rows <= 4 ? 4 : b.rows <= 8 ? 8 : 16;
+  b.G = kDotThreads / b.R2;                       // threads per row, 32 .. 512
+  b.r = tid / b.G;
+  b.g = tid - b.r * b.G;
+  return true;
+}
+
+// int3 V (row layout): triplets of 32 columns, two per batch of loads.
+// Dequantization is folded out of the dot product: v_dot2 forms
+// sum x (off + q) per 64-wide group from the extracted pairs as they are
+// (off = 64 or 8 per pair), and once per triplet the activation sums
+// sum x and sum x off; the group then adds s (sum x (off + q) - sum x off -
+// z sum x).
+template <int NJ>
+__global__ void __launch_bounds__(kDotThreads) prepass_dotq_kernel(PrepassArgs a) {
+  __shared__ float part[NJ * (kDotThreads / 64)];
+  const CodeConsts kc = make_code_consts();
+  DotBlock b;
+  if (!dot_block<NJ>(a, b)) return;
+  constexpr int B = 2;
+  const int T32 = a.K / 32;
+  float acc[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) acc[jj] = 0.f;
+  if (b.r < b.rows) {
+    const int i = b.base + b.m0 + b.r;
+    const int xr = a.gather_div > 0 ? a.sorted_pairs[i] / a.gather_div : i;
+    const uint16_t* xp = a.x + (size_t)xr * a.K;
+    const uint32_t* qp = a.Vq[b.f] + b.e * a.vq_per_expert + (size_t)b.j0 * T32 * 3;
+    const uint32_t* sp = a.Vsz[b.f] + b.e * a.vsz_per_expert + (size_t)b.j0 * (a.K / kGroup);
+    const f16x2 one2 = {(_Float16)1.f, (_Float16)1.f};
+    for (int t0 = b.g; t0 < T32; t0 += B * b.G) {
+      uint32_t q[B][NJ][3];
+      uint2 zw[B][NJ];
+      f16x8 xv[B][4];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int tau = t0 + b.G * u;
+        const bool in = tau < T32;
+        const int tc = in ? tau : 0;
+        const uint16_t* xc = xp + 128 * (tc >> 2) + 8 * (tc & 3);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xv[u][s] = in ? *(const f16x8*)(xc + 32 * s) : f16x8{};
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+          const bool ld = b.j0 + jj < b.rk;       // block-uniform
+          const uint32_t* tp = qp + ((size_t)jj * T32 + tc) * 3;
+          q[u][jj][0] = ld ? tp[0] : 0u;
+          q[u][jj][1] = ld ? tp[1] : 0u;
+          q[u][jj][2] = ld ? tp[2] : 0u;
+          zw[u][jj] = ld ? *(const uint2*)(sp + (size_t)jj * (a.K / kGroup) + 2 * (tc >> 2)) : uint2{0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        // activation sums of the two groups: sum x and sum x off
+        float dx[2], dxo[2];
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          float d64 = 0.f, d8 = 0.f;
+#pragma unroll
+          for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int s = 2 * gg + ss, pi = 4 * s + v;
+              const f16x2 x2 = {xv[u][s][2 * v], xv[u][s][2 * v + 1]};
+              if (pair_offset(pi) == 64) d64 = __builtin_amdgcn_fdot2(x2, one2, d64, false);
+              else d8 = __builtin_amdgcn_fdot2(x2, one2, d8, false);
+            }
+          dx[gg] = d64 + d8;
+          dxo[gg] = __builtin_fmaf(64.f, d64, 8.f * d8);
+        }
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+          uint32_t h[16];
+          extract_triplet(q[u][jj][0], q[u][jj][1], q[u][jj][2], h, kc);
+#pragma unroll
+          for (int gg = 0; gg < 2; ++gg) {
+            float dq = 0.f;
+#pragma unroll
+            for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const int s = 2 * gg + ss, pi = 4 * s + v;
+                const f16x2 x2 = {xv[u][s][2 * v], xv[u][s][2 * v + 1]};
+                dq = __builtin_amdgcn_fdot2(x2, __builtin_bit_cast(f16x2, h[pi]), dq, false);
+              }
+            const uint32_t w = gg ? zw[u][jj].y : zw[u][jj].x;
+            const float sc = half_bits_to_float(w & 0xFFFFu), zp = half_bits_to_float(w >> 16);
+            acc[jj] = __builtin_fmaf(sc, __builtin_fmaf(-zp, dx[gg], dq - dxo[gg]), acc[jj]);
+          }
+        }
+      }
+    }
+  }
+  dot_reduce_store<NJ>(acc, b.G, b.rows, b.tout, b.RW, part);
 }
 
 template <int NRT, int NWAVES, int UNR>
@@ -222,6 +389,116 @@ __global__ void __launch_bounds__(64 * NWAVES) prepass_kernel(PrepassArgs a) {
   }
 }
 
+// int3 factors, prefill form: block = one 16-row tile of pairs x NRT rank
+// tiles of 16 ranks; its NWAVES waves split the 128-wide K blocks.  Per K
+// block a lane loads the triplet (row 16 jt + L mod 16, kq = L div 16) of
+// each rank tile -- in the V layout that triplet is exactly its matrix-core
+// B operand for the block's four 16x16x32 steps -- and the row's two
+// scale/zero words, extracts the codes and dequantizes them to fp16
+// ((q - z) s, rounded once).  Rank rows at or beyond the expert's rank are
+// not loaded (zero operand), so T is exactly 0 there.  Wave partials are
+// added in LDS in wave order.
+template <int NRT, int NWAVES, int UNR>
+__global__ void __launch_bounds__(64 * NWAVES) prepass_q_kernel(PrepassArgs a) {
+  __shared__ float red[NWAVES][NRT][64][4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const CodeConsts kc = make_code_consts();
+  int e, m0, M;
+  if (!find_tile16(a.offsets, a.num_experts, blockIdx.x, &e, &m0, &M)) return;
+  if ((int)blockIdx.y == a.aux_y) {
+    prepass_aux(a, e, m0, M);
+    return;
+  }
+  const int base = a.offsets[e];
+  const int RW = a.n_w * a.rp;
+  const int tiles_per_w = a.rp / 16;
+  const int tr0 = blockIdx.y * NRT;
+  const int KB = a.K / kTileK;
+  const int T32 = a.K / 32;
+
+  const int m = m0 + (lane & 15);
+  const bool row_ok = m < M;
+  int xr = 0;
+  if (row_ok) xr = a.gather_div > 0 ? a.sorted_pairs[base + m] / a.gather_div : base + m;
+  const uint16_t* xp = a.x + (size_t)xr * a.K + 8 * (lane >> 4);
+
+  const uint32_t* vq[NRT];
+  const uint32_t* vs[NRT];
+  bool vok[NRT];
+  bool any = false;
+#pragma unroll
+  for (int t = 0; t < NRT; ++t) {
+    const int tr = tr0 + t;
+    const int f = tr / tiles_per_w, jt = tr % tiles_per_w;
+    const int rk = a.rank[f][e];
+    const int j = 16 * jt + (lane & 15);
+    vok[t] = j < rk;                        // rank <= max_rank: the row is stored
+    any |= 16 * jt < rk;
+    const int jc = vok[t] ? j : 0;
+    vq[t] = a.Vq[f] + e * a.vq_per_expert + ((size_t)jc * T32 + (lane >> 4)) * 3;
+    vs[t] = a.Vsz[f] + e * a.vsz_per_expert + (size_t)jc * (a.K / kGroup);
+  }
+
+  f32x4 acc[NRT];
+#pragma unroll
+  for (int t = 0; t < NRT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (any) {
+    for (int kb0 = wave; kb0 < KB; kb0 += UNR * NWAVES) {
+      f16x8 xa[UNR][4];
+      uint32_t q[UNR][NRT][3], zw[UNR][NRT][2];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int kb = kb0 + NWAVES * u;
+        const bool in = kb < KB;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          xa[u][s] = (in && row_ok) ? *(const f16x8*)(xp + (size_t)kb * kTileK + 32 * s) : f16x8{};
+#pragma unroll
+        for (int t = 0; t < NRT; ++t) {
+          const bool ld = in && vok[t];
+          const uint32_t* qp = vq[t] + (size_t)(ld ? kb : 0) * 12;
+          q[u][t][0] = ld ? qp[0] : 0u;
+          q[u][t][1] = ld ? qp[1] : 0u;
+          q[u][t][2] = ld ? qp[2] : 0u;
+          const uint2 z2 = ld ? *(const uint2*)(vs[t] + 2 * (size_t)kb) : uint2{0u, 0u};
+          zw[u][t][0] = z2.x;
+          zw[u][t][1] = z2.y;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+#pragma unroll
+        for (int t = 0; t < NRT; ++t) {
+          uint32_t h[16];
+          extract_triplet(q[u][t][0], q[u][t][1], q[u][t][2], h, kc);
+          const GroupConst g0 = group_const(zw[u][t][0]), g1 = group_const(zw[u][t][1]);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            f16x8 vb = dequant_step(h, s, s < 2 ? g0 : g1);
+            if (!vok[t]) vb = f16x8{};
+            acc[t] = mfma16x16x32(xa[u][s], vb, acc[t]);
+          }
+        }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NRT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][t][lane][r] = acc[t][r];
+  __syncthreads();
+
+  for (int o = threadIdx.x; o < NRT * 256; o += 64 * NWAVES) {
+    const int t = o >> 8, ln = (o >> 2) & 63, r = o & 3;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) v += red[w][t][ln][r];
+    const int row = 4 * (ln >> 4) + r;
+    const int col = (tr0 + t) * 16 + (ln & 15);
+    if (m0 + row < M) a.T[(size_t)(base + m0 + row) * RW + col] = float_to_half_bits(v);
+  }
+}
+
 int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st) {
   const int nrt = d->n_w * p.rp / 16;                   // rank tiles in total
   const int per = p.rp ? p.lr_tiles_per_block : 1;      // 1 (decode) or nrt (prefill)
@@ -236,9 +513,15 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
   a.offsets = d->offsets;
   a.slot_w = d->slot_w;
   for (int f = 0; f < 2; ++f) {
-    a.V[f] = d->w[f < d->n_w ? f : 0].V;
-    a.rank[f] = d->w[f < d->n_w ? f : 0].rank;
+    const milo_weights& w = d->w[f < d->n_w ? f : 0];
+    a.V[f] = w.V;
+    a.Vq[f] = w.Vq;
+    a.Vsz[f] = w.Vsz;
+    a.rank[f] = w.rank;
   }
+  const bool lrq = d->w[0].lr_format == MILO_LR_INT3;
+  a.vq_per_expert = d->max_rank ? milo_lr_v_words(d->max_rank, d->K) : 0;
+  a.vsz_per_expert = d->max_rank ? milo_lr_v_sz_words(d->max_rank, d->K) : 0;
   a.T = (uint16_t*)(ws + p.off_t);
   a.xg = need_xg ? (uint16_t*)(ws + p.off_xg) : nullptr;
   a.pw = need_pw ? (float*)(ws + p.off_pw) : nullptr;
@@ -250,12 +533,29 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
   a.max_rank = d->max_rank;
   a.aux_y = aux_blocks ? rank_blocks : -1;
   a.dec_max_rows = p.dec_max_rows;
-  if (per == 1) {                                   // decode: one block per rank
-    const int rank_rows = p.rp ? d->n_w * p.rp : 0;
-    a.aux_y = aux_blocks ? rank_rows : -1;
-    dim3 grid(p.lr_tiles, rank_rows + aux_blocks);
-    hipLaunchKernelGGL(prepass_dot_kernel, grid, dim3(kDotThreads), 0, st, a);
-  } else {
+  if (per == 1) {                                   // decode
+    constexpr int kNJ3 = 4;
+    const int nj = lrq ? kNJ3 : 1;
+    const int rank_groups = p.rp ? d->n_w * p.rp / nj : 0;
+    a.aux_y = aux_blocks ? rank_groups : -1;
+    dim3 grid(p.lr_tiles, rank_groups + aux_blocks);
+    if (lrq) hipLaunchKernelGGL(prepass_dotq_kernel<kNJ3>, grid, dim3(kDotThreads), 0, st, a);
+    else hipLaunchKernelGGL(prepass_dot_kernel, grid, dim3(kDotThreads), 0, st, a);
+    return hip_status(hipGetLastError(), "prepass_dot_kernel launch");
+  }
+  if (lrq) {
+    dim3 grid(p.lr_tiles, rank_blocks + aux_blocks);
+    switch (per) {
+      case 2: hipLaunchKernelGGL((prepass_q_kernel<2, 4, 2>), grid, dim3(256), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((prepass_q_kernel<4, 4, 2>), grid, dim3(256), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((prepass_q_kernel<8, 4, 2>), grid, dim3(256), 0, st, a); break;
+      default:
+        set_error("internal: unsupported rank-tile count %d", per);
+        return MILO_ERR_RANK;
+    }
+    return hip_status(hipGetLastError(), "prepass_q_kernel launch");
+  }
+  {
     dim3 grid(p.lr_tiles, rank_blocks + aux_blocks);
     switch (per) {
       case 2: hipLaunchKernelGGL((prepass_kernel<2, 4, 4>), grid, dim3(256), 0, st, a); break;

@@ -157,8 +157,12 @@ void set_error(const char* fmt, ...);
 int32_t hip_status(hipError_t e, const char* what);
 
 // launchers (return MILO_OK or MILO_ERR_HIP)
-int32_t launch_quantize(const float* W, int64_t rows, int64_t K, uint8_t* codes,
+int32_t launch_quantize(const float* W, int64_t rows, int64_t K, int group, uint8_t* codes,
                         uint16_t* scale, uint16_t* zero, hipStream_t st);
+int32_t launch_pack_lr(const uint8_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
+                       const uint8_t* u_codes, const uint16_t* u_scale, const uint16_t* u_zero,
+                       int64_t N, int64_t K, int rank, int max_rank, uint32_t* vq, uint32_t* vsz,
+                       uint32_t* uq, uint32_t* usz, hipStream_t st);
 int32_t launch_pack(const uint8_t* codes, const uint16_t* scale, const uint16_t* zero,
                     int64_t rows, int64_t K, uint32_t* packed, uint32_t* sz, hipStream_t st);
 int32_t launch_route(const float* logits, int T, int E, int k, int S, int renorm,

@@ -39,19 +39,22 @@ __device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
   return (double)(float)__builtin_bit_cast(_Float16, h);
 }
 
-// One wave per (row, group): lane = column inside the group.
+// One wave per (row, group): lane = column inside the group (group <= 64;
+// lanes past the group take part in the min/max with the group's first value).
 __global__ void __launch_bounds__(256) quantize_kernel(const float* __restrict__ W, int64_t rows,
-                                                       int64_t K, uint8_t* __restrict__ codes,
+                                                       int64_t K, int group,
+                                                       uint8_t* __restrict__ codes,
                                                        uint16_t* __restrict__ scale,
                                                        uint16_t* __restrict__ zero) {
   const int lane = threadIdx.x & 63;
-  const int64_t groups = K / kGroup;
+  const int64_t groups = K / group;
   const int64_t total = rows * groups;
   const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const bool in = lane < group;
   for (int64_t gi = wave0; gi < total; gi += nwaves) {
     const int64_t r = gi / groups, g = gi - r * groups;
-    const int64_t idx = r * K + g * kGroup + lane;
+    const int64_t idx = r * K + g * group + (in ? lane : 0);
     const float w = W[idx];
     float lo = w, hi = w;
 #pragma unroll
@@ -68,7 +71,7 @@ __global__ void __launch_bounds__(256) quantize_kernel(const float* __restrict__
     const double z = f16_bits_to_f64(zb);
     double q = rint((double)w / s + z);
     q = fmin(fmax(q, 0.0), 7.0);
-    codes[idx] = (uint8_t)q;
+    if (in) codes[idx] = (uint8_t)q;
     if (lane == 0) {
       scale[r * groups + g] = sb;
       zero[r * groups + g] = zb;
@@ -124,6 +127,87 @@ __global__ void __launch_bounds__(256) pack_kernel(const uint8_t* __restrict__ c
   }
 }
 
+// Set the bits of code c (value q) of a triplet, layout v1 bit assignment.
+__device__ __forceinline__ void put_code(uint32_t (&word)[3], int c, uint32_t q) {
+  const int pi = c >> 1, h = c & 1;
+  if (pi < 15) {
+    word[pi / 5] |= q << (16 * h + 1 + 3 * (pi % 5));
+  } else {
+#pragma unroll
+    for (int b = 0; b < 3; ++b) word[b] |= ((q >> b) & 1u) << (16 * h);
+  }
+}
+
+constexpr uint32_t kPadSz = 0x00003C00u;   // scale 1.0, zero 0.0
+
+// V factor of an int3 compensator: one thread per (rank row j, triplet tau);
+// the threads of triplets kq = 0 and 1 of each 128-wide block also write the
+// row's two group words.
+__global__ void __launch_bounds__(256) pack_lr_v_kernel(const uint8_t* __restrict__ codes,
+                                                        const uint16_t* __restrict__ scale,
+                                                        const uint16_t* __restrict__ zero,
+                                                        int rank, int max_rank, int64_t K,
+                                                        uint32_t* __restrict__ vq,
+                                                        uint32_t* __restrict__ vsz) {
+  const int64_t T32 = K / 32, groups = K / kGroup;
+  const int64_t n = (int64_t)max_rank * T32;
+  for (int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; tid < n;
+       tid += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t j = tid / T32, tau = tid - j * T32;
+    const int64_t kb = tau >> 2;
+    const int kq = (int)(tau & 3);
+    uint32_t word[3] = {0u, 0u, 0u};
+    if (j < rank) {
+      const uint8_t* rowp = codes + j * K + kb * kTileK + 8 * kq;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) put_code(word, c, rowp[32 * (c >> 3) + (c & 7)] & 7u);
+    }
+    vq[3 * tid] = word[0];
+    vq[3 * tid + 1] = word[1];
+    vq[3 * tid + 2] = word[2];
+    if (kq < 2) {
+      const int64_t gg = 2 * kb + kq;
+      vsz[j * groups + gg] =
+          j < rank ? ((uint32_t)scale[j * groups + gg] | ((uint32_t)zero[j * groups + gg] << 16)) : kPadSz;
+    }
+  }
+}
+
+// U factor: one thread per (64-row x 32-rank tile, lane); the lanes of rank
+// tile 0 also write their n-tile's scale/zero words.
+__global__ void __launch_bounds__(256) pack_lr_u_kernel(const uint8_t* __restrict__ codes,
+                                                        const uint16_t* __restrict__ scale,
+                                                        const uint16_t* __restrict__ zero,
+                                                        int64_t N, int rank, int R32,
+                                                        uint32_t* __restrict__ uq,
+                                                        uint32_t* __restrict__ usz) {
+  const int JT = R32 / 32;
+  const int64_t n_all = (N / kTileRows) * JT * 64;
+  for (int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; tid < n_all;
+       tid += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t tile = tid >> 6;
+    const int L = (int)(tid & 63);
+    const int64_t nt = tile / JT;
+    const int jt = (int)(tile - nt * JT);
+    uint32_t word[3] = {0u, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      const int64_t n = 64 * nt + 16 * (c >> 3) + (L & 15);
+      const int j = 32 * jt + 8 * (L >> 4) + (c & 7);
+      if (j < rank) put_code(word, c, codes[n * rank + j] & 7u);
+    }
+    uint32_t* tp = uq + tile * 192 + L;
+    tp[0] = word[0];
+    tp[64] = word[1];
+    tp[128] = word[2];
+    if (jt == 0) {
+      const int64_t n = 64 * nt + L;
+      usz[64 * nt + 4 * (L & 15) + (L >> 4)] =
+          rank > 0 ? ((uint32_t)scale[n] | ((uint32_t)zero[n] << 16)) : kPadSz;
+    }
+  }
+}
+
 static int grid_for(int64_t work, int per_block) {
   int64_t g = (work + per_block - 1) / per_block;
   if (g > 65536) g = 65536;
@@ -131,11 +215,11 @@ static int grid_for(int64_t work, int per_block) {
   return (int)g;
 }
 
-int32_t launch_quantize(const float* W, int64_t rows, int64_t K, uint8_t* codes,
+int32_t launch_quantize(const float* W, int64_t rows, int64_t K, int group, uint8_t* codes,
                         uint16_t* scale, uint16_t* zero, hipStream_t st) {
-  const int64_t waves = rows * (K / kGroup);
+  const int64_t waves = rows * (K / group);
   hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(waves, 4)), dim3(256), 0, st, W, rows, K,
-                     codes, scale, zero);
+                     group, codes, scale, zero);
   return hip_status(hipGetLastError(), "quantize_kernel launch");
 }
 
@@ -145,6 +229,22 @@ int32_t launch_pack(const uint8_t* codes, const uint16_t* scale, const uint16_t*
   hipLaunchKernelGGL(pack_kernel, dim3(grid_for(ntrip, 256)), dim3(256), 0, st, codes, scale,
                      zero, rows, K, packed, sz);
   return hip_status(hipGetLastError(), "pack_kernel launch");
+}
+
+int32_t launch_pack_lr(const uint8_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
+                       const uint8_t* u_codes, const uint16_t* u_scale, const uint16_t* u_zero,
+                       int64_t N, int64_t K, int rank, int max_rank, uint32_t* vq, uint32_t* vsz,
+                       uint32_t* uq, uint32_t* usz, hipStream_t st) {
+  const int R32 = (max_rank + 31) / 32 * 32;
+  const int64_t nv = (int64_t)max_rank * (K / 32);
+  hipLaunchKernelGGL(pack_lr_v_kernel, dim3(grid_for(nv, 256)), dim3(256), 0, st, v_codes, v_scale,
+                     v_zero, rank, max_rank, K, vq, vsz);
+  int32_t rc = hip_status(hipGetLastError(), "pack_lr_v_kernel launch");
+  if (rc != MILO_OK) return rc;
+  const int64_t nu = (N / kTileRows) * (R32 / 32) * 64;
+  hipLaunchKernelGGL(pack_lr_u_kernel, dim3(grid_for(nu, 256)), dim3(256), 0, st, u_codes, u_scale,
+                     u_zero, N, rank, R32, uq, usz);
+  return hip_status(hipGetLastError(), "pack_lr_u_kernel launch");
 }
 
 }  // namespace milo

@@ -34,17 +34,46 @@ def sz_words(rows, K):
     return int(L.lib().milo_sz_words(rows, K))
 
 
-def quantize_rtn_int3(W):
-    """fp32 [rows][K] -> (codes u8 [rows][K], scale fp16 [rows][K/64], zero fp16)."""
+def quantize_rtn_int3(W, group=64):
+    """fp32 [rows][K] -> (codes u8 [rows][K], scale fp16 [rows][K/group], zero fp16)."""
     W = W.contiguous()
     _cuda(W)
     rows, K = W.shape
     codes = torch.empty((rows, K), dtype=torch.uint8, device=W.device)
-    scale = torch.empty((rows, K // 64), dtype=torch.float16, device=W.device)
+    scale = torch.empty((rows, K // group), dtype=torch.float16, device=W.device)
     zero = torch.empty_like(scale)
-    check("milo_quantize_rtn_int3", L.lib().milo_quantize_rtn_int3(
-        _p(W), rows, K, _p(codes), _p(scale), _p(zero), _stream()))
+    if group == 64:
+        check("milo_quantize_rtn_int3", L.lib().milo_quantize_rtn_int3(
+            _p(W), rows, K, _p(codes), _p(scale), _p(zero), _stream()))
+    else:
+        check("milo_quantize_rtn_int3_grouped", L.lib().milo_quantize_rtn_int3_grouped(
+            _p(W), rows, K, group, _p(codes), _p(scale), _p(zero), _stream()))
     return codes, scale, zero
+
+
+def lr_words(N, K, max_rank):
+    """Per-expert uint32 word counts of the int3 compensator layouts:
+    (V codes, V scale/zero, U codes, U scale/zero)."""
+    lib = L.lib()
+    return (int(lib.milo_lr_v_words(max_rank, K)), int(lib.milo_lr_v_sz_words(max_rank, K)),
+            int(lib.milo_lr_u_words(N, max_rank)), int(lib.milo_lr_u_sz_words(N)))
+
+
+def pack_lr_int3(v, u, N, K, rank, max_rank, out=None):
+    """Pack one expert's quantized factors: v = (codes [rank][K], scale, zero
+    [rank][K/64]), u = (codes [N][rank], scale, zero [N]) (None when rank == 0).
+    out: optional (vq, vsz, uq, usz) int32 views to write into."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    if out is None:
+        out = tuple(torch.empty(n, dtype=torch.int32, device=dev) for n in lr_words(N, K, max_rank))
+    vq, vsz, uq, usz = out
+    vc, vs, vz = v if v is not None else (None, None, None)
+    uc, us, uz = u if u is not None else (None, None, None)
+    _cuda(vc, vs, vz, uc, us, uz, vq, vsz, uq, usz)
+    check("milo_pack_lr_int3", L.lib().milo_pack_lr_int3(
+        _p(vc), _p(vs), _p(vz), _p(uc), _p(us), _p(uz), N, K, rank, max_rank,
+        _p(vq), _p(vsz), _p(uq), _p(usz), _stream()))
+    return out
 
 
 def pack_int3(codes, scale, zero):
@@ -96,19 +125,26 @@ def route_sort(logits, k, S=0, renormalize=True):
 
 class Family:
     """One projection family (e.g. every expert's W1) in the library's format:
-    packed int3 codes (layout v1), tiled scale/zero, compensator factors
-    U [E][N][max_rank] and V [E][max_rank][K] (fp16, zero beyond each expert's
-    rank) and the device rank array."""
+    packed int3 codes (layout v1), tiled scale/zero, compensator factors and
+    the device rank array.  Factors are fp16 U [E][N][max_rank] and
+    V [E][max_rank][K] (zero beyond each expert's rank), or with
+    lr_format "int3" the int3 compensator layouts Uq, Usz, Vq, Vsz."""
 
-    def __init__(self, packed, sz, U, V, rank, num_experts, N, K, max_rank):
+    def __init__(self, packed, sz, U, V, rank, num_experts, N, K, max_rank,
+                 lr_format="fp16", lrq=None):
         self.packed, self.sz, self.U, self.V, self.rank = packed, sz, U, V, rank
         self.num_experts, self.N, self.K, self.max_rank = num_experts, N, K, max_rank
+        self.lr_format = lr_format
+        self.lrq = lrq            # (Vq, Vsz, Uq, Usz) for int3 factors
 
     @staticmethod
-    def from_dense(Ws, As, Bs, max_rank=None, device="cuda"):
+    def from_dense(Ws, As, Bs, max_rank=None, device="cuda", lr_format="fp16"):
         """Ws: list of fp32 [N][K]; As: list of fp16 [K][r_e]; Bs: fp16 [r_e][N]
         (the compensator as X A B, i.e. V = A^T, U = B^T).  Quantizes each W on
-        the GPU (RTN int3, group 64) and packs all experts in one call."""
+        the GPU (RTN int3, group 64) and packs all experts in one call.  With
+        lr_format "int3" the factors are quantized on the GPU as well (V rows
+        in groups of 64 along K, U rows in one group of r_e) and packed per
+        expert."""
         E = len(Ws)
         N, K = Ws[0].shape
         ranks = [int(a.shape[1]) for a in As]
@@ -122,6 +158,13 @@ class Family:
             scale[e * N:(e + 1) * N] = s
             zero[e * N:(e + 1) * N] = z
         packed, sz = pack_int3(codes, scale, zero)
+        del codes, scale, zero
+        rank = torch.tensor(ranks, dtype=torch.int32, device=device)
+        if lr_format == "int3":
+            lrq = Family._pack_int3_factors(As, Bs, ranks, N, K, R, device)
+            return Family(packed, sz, None, None, rank, E, N, K, R, "int3", lrq)
+        if lr_format != "fp16":
+            raise ValueError(f"unknown compensator format {lr_format!r}")
         U = torch.zeros((E, N, max(R, 1)), dtype=torch.float16, device=device)
         V = torch.zeros((E, max(R, 1), K), dtype=torch.float16, device=device)
         for e in range(E):
@@ -129,21 +172,55 @@ class Family:
             if r:
                 U[e, :, :r] = Bs[e].to(device).t()
                 V[e, :r, :] = As[e].to(device).t()
-        rank = torch.tensor(ranks, dtype=torch.int32, device=device)
         return Family(packed, sz, U, V, rank, E, N, K, R)
+
+    @staticmethod
+    def _pack_int3_factors(As, Bs, ranks, N, K, R, device):
+        E = len(As)
+        if R == 0:
+            return None
+        nv, nvs, nu, nus = lr_words(N, K, R)
+        Vq = torch.empty(E * nv, dtype=torch.int32, device=device)
+        Vsz = torch.empty(E * nvs, dtype=torch.int32, device=device)
+        Uq = torch.empty(E * nu, dtype=torch.int32, device=device)
+        Usz = torch.empty(E * nus, dtype=torch.int32, device=device)
+        for e in range(E):
+            r = ranks[e]
+            out = (Vq[e * nv:(e + 1) * nv], Vsz[e * nvs:(e + 1) * nvs],
+                   Uq[e * nu:(e + 1) * nu], Usz[e * nus:(e + 1) * nus])
+            v = u = None
+            if r:
+                Vt = As[e].to(device=device, dtype=torch.float32).t().contiguous()   # [r][K]
+                Ut = Bs[e].to(device=device, dtype=torch.float32).t().contiguous()   # [N][r]
+                v = quantize_rtn_int3(Vt, 64)
+                uc, us, uz = quantize_rtn_int3(Ut, r)
+                u = (uc, us.reshape(N).contiguous(), uz.reshape(N).contiguous())
+            pack_lr_int3(v, u, N, K, r, R, out)
+        return (Vq, Vsz, Uq, Usz)
 
     def weights_struct(self):
         w = L.MiloWeights()
         w.packed = self.packed.data_ptr()
         w.sz = self.sz.data_ptr()
-        w.U = self.U.data_ptr()
-        w.V = self.V.data_ptr()
         w.rank = self.rank.data_ptr()
+        if self.lr_format == "int3":
+            w.lr_format = L.LR_INT3
+            if self.lrq is not None:
+                w.Vq, w.Vsz, w.Uq, w.Usz = (t.data_ptr() for t in self.lrq)
+        else:
+            w.lr_format = L.LR_FP16
+            w.U = self.U.data_ptr()
+            w.V = self.V.data_ptr()
         return w
 
     def nbytes(self):
-        return {"packed": self.packed.numel() * 4, "sz": self.sz.numel() * 4,
-                "U": self.U.numel() * 2, "V": self.V.numel() * 2}
+        out = {"packed": self.packed.numel() * 4, "sz": self.sz.numel() * 4}
+        if self.lr_format == "int3":
+            for n, t in zip(("Vq", "Vsz", "Uq", "Usz"), self.lrq or ()):
+                out[n] = t.numel() * 4
+        else:
+            out.update({"U": self.U.numel() * 2, "V": self.V.numel() * 2})
+        return out
 
 
 _gemm_ws = {}

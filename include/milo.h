@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define MILO_ABI_VERSION 1
+#define MILO_ABI_VERSION 2
 #define MILO_LAYOUT_VERSION 1
 
 typedef enum milo_status {
@@ -80,6 +80,18 @@ int32_t milo_quantize_rtn_int3(const float* W, int64_t rows, int64_t K,
                                uint8_t* codes, uint16_t* scale, uint16_t* zero,
                                void* stream);
 
+/*
+ * The same quantizer with groups of `group` consecutive columns (1 <= group
+ * <= 64, K % group == 0); scale and zero are [rows][K/group].  With
+ * group == 64 it is milo_quantize_rtn_int3.  Used for the int3 compensator
+ * factors (see milo_pack_lr_int3): V rows in groups of 64, U rows in one
+ * group of the expert's rank.
+ */
+int32_t milo_quantize_rtn_int3_grouped(const float* W, int64_t rows, int64_t K,
+                                       int32_t group, uint8_t* codes,
+                                       uint16_t* scale, uint16_t* zero,
+                                       void* stream);
+
 /* Number of uint32 words of the packed codes of a rows x K matrix: 3*rows*K/32. */
 int64_t milo_packed_words(int64_t rows, int64_t K);
 /* Number of uint32 words of the tiled scale/zero of a rows x K matrix: rows*K/64. */
@@ -113,6 +125,56 @@ int64_t milo_sz_words(int64_t rows, int64_t K);
 int32_t milo_pack_int3(const uint8_t* codes, const uint16_t* scale,
                        const uint16_t* zero, int64_t rows, int64_t K,
                        uint32_t* packed, uint32_t* sz, void* stream);
+
+/*
+ * int3 compensator factors of one expert.
+ * [talk] MiLo Algorithm, last step, and Experimental Setup & Results,
+ * "Compensator Quantization": the low-rank factors U (out x R) and V (R x in)
+ * are themselves quantized to int3 by simple asymmetric linear quantization.
+ * Quantizer: milo_quantize_rtn_int3_grouped, with the groups along the
+ * dimension each factor is summed over: V rows (one per rank j) in groups of
+ * 64 along K; U rows (one per output n) in one group of the expert's r ranks.
+ * Triplets keep the layout v1 bit assignment (32 codes in 3 words; code
+ * c = 2 pi + h at bits [16 h + 1 + 3 (pi mod 5), +3) of word pi div 5 for
+ * pi < 15, bit b of codes 30 + h at bit 16 h of word b).
+ *
+ * V layout: max_rank rows (rank rows j), each its K/32 triplets in order
+ *   tau = 4 kb + kq (kb = column block of 128, kq = 0..3); triplet tau of
+ *   row j is at vq[3 (j K/32 + tau) ...], its code c at column
+ *   128 kb + 32 (c div 8) + 8 kq + (c mod 8).  Scale/zero:
+ *   vsz[j (K/64) + gg] = scale | zero << 16 for row j, group gg.  Rows
+ *   j >= rank: codes 0, scale 1, zero 0.  milo_lr_v_words /
+ *   milo_lr_v_sz_words words per expert.
+ * U layout: ranks padded to R32 = max_rank rounded up to 32.  Tile (nt, jt) =
+ *   rows [64 nt, +64) x ranks [32 jt, +32), index t = nt (R32/32) + jt, 192
+ *   words.  Word 64 p + L is word p of the triplet whose code c is U[n][j],
+ *   n = 64 nt + 16 (c div 8) + (L mod 16), j = 32 jt + 8 (L div 16) + (c mod 8)
+ *   (one lane's triplet is exactly its matrix-core B operand of 4 x 8 values).
+ *   Ranks j >= rank: code 0.  Scale/zero, one per row:
+ *   usz[64 (n div 64) + 4 (n mod 16) + (n mod 64) div 16].
+ *   milo_lr_u_words / milo_lr_u_sz_words (= N) words per expert.
+ */
+int64_t milo_lr_v_words(int32_t max_rank, int64_t K);
+int64_t milo_lr_v_sz_words(int32_t max_rank, int64_t K);
+int64_t milo_lr_u_words(int64_t N, int32_t max_rank);
+int64_t milo_lr_u_sz_words(int64_t N);
+
+/*
+ * Pack one expert's quantized compensator factors into the layouts above.
+ * v_codes : uint8 [rank][K];  v_scale, v_zero : fp16 bits [rank][K/64].
+ * u_codes : uint8 [N][rank];  u_scale, u_zero : fp16 bits [N] (one group).
+ * vq, vsz, uq, usz : out, milo_lr_*_words(...) uint32 each, 16-byte aligned.
+ * Every output word is written (padding included).  The v_* / u_* inputs
+ * may be NULL when rank == 0.
+ * Constraints: N % 64 == 0, K % 128 == 0, 0 <= rank <= max_rank <= 64, both
+ * multiples of 8, max_rank >= 8.
+ */
+int32_t milo_pack_lr_int3(const uint8_t* v_codes, const uint16_t* v_scale,
+                          const uint16_t* v_zero, const uint8_t* u_codes,
+                          const uint16_t* u_scale, const uint16_t* u_zero,
+                          int64_t N, int64_t K, int32_t rank, int32_t max_rank,
+                          uint32_t* vq, uint32_t* vsz, uint32_t* uq,
+                          uint32_t* usz, void* stream);
 
 /* ======================================================================
  * Routing
@@ -163,14 +225,26 @@ int32_t milo_route_sort(const float* logits, int32_t T, int32_t E, int32_t k,
  *   rank   : DEVICE int32 [num_experts], 0 <= rank[e] <= max_rank,
  *            rank[e] % 8 == 0.  Columns of U and rows of V at or beyond
  *            rank[e] are never read.
- * U and V may be NULL when max_rank == 0.
+ *   lr_format : MILO_LR_FP16 (U, V above) or MILO_LR_INT3 (Uq, Usz, Vq, Vsz:
+ *            the int3 compensator layouts of milo_pack_lr_int3, expert e at
+ *            e times the per-expert word counts; U and V are then unused).
+ *            Ranks at or beyond rank[e] contribute nothing whatever the
+ *            padding holds.
+ * The compensator pointers may be NULL when max_rank == 0.
  */
+enum { MILO_LR_FP16 = 0, MILO_LR_INT3 = 1 };
+
 typedef struct milo_weights {
   const uint32_t* packed;
   const uint32_t* sz;
   const uint16_t* U;
   const uint16_t* V;
   const int32_t* rank;
+  int32_t lr_format;
+  const uint32_t* Uq;
+  const uint32_t* Usz;
+  const uint32_t* Vq;
+  const uint32_t* Vsz;
 } milo_weights;
 
 enum {
@@ -220,6 +294,8 @@ size_t milo_moe_gemm_workspace_bytes(const milo_gemm_desc* desc);
  * The fused routed grouped GEMM.  For every pair i of expert e (rows of x
  * gathered through sorted_pairs when gather_div > 0), and each weight family w:
  *     Y_w[i] = x_i . deq(W_w,e)^T + (x_i . V_w,e^T) . U_w,e^T
+ * (with int3 factors, V and U are their dequantized values (q - z) s, each
+ * rounded once to fp16 inside the kernels)
  * [talk] MiLo Algorithm (W_out = W_quant + U V) and MiLo Kernel (int3 x fp16
  * GEMM with dequantization fused into the kernel), with deq(q) = (q - z) * s
  * per 64-column group, fp16 activations and fp32 accumulation.  Then the
@@ -233,8 +309,8 @@ size_t milo_moe_gemm_workspace_bytes(const milo_gemm_desc* desc);
  *   aligned, scratch only (no initialisation needed, contents undefined after
  *   the call).  Two calls that overlap in time must not share a workspace.
  * Constraints: N % 64 == 0, K % 128 == 0, N, K <= 65536, 1 <= num_experts
- *   <= 256, num_pairs <= 1048576, x/y/U/V 16-byte aligned; for SWIGLU both
- *   families have the same N, K, max_rank.
+ *   <= 256, num_pairs <= 1048576, x/y/U/V/Uq/Usz/Vq/Vsz 16-byte aligned;
+ *   for SWIGLU both families have the same N, K, max_rank and lr_format.
  */
 int32_t milo_moe_w3a16_lowrank_gemm(const milo_gemm_desc* desc,
                                     void* workspace, size_t ws_bytes,

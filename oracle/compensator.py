@@ -22,15 +22,13 @@ assignment of layout v1 (oracle/layout.py): code c = 2 pi + h, pair pi < 15 at
 bits [16 h + 1 + 3 (pi mod 5), +3) of word pi div 5; pair 15: bit b of code
 30 + h is bit 16 h of word b.
 
-V layout.  Rank rows padded to R16 = max_rank rounded up to 16.  Tile
-(jt, kb) covers rank rows [16 jt, 16 jt + 16) and k in [128 kb, 128 kb + 128),
-tile index t = jt (K / 128) + kb, 192 words at [192 t, 192 t + 192).  Word
-64 p + L (plane p = 0..2, lane L = 0..63) is word p of the triplet of rank row
-16 jt + (L mod 16) whose code c sits at k = 128 kb + 32 (c div 8) +
-8 (L div 16) + (c mod 8).  Scale/zero of row j, group gg = k div 64: word
-32 t + 2 (j mod 16) + (gg mod 2) with t = (j div 16)(K / 128) + gg div 2,
-scale bits low, zero bits high.  Rows j >= rank hold code 0 and the word
-0x00003C00 (scale 1, zero 0).
+V layout.  max_rank rows (rank rows j; rows j >= rank are padding), each
+the K / 32 triplets of that row in order tau = 4 kb + kq (kb = 0..K/128-1,
+kq = 0..3).  Triplet tau of row j is at words [3 (j K/32 + tau), +3) (word p
+of the triplet at offset p); its code c sits at k = 128 kb + 32 (c div 8) +
+8 kq + (c mod 8).  Scale/zero of row j, group gg = k div 64: word
+j (K / 64) + gg, scale bits low, zero bits high.  Rows j >= rank hold code 0
+and the word 0x00003C00 (scale 1, zero 0).
 
 U layout.  Ranks padded to R32 = max_rank rounded up to 32.  Tile (nt, jt)
 covers rows n in [64 nt, 64 nt + 64) and ranks [32 jt, 32 jt + 32), tile index
@@ -132,65 +130,48 @@ def _round_up(v, a):
 # V layout
 
 def lr_v_words(max_rank: int, K: int) -> int:
-    return 3 * _round_up(max_rank, 16) * K // 32
+    return 3 * max_rank * K // 32
 
 
 def lr_v_sz_words(max_rank: int, K: int) -> int:
-    return _round_up(max_rank, 16) * K // 64
+    return max_rank * K // 64
 
 
-def _v_index(R16, K):
-    """(row, col) of code c of lane L in tile (jt, kb): arrays [JT, KB, 64, 32]."""
-    JT, KB = R16 // 16, K // 128
-    jt = np.arange(JT)[:, None, None, None]
-    kb = np.arange(KB)[None, :, None, None]
-    L = np.arange(64)[None, None, :, None]
-    c = np.arange(32)[None, None, None, :]
-    row = 16 * jt + (L % 16)
-    col = 128 * kb + 32 * (c // 8) + 8 * (L // 16) + (c % 8)
-    return np.broadcast_arrays(row, col)
-
-
-def _v_sz_index(R16, K):
-    j = np.arange(R16)[:, None]
-    gg = np.arange(K // 64)[None, :]
-    t = (j // 16) * (K // 128) + gg // 2
-    return 32 * t + 2 * (j % 16) + (gg % 2)
+def _v_index(R, K):
+    """(row, col) of code c of triplet (j, tau): arrays [R, K/32, 32]."""
+    j = np.arange(R)[:, None, None]
+    tau = np.arange(K // 32)[None, :, None]
+    c = np.arange(32)[None, None, :]
+    kb, kq = tau // 4, tau % 4
+    col = 128 * kb + 32 * (c // 8) + 8 * kq + (c % 8)
+    return np.broadcast_arrays(j, col)
 
 
 def pack_lr_v(codes, scale, zero, max_rank):
     """codes uint8 [rank][K], scale/zero fp16 [rank][K/64] -> (words, sz) of
-    the V layout for ranks padded to max_rank rounded up to 16."""
+    the V layout for max_rank rows."""
     codes = np.asarray(codes)
     rank, K = codes.shape
     if K % 128 or rank > max_rank or rank % 8 or max_rank % 8:
         raise ValueError("V layout needs K % 128 == 0 and rank <= max_rank, both multiples of 8")
-    R16 = _round_up(max_rank, 16)
-    full = np.zeros((R16, K), np.uint8)
+    full = np.zeros((max_rank, K), np.uint8)
     full[:rank] = codes
-    row, col = _v_index(R16, K)
-    q = full[row, col]                              # [JT, KB, 64, 32]
-    w = _encode(q)                                  # [JT, KB, 64, 3]
-    words = np.ascontiguousarray(np.moveaxis(w, 3, 2)).reshape(-1)   # [JT, KB, 3, 64]
-    szw = np.full((R16, K // 64), PAD_SZ_WORD, dtype=np.uint32)
+    row, col = _v_index(max_rank, K)
+    words = _encode(full[row, col]).reshape(-1)     # [R, K/32, 3] in that order
+    sz = np.full((max_rank, K // 64), PAD_SZ_WORD, dtype=np.uint32)
     if rank:
-        szw[:rank] = _sz_word(scale, zero)
-    sz = np.zeros(R16 * K // 64, dtype=np.uint32)
-    sz[_v_sz_index(R16, K)] = szw
-    return words, sz
+        sz[:rank] = _sz_word(scale, zero)
+    return words, sz.reshape(-1)
 
 
 def unpack_lr_v(words, sz, max_rank, K):
-    """Inverse of pack_lr_v over all R16 rows: (codes [R16][K], scale, zero
-    fp16 [R16][K/64])."""
-    R16 = _round_up(max_rank, 16)
-    JT, KB = R16 // 16, K // 128
-    w = np.moveaxis(np.asarray(words, np.uint32).reshape(JT, KB, 3, 64), 2, 3)
-    q = _decode(w)
-    out = np.zeros((R16, K), np.uint8)
-    row, col = _v_index(R16, K)
-    out[row, col] = q
-    szw = np.asarray(sz, np.uint32)[_v_sz_index(R16, K)]
+    """Inverse of pack_lr_v over all max_rank rows: (codes [R][K], scale,
+    zero fp16 [R][K/64])."""
+    w = np.asarray(words, np.uint32).reshape(max_rank, K // 32, 3)
+    out = np.zeros((max_rank, K), np.uint8)
+    row, col = _v_index(max_rank, K)
+    out[row, col] = _decode(w)
+    szw = np.asarray(sz, np.uint32).reshape(max_rank, K // 64)
     s = (szw & np.uint32(0xFFFF)).astype(np.uint16).view(np.float16)
     z = (szw >> np.uint32(16)).astype(np.uint16).view(np.float16)
     return out, s, z
@@ -264,31 +245,29 @@ def unpack_lr_u(words, sz, N, max_rank):
 # ----------------------------------------------------------------------------
 # one code at a time, from the spec read backwards (tiny shapes only)
 
-def _put(words, base, c, v):
+def _put(words, base, c, v, plane_stride):
     pi, h = divmod(c, 2)
     if pi < 15:
         p, o = divmod(pi, 5)
-        words[base + 64 * p] |= v << (16 * h + 1 + 3 * o)
+        words[base + plane_stride * p] |= v << (16 * h + 1 + 3 * o)
     else:
         for b in range(3):
-            words[base + 64 * b] |= ((v >> b) & 1) << (16 * h)
+            words[base + plane_stride * b] |= ((v >> b) & 1) << (16 * h)
 
 
 def pack_lr_v_scalar(codes, max_rank):
-    """Codes only: walks every (j, k), finds its tile, lane and code slot."""
+    """Codes only: walks every (j, k), finds its triplet and code slot."""
     rank = len(codes)
     K = len(codes[0]) if rank else 0
     words = [0] * lr_v_words(max_rank, K)
     for j in range(rank):
         for k in range(K):
-            jt, j16 = divmod(j, 16)
             kb, kk = divmod(k, 128)
             step, rem = divmod(kk, 32)
             kq, t8 = divmod(rem, 8)
-            L = 16 * kq + j16
+            tau = 4 * kb + kq
             c = 8 * step + t8
-            tile = jt * (K // 128) + kb
-            _put(words, 192 * tile + L, c, int(codes[j][k]))
+            _put(words, 3 * (j * (K // 32) + tau), c, int(codes[j][k]), 1)
     return words
 
 
@@ -306,5 +285,5 @@ def pack_lr_u_scalar(codes, max_rank):
             L = 16 * kq + n16
             c = 8 * i + t8
             tile = nt * (R32 // 32) + jt
-            _put(words, 192 * tile + L, c, int(codes[n][j]))
+            _put(words, 192 * tile + L, c, int(codes[n][j]), 64)
     return words

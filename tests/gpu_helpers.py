@@ -28,10 +28,12 @@ def assert_close(got, ref, what, rel=REL_FRO_TOL, mabs=MAX_ABS_TOL):
 
 
 def make_family(rng_seed, E, N, K, ranks, w_sigma=0.02, lr_sigma=0.01, device="cuda",
-                zero_w=False, zero_lr=False):
+                zero_w=False, zero_lr=False, lr_format="fp16"):
     """Random fp32 weights + fp16 compensators for E experts (CPU torch
     generator), the library Family built from them on the GPU, and the
-    oracle's own quantization of the same weights."""
+    oracle's own quantization of the same weights.  With lr_format "int3" the
+    library quantizes the factors too, and the reference factors are the
+    oracle's dequantized int3 factors."""
     from extreme_quantized_moe_amd import Family
     g = torch.Generator().manual_seed(rng_seed)
     Ws, As, Bs, q = [], [], [], []
@@ -50,5 +52,9 @@ def make_family(rng_seed, E, N, K, ranks, w_sigma=0.02, lr_sigma=0.01, device="c
         Bs.append(B)
         q.append(oracle.quantize_rtn_int3(W.numpy()))
     fam = Family.from_dense([w.to(device) for w in Ws], As, Bs,
-                            max_rank=max(max(ranks), 0))
-    return fam, {"W": Ws, "A": [a.numpy() for a in As], "B": [b.numpy() for b in Bs], "q": q}
+                            max_rank=max(max(ranks), 0), lr_format=lr_format)
+    A_ref, B_ref = [a.numpy() for a in As], [b.numpy() for b in Bs]
+    if lr_format == "int3":
+        deq = [oracle.dequant_compensator(oracle.quantize_compensator(a, b)) for a, b in zip(A_ref, B_ref)]
+        A_ref, B_ref = [d[0] for d in deq], [d[1] for d in deq]
+    return fam, {"W": Ws, "A": A_ref, "B": B_ref, "q": q}

@@ -33,7 +33,7 @@ def test_exports_every_declared_function(L):
 
 def test_versions_and_strings(L):
     lib = L.lib()
-    assert lib.milo_abi_version() == 1
+    assert lib.milo_abi_version() == 2
     assert lib.milo_layout_version() == 1
     for s in range(8):
         assert len(lib.milo_status_string(s)) > 0
@@ -56,6 +56,41 @@ def test_quantize_rejects(L):
     fake = C.c_void_p(0x1000)
     assert lib.milo_quantize_rtn_int3(fake, 4, 100, fake, fake, fake, None) == 2
     assert lib.milo_quantize_rtn_int3(None, 4, 128, fake, fake, fake, None) == 1
+
+
+def test_quantize_grouped_rejects(L):
+    lib = L.lib()
+    fake = C.c_void_p(0x1000)
+    assert lib.milo_quantize_rtn_int3_grouped(fake, 4, 128, 0, fake, fake, fake, None) == 2
+    assert lib.milo_quantize_rtn_int3_grouped(fake, 4, 128, 65, fake, fake, fake, None) == 2
+    assert lib.milo_quantize_rtn_int3_grouped(fake, 4, 40, 16, fake, fake, fake, None) == 2
+    assert lib.milo_quantize_rtn_int3_grouped(None, 4, 48, 16, fake, fake, fake, None) == 1
+
+
+@pytest.mark.parametrize("N,K,max_rank", [(64, 128, 8), (64, 128, 16), (128, 256, 24), (14336, 4096, 64),
+                                          (4096, 14336, 40)])
+def test_lr_word_counts_match_the_spec(L, N, K, max_rank):
+    import oracle
+    lib = L.lib()
+    assert lib.milo_lr_v_words(max_rank, K) == oracle.lr_v_words(max_rank, K)
+    assert lib.milo_lr_v_sz_words(max_rank, K) == oracle.lr_v_sz_words(max_rank, K)
+    assert lib.milo_lr_u_words(N, max_rank) == oracle.lr_u_words(N, max_rank)
+    assert lib.milo_lr_u_sz_words(N) == oracle.lr_u_sz_words(N)
+
+
+def test_pack_lr_rejects(L):
+    lib = L.lib()
+    f = C.c_void_p(0x1000)
+    call = lambda N, K, r, R, vq=f, first=f: lib.milo_pack_lr_int3(first, f, f, f, f, f, N, K, r, R, vq, f, f, f, None)
+    assert call(64, 128, 8, 16, vq=None) == 1
+    assert call(64, 128, 8, 16, first=None) == 1
+    assert call(96, 128, 8, 16) == 2
+    assert call(64, 192, 8, 16) == 2
+    assert call(64, 128, 12, 16) == 4
+    assert call(64, 128, 24, 16) == 4
+    assert call(64, 128, 8, 72) == 4
+    assert call(64, 128, 0, 0) == 4
+    assert call(64, 128, 8, 16, vq=C.c_void_p(0x1004)) == 3
 
 
 def test_route_rejects(L):
@@ -103,6 +138,22 @@ def test_gemm_rejects(L, field, value, code):
         d.slot_w = None
     assert lib.milo_moe_w3a16_lowrank_gemm(C.byref(d), None, 0, None) == code
     assert len(lib.milo_last_error()) > 0
+
+
+def test_gemm_rejects_compensator_formats(L):
+    lib = L.lib()
+    d = _desc(L)
+    d.w[0].lr_format = 2
+    assert lib.milo_moe_w3a16_lowrank_gemm(C.byref(d), None, 0, None) == 6
+    d = _desc(L)
+    d.w[0].lr_format = L.LR_INT3              # int3 factors missing
+    assert lib.milo_moe_w3a16_lowrank_gemm(C.byref(d), None, 0, None) == 1
+    d.w[0].Uq = d.w[0].Usz = d.w[0].Vq = 0x10000
+    d.w[0].Vsz = 0x10004
+    assert lib.milo_moe_w3a16_lowrank_gemm(C.byref(d), None, 0, None) == 3
+    d = _desc(L, n_w=2, epilogue=L.EPI_SWIGLU)
+    d.w[1].lr_format = L.LR_INT3              # families disagree
+    assert lib.milo_moe_w3a16_lowrank_gemm(C.byref(d), None, 0, None) == 6
 
 
 def test_gemm_workspace_query_and_shortfall(L):

@@ -24,12 +24,12 @@ from tests.gpu_helpers import assert_close
 pytestmark = pytest.mark.gpu
 
 
-def _run_layer(cfg, layer):
+def _run_layer(cfg, layer, lr_format="fp16"):
     import bench
     import extreme_quantized_moe_amd as m
     X = synth.gen_tokens(cfg, 0, device="cuda")
     logits = synth.gen_logits(cfg, layer, device="cuda")
-    lay = bench.Layer(m, cfg, layer, X, logits, 0)
+    lay = bench.Layer(m, cfg, layer, X, logits, 0, lr_format=lr_format)
     lay.ws = torch.zeros(lay.ws_need, dtype=torch.uint8, device="cuda")
     lay.step(torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
@@ -44,12 +44,19 @@ def _quantize_rows(W, rows):
     return oracle.quantize_rtn_int3(W[rows].astype(np.float32))
 
 
-def _expert_host(cfg, layer, e, rank, which):
+def _expert_host(cfg, layer, e, rank, which, lr_format="fp16"):
+    """One expert's tensors on the host; with int3 factors the compensators
+    are replaced by the oracle's dequantized int3 factors."""
     d = synth.gen_expert(cfg, layer, e, rank, device="cuda", which=which)
-    return {k: v.cpu().numpy() for k, v in d.items()}
+    d = {k: v.cpu().numpy() for k, v in d.items()}
+    if lr_format == "int3":
+        for a, b in (("A1", "B1"), ("A3", "B3"), ("A2", "B2")):
+            if a in d:
+                d[a], d[b] = oracle.dequant_compensator(oracle.quantize_compensator(d[a], d[b]))
+    return d
 
 
-def _check_g(cfg, layer, lay, ncols, seed):
+def _check_g(cfg, layer, lay, ncols, seed, lr_format="fp16"):
     """G[pair][n] = silu(h1) * h3 for every pair and sampled columns n."""
     cols = _cols(cfg.F, ncols, seed)
     route = oracle.route_ref(lay.logits.cpu().numpy(), cfg.k, cfg.S, cfg.renormalize)
@@ -60,24 +67,24 @@ def _check_g(cfg, layer, lay, ncols, seed):
     for e in range(cfg.E + cfg.S):
         if off[e + 1] == off[e]:
             continue
-        d = _expert_host(cfg, layer, e, lay.ranks[e], ("W1", "W3"))
+        d = _expert_host(cfg, layer, e, lay.ranks[e], ("W1", "W3"), lr_format)
         rows = X[sp[off[e]:off[e + 1]] // cfg.slots]
         h = []
         for n, a, b in (("W1", "A1", "B1"), ("W3", "A3", "B3")):
             q, s, z = _quantize_rows(d[n], cols)
             h.append(oracle.linear_ref(rows, q, s, z, d[a], d[b][:, cols]))
         want[off[e]:off[e + 1]] = oracle.silu(h[0]) * h[1]
-    assert_close(got, want, f"{cfg.name} G (all pairs, {ncols} columns)")
+    assert_close(got, want, f"{cfg.name} G (all pairs, {ncols} columns, {lr_format} factors)")
 
 
-def _check_out(cfg, layer, lay, toks, ncols, seed):
+def _check_out(cfg, layer, lay, toks, ncols, seed, lr_format="fp16"):
     """out[t][c] for sampled tokens t and output columns c."""
     cols = _cols(cfg.H, ncols, seed) if ncols < cfg.H else np.arange(cfg.H)
     X = lay.X.cpu().numpy()[toks].astype(np.float64)
     logits = lay.logits.cpu().numpy()[toks]
 
     def get_expert(e):
-        d = _expert_host(cfg, layer, e, lay.ranks[e], ("W1", "W3", "W2"))
+        d = _expert_host(cfg, layer, e, lay.ranks[e], ("W1", "W3", "W2"), lr_format)
         qe = {n: oracle.quantize_rtn_int3(d[n]) for n in ("W1", "W3")}
         qe["W2"] = _quantize_rows(d["W2"], cols)
         qe.update({n: d[n] for n in ("A1", "B1", "A3", "B3", "A2")})
@@ -88,7 +95,7 @@ def _check_out(cfg, layer, lay, toks, ncols, seed):
     ref = oracle.moe_layer_ref(X, logits, get_expert, cfg.k, cfg.S, cfg.renormalize,
                                out_cols=np.arange(len(cols)))
     got = lay.out.cpu().numpy().astype(np.float64)[toks][:, cols]
-    assert_close(got, ref["out"], f"{cfg.name} out (tokens {list(toks)}, {len(cols)} columns)")
+    assert_close(got, ref["out"], f"{cfg.name} out (tokens {list(toks)}, {len(cols)} columns, {lr_format} factors)")
 
 
 def test_c2_full_decode_layer():
@@ -122,3 +129,19 @@ def test_c5_layer_at_batch(T):
     lay = _run_layer(cfg, 7)
     _check_g(cfg, 7, lay, 32, seed=7)
     _check_out(cfg, 7, lay, [0] if T == 1 else [5, 17, 40, T - 1], 256, seed=8)
+
+
+def test_c2_full_decode_layer_int3_factors():
+    """C2 with the compensators stored as int3 (V rows in groups of 64 along
+    K, U rows in one group of r), quantized and packed on the GPU."""
+    cfg = SC.get_config("C2")
+    lay = _run_layer(cfg, 0, "int3")
+    _check_g(cfg, 0, lay, 96, seed=11, lr_format="int3")
+    _check_out(cfg, 0, lay, np.arange(cfg.T), 512, seed=12, lr_format="int3")
+
+
+def test_c4_full_layer_int3_factors():
+    cfg = SC.get_config("C4")
+    lay = _run_layer(cfg, 0, "int3")
+    _check_g(cfg, 0, lay, 64, seed=13, lr_format="int3")
+    _check_out(cfg, 0, lay, np.arange(cfg.T), cfg.H, seed=14, lr_format="int3")

@@ -47,7 +47,8 @@ def _route(T, E, k, S, seed, skew=None):
     return logits
 
 
-def _moe_case(E, S, N, K, ranks, T, k, epilogue, path, seed, skew=None, zero_w=False, zero_lr=False):
+def _moe_case(E, S, N, K, ranks, T, k, epilogue, path, seed, skew=None, zero_w=False, zero_lr=False,
+              lr_format="fp16"):
     m = _m()
     ET = E + S
     logits = _route(T, E, k, S, seed, skew)
@@ -66,7 +67,8 @@ def _moe_case(E, S, N, K, ranks, T, k, epilogue, path, seed, skew=None, zero_w=F
     nfam = 2 if epilogue == m.EPI_SWIGLU else 1
     fams, refs = [], []
     for f in range(nfam):
-        fam, ref = make_family(seed * 10 + f, ET, N, K, ranks, zero_w=zero_w, zero_lr=zero_lr)
+        fam, ref = make_family(seed * 10 + f, ET, N, K, ranks, zero_w=zero_w, zero_lr=zero_lr,
+                               lr_format=lr_format)
         fams.append(fam)
         refs.append(ref)
     if epilogue == m.EPI_ROUTE_SCALE:

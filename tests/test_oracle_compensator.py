@@ -171,7 +171,7 @@ def test_v_round_trip_and_scalar(rank, max_rank, K):
     s = (rng.uniform(0.001, 0.01, (rank, K // 64))).astype(np.float16)
     z = (rng.uniform(0, 7, (rank, K // 64))).astype(np.float16)
     words, sz = OC.pack_lr_v(codes, s, z, max_rank)
-    assert words.size == OC.lr_v_words(max_rank, K) and words.size * 32 == 3 * (-(-max_rank // 16) * 16) * K
+    assert words.size == OC.lr_v_words(max_rank, K) and words.size * 32 == 3 * max_rank * K
     assert sz.size == OC.lr_v_sz_words(max_rank, K)
     scal = np.array(OC.pack_lr_v_scalar(codes.tolist(), max_rank), dtype=np.uint32)
     np.testing.assert_array_equal(words, scal)
