@@ -31,9 +31,11 @@ __global__ void __launch_bounds__(256) gemm_prefill_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
   const CodeConsts kc = make_code_consts();
-  int e, m0, M;
-  if (!find_row_tile(a.offsets, a.num_experts, a.pre_min_rows, kBM, blockIdx.x, &e, &m0, &M)) return;
-  const int base = a.offsets[e];
+  RowTile rt;
+  if (!find_row_tile(a.offsets, a.num_experts, a.pre_min_rows, kBM, blockIdx.x, a.rp ? a.rank[0] : nullptr,
+                     a.rp ? a.rank[1] : nullptr, &rt))
+    return;
+  const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
   const int f = (NW == 2) ? (wave & 1) : 0;
   const int nt = (NW == 2) ? (2 * blockIdx.y + (wave >> 1)) : (4 * blockIdx.y + wave);
   const bool wave_on = nt < a.n_tiles;
@@ -132,7 +134,7 @@ __global__ void __launch_bounds__(256) gemm_prefill_kernel(GemmArgs a) {
   // triplet of each 32-rank U tile is its B operand for the four row groups)
   if (wave_on && a.rp > 0) {
     const int RW = a.n_w * a.rp;
-    const int rk = a.rank[f][e];
+    const int rk = rt.rank(f);
     u32x4 usz = {0u, 0u, 0u, 0u};
     if constexpr (LRQ) usz = *(const u32x4*)(a.Usz[f] + (size_t)e * a.N + nt * kTileRows + 4 * (lane & 15));
     for (int s2 = 0; s2 < a.rp / 32; ++s2) {

@@ -44,14 +44,15 @@ struct PrepassArgs {
   int dec_max_rows;   // experts with more rows are not gathered
 };
 
-__device__ __forceinline__ bool find_tile16(const int32_t* offsets, int num_experts, int tile,
-                                            int* e_out, int* m0_out, int* rows_out) {
-  return find_row_tile(offsets, num_experts, 0, 16, tile, e_out, m0_out, rows_out);
+// The block's 16-row tile (all experts with rows), with the expert's first
+// pair and its ranks in both families.
+__device__ __forceinline__ bool find_tile16(const PrepassArgs& a, RowTile* t) {
+  return find_row_tile(a.offsets, a.num_experts, 0, 16, blockIdx.x, a.rp ? a.rank[0] : nullptr,
+                       a.rp ? a.rank[1] : nullptr, t);
 }
 
 // Gathered rows (pair order) and pair weights of one 16-row tile.
-__device__ void prepass_aux(const PrepassArgs& a, int e, int m0, int M) {
-  const int base = a.offsets[e];
+__device__ void prepass_aux(const PrepassArgs& a, int base, int m0, int M) {
   const int rows = (M - m0) < 16 ? (M - m0) : 16;
   if (a.pw && threadIdx.x < rows) {
     const int i = base + m0 + threadIdx.x;
@@ -94,19 +95,19 @@ constexpr int kDotBatch = 8;
 
 __global__ void __launch_bounds__(kDotThreads) prepass_dot_kernel(PrepassArgs a) {
   __shared__ float part[kDotThreads / 64];
-  int e, m0, M;
-  if (!find_tile16(a.offsets, a.num_experts, blockIdx.x, &e, &m0, &M)) return;
+  RowTile rt;
+  if (!find_tile16(a, &rt)) return;
+  const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
   if ((int)blockIdx.y == a.aux_y) {
-    prepass_aux(a, e, m0, M);
+    prepass_aux(a, base, m0, M);
     return;
   }
-  const int base = a.offsets[e];
   const int RW = a.n_w * a.rp;
   const int f = blockIdx.y / a.rp, j = blockIdx.y - f * a.rp;
   const int rows = (M - m0) < 16 ? (M - m0) : 16;
   const int tid = threadIdx.x;
   uint16_t* tout = a.T + (size_t)(base + m0) * RW + f * a.rp + j;
-  if (j >= a.rank[f][e]) {                        // beyond the expert's rank: T = 0
+  if (j >= rt.rank(f)) {                          // beyond the expert's rank: T = 0
     if (tid < rows) tout[(size_t)tid * RW] = 0;
     return;
   }
@@ -195,19 +196,23 @@ struct DotBlock {
 
 template <int NJ>
 __device__ __forceinline__ bool dot_block(const PrepassArgs& a, DotBlock& b) {
-  if (!find_tile16(a.offsets, a.num_experts, blockIdx.x, &b.e, &b.m0, &b.M)) return false;
+  RowTile rt;
+  if (!find_tile16(a, &rt)) return false;
+  b.e = rt.e;
+  b.m0 = rt.m0;
+  b.M = rt.rows;
+  b.base = rt.base;
   if ((int)blockIdx.y == a.aux_y) {
-    prepass_aux(a, b.e, b.m0, b.M);
+    prepass_aux(a, b.base, b.m0, b.M);
     return false;
   }
-  b.base = a.offsets[b.e];
   b.RW = a.n_w * a.rp;
   const int y0 = blockIdx.y * NJ;
   b.f = y0 / a.rp;
   b.j0 = y0 - b.f * a.rp;
   b.rows = (b.M - b.m0) < 16 ? (b.M - b.m0) : 16;
   b.tout = a.T + (size_t)(b.base + b.m0) * b.RW + b.f * a.rp + b.j0;
-  b.rk = a.rank[b.f][b.e];
+  b.rk = rt.rank(b.f);
   const int tid = threadIdx.x;
   if (b.j0 >= b.rk) {                             // beyond the expert's rank: T = 0
     if (tid < b.rows * NJ) b.tout[(size_t)(tid / NJ) * b.RW + tid % NJ] = 0;
@@ -315,13 +320,13 @@ template <int NRT, int NWAVES, int UNR>
 __global__ void __launch_bounds__(64 * NWAVES) prepass_kernel(PrepassArgs a) {
   __shared__ float red[NWAVES][NRT][64][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int e, m0, M;
-  if (!find_tile16(a.offsets, a.num_experts, blockIdx.x, &e, &m0, &M)) return;
+  RowTile rt;
+  if (!find_tile16(a, &rt)) return;
+  const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
   if ((int)blockIdx.y == a.aux_y) {
-    prepass_aux(a, e, m0, M);
+    prepass_aux(a, base, m0, M);
     return;
   }
-  const int base = a.offsets[e];
   const int RW = a.n_w * a.rp;
   const int tiles_per_w = a.rp / 16;
   const int tr0 = blockIdx.y * NRT;            // first rank tile of this block
@@ -342,8 +347,8 @@ __global__ void __launch_bounds__(64 * NWAVES) prepass_kernel(PrepassArgs a) {
     const int tr = tr0 + t;
     const int f = tr / tiles_per_w;
     const int j = (tr % tiles_per_w) * 16 + (lane & 15);
-    vok[t] = j < a.rank[f][e];
-    any |= (tr % tiles_per_w) * 16 < a.rank[f][e];
+    vok[t] = j < rt.rank(f);
+    any |= (tr % tiles_per_w) * 16 < rt.rank(f);
     vp[t] = a.V[f] + ((size_t)e * a.max_rank + (vok[t] ? j : 0)) * a.K + 8 * (lane >> 4);
   }
 
@@ -403,13 +408,13 @@ __global__ void __launch_bounds__(64 * NWAVES) prepass_q_kernel(PrepassArgs a) {
   __shared__ float red[NWAVES][NRT][64][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const CodeConsts kc = make_code_consts();
-  int e, m0, M;
-  if (!find_tile16(a.offsets, a.num_experts, blockIdx.x, &e, &m0, &M)) return;
+  RowTile rt;
+  if (!find_tile16(a, &rt)) return;
+  const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
   if ((int)blockIdx.y == a.aux_y) {
-    prepass_aux(a, e, m0, M);
+    prepass_aux(a, base, m0, M);
     return;
   }
-  const int base = a.offsets[e];
   const int RW = a.n_w * a.rp;
   const int tiles_per_w = a.rp / 16;
   const int tr0 = blockIdx.y * NRT;
@@ -430,7 +435,7 @@ __global__ void __launch_bounds__(64 * NWAVES) prepass_q_kernel(PrepassArgs a) {
   for (int t = 0; t < NRT; ++t) {
     const int tr = tr0 + t;
     const int f = tr / tiles_per_w, jt = tr % tiles_per_w;
-    const int rk = a.rank[f][e];
+    const int rk = rt.rank(f);
     const int j = 16 * jt + (lane & 15);
     vok[t] = j < rk;                        // rank <= max_rank: the row is stored
     any |= 16 * jt < rk;

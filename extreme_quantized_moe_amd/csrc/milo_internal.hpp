@@ -105,29 +105,55 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t h, float s, float c) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Locate the (expert, first row, expert rows) of row tile `tile` when the
-// experts with more than `min_rows` rows are cut into tiles of `rows_per_tile`
-// rows, expert by expert.  Block-uniform result; returns false past the last
-// tile.  The first wave reads the expert offsets (all loads issued at once),
-// scans the per-expert tile counts with lane shuffles and the lane holding the
-// tile publishes it through LDS.  Every thread of the block must call it.
+// Row tile `tile` when the experts with more than `min_rows` rows are cut
+// into tiles of `rows_per_tile` rows, expert by expert: its expert, first row
+// within the expert, the expert's row count and first pair, and the expert's
+// compensator rank in the two weight families (0 where the rank array is
+// null).  Block-uniform result; returns false past the last tile.  The first
+// wave issues every load at once (offsets and ranks of up to 256 experts;
+// indexes are clamped instead of predicated, since a predicated load per
+// expert group is compiled to its own branch with a wait after it), scans
+// the per-expert tile counts with lane shuffles, and the lane holding the
+// tile publishes it through LDS, so callers need no further dependent load
+// for these values.  Every thread of the block must call it.
+struct RowTile {
+  int e, m0, rows, base, rank0, rank1;
+  // by selection, not indexing: a runtime index would put the struct in memory
+  __device__ __forceinline__ int rank(int f) const { return f ? rank1 : rank0; }
+};
+
 __device__ __forceinline__ bool find_row_tile(const int32_t* __restrict__ offsets, int num_experts,
                                               int min_rows, int rows_per_tile, int tile,
-                                              int* e_out, int* m0_out, int* rows_out) {
-  __shared__ int res[3];
+                                              const int32_t* __restrict__ rank0,
+                                              const int32_t* __restrict__ rank1, RowTile* out) {
+  __shared__ int res[6];
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    int m[4];
+    const int32_t* rk0 = rank0 ? rank0 : offsets;   // valid dummy, values unused
+    const int32_t* rk1 = rank1 ? rank1 : offsets;
+    int o0[4], m[4], r0[4], r1[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {          // up to 256 experts
       const int e = 64 * c + lane;
-      m[c] = e < num_experts ? offsets[e + 1] - offsets[e] : 0;
+      const int ec = e < num_experts ? e : num_experts - 1;
+      o0[c] = offsets[ec];
+      m[c] = offsets[ec + 1];
+      r0[c] = rk0[ec];
+      r1[c] = rk1[ec];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bool in = 64 * c + lane < num_experts;
+      m[c] = in ? m[c] : o0[c];            // no rows past the last expert
+      r0[c] = rank0 ? r0[c] : 0;
+      r1[c] = rank1 ? r1[c] : 0;
     }
     if (lane == 0) res[0] = -1;
     int before = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       if (64 * c >= num_experts) break;
+      m[c] -= o0[c];
       const int nt = m[c] > min_rows ? (m[c] + rows_per_tile - 1) / rows_per_tile : 0;
       int incl = nt;
 #pragma unroll
@@ -140,16 +166,21 @@ __device__ __forceinline__ bool find_row_tile(const int32_t* __restrict__ offset
         res[0] = 64 * c + lane;
         res[1] = (tile - first) * rows_per_tile;
         res[2] = m[c];
+        res[3] = o0[c];
+        res[4] = r0[c];
+        res[5] = r1[c];
       }
       before += __shfl(incl, 63);
     }
   }
   __syncthreads();
-  const int e = res[0];
-  *e_out = e;
-  *m0_out = res[1];
-  *rows_out = res[2];
-  return e >= 0;
+  out->e = res[0];
+  out->m0 = res[1];
+  out->rows = res[2];
+  out->base = res[3];
+  out->rank0 = res[4];
+  out->rank1 = res[5];
+  return out->e >= 0;
 }
 
 // ---------------------------------------------------------------- host side

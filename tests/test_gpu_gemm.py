@@ -227,3 +227,31 @@ def test_workspace_reused_across_different_plans():
         want = np.concatenate([oracle.linear_ref(x.numpy()[cut[e]:cut[e + 1]], *ref["q"][e],
                                                  ref["A"][e], ref["B"][e]) for e in range(3)])
         assert_close(to_np(y), want, f"reuse T={T} path={path}")
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_fp16_factors_beyond_rank_are_never_read(path):
+    """Columns of U and rows of V at or beyond an expert's rank are never
+    read (documented contract): poison them with NaN, the result must not
+    change."""
+    m = _m()
+    E, N, K, ranks = 3, 128, 256, [8, 24, 40]
+    fam, _ = make_family(88, E, N, K, ranks)
+    g = torch.Generator().manual_seed(89)
+    T = 20
+    x = torch.randn((T, K), generator=g).half().cuda()
+    offsets = torch.tensor([0, 7, 13, T], dtype=torch.int32, device="cuda")
+
+    def run():
+        y = torch.empty((T, N), dtype=torch.float16, device="cuda")
+        m.moe_w3a16_lowrank_gemm((fam,), x, offsets, T, m.EPI_NONE, y, max_rows_per_expert=T,
+                                 path=PATHS[path])
+        torch.cuda.synchronize()
+        return y.clone()
+
+    clean = run()
+    for e, r in enumerate(ranks):
+        fam.U[e, :, r:] = float("nan")
+        fam.V[e, r:, :] = float("nan")
+    dirty = run()
+    assert torch.equal(clean, dirty)
