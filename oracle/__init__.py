@@ -46,6 +46,12 @@ from .compensator import (  # noqa: F401
     lr_u_words,
     lr_u_sz_words,
 )
+from .builder import (  # noqa: F401
+    residual_ref,
+    exact_lowrank_ref,
+    rsvd_ref,
+    build_ref,
+)
 from .moe import (  # noqa: F401
     linear_ref,
     quantize_expert,
