@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--lr", default="fp16", choices=["fp16", "int3"],
                     help="storage of the compensator factors U, V")
+    ap.add_argument("--build", action="store_true",
+                    help="time the offline compensator construction (quantize <-> rank-64 SVD refinement) of "
+                         "one Mixtral-shaped 14336x4096 weight matrix instead of the MoE layer")
     ap.add_argument("--hbm-probe", action="store_true",
                     help="only measure plain device read (sum) and copy bandwidth on 4 GiB")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -302,6 +305,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_each_way": n, "copies": 5}))
         return
+    if args.build:
+        return bench_build(args, m)
     cfg = SC.get_config(args.config)
     if args.config == "C1":
         return bench_c1(args, m, cfg)
@@ -430,6 +435,74 @@ def traffic_for(config, T, lr="fp16"):
         return ent.get("bytes_per_launch")
     except Exception:
         return None
+
+
+def bench_build(args, m):
+    """Offline compensator construction of one Mixtral-shaped gate matrix:
+    iters rounds of (RTN int3 of W - L, residual, rank-r randomized SVD with q
+    power iterations).  Reported per matrix; the roofline line is the whole
+    call's algorithmic fp32 flops against the fp32 vector peak (its big
+    products are fp32 FMA on the vector units)."""
+    import torch
+    import synth
+    from synth import configs as SC
+    N, K, r, p, q, iters = 14336, 4096, 64, 16, 2, 2
+    l = r + p
+    cfg = SC.get_config("C2")
+    W = synth.gen_expert(cfg, 0, 0, r, device="cuda", which=("W1",))["W1"].contiguous()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2504)
+    omega = torch.randn((iters, l, K), generator=g, device="cuda")
+    steps = max(1, min(args.steps, 5))
+    warm = max(1, min(args.warmup, 2))
+    for _ in range(warm):
+        m.build_compensator(W, r, iters, omega, power_iters=q)
+    torch.cuda.synchronize()
+    global TIMER
+    TIMER = HipTimer()
+    a, b = TIMER.event(), TIMER.event()
+    stream = torch.cuda.current_stream().cuda_stream
+    TIMER.record(a, stream)
+    for _ in range(steps):
+        out = m.build_compensator(W, r, iters, omega, power_iters=q)
+    TIMER.record(b, stream)
+    torch.cuda.synchronize()
+    ms = TIMER.ms(a, b) / steps
+    per_iter = (2 * N * K * l * (2 + 2 * q) + 8 * l * l * (N * (q + 1) + K * q) + 2 * K * l * l
+                + 2 * N * l * r + 2 * l * r * K)
+    flops = iters * per_iter + (iters - 1) * 2 * N * K * r
+    tfl = flops / (ms * 1e-3) / 1e12
+    peak = 157.3
+    res = {
+        "metric": "offline compensator construction time per weight matrix", "value": round(ms, 3),
+        "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": round(ms, 3),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"compensator build: W {N}x{K} ~N(0,0.02), rank {r}, oversampling {p}, "
+                               f"{q} power iterations, {iters} quantize/compensate rounds",
+                   "alg_flops": int(flops)},
+        "roofline": {"bound": "alu", "achieved": round(tfl, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tfl / peak, 4), "traffic": None,
+                     "kernel": "whole milo_build_compensator call (single-block l x l factorizations take most of it, "
+                               "then the skinny fp32 products)"},
+    }
+    if not args.no_cpu:
+        import numpy as np
+        import oracle
+        from threadpoolctl import threadpool_info
+        Wh = W.cpu().numpy()
+        om = omega.cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.build_ref(Wh, r, iters, om, q)
+        cpu_s = time.perf_counter() - t0
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        res["cpu_baseline"] = {"value": round(cpu_s * 1000, 1), "unit": "ms", "cores": int(threads),
+                               "kind": "oracle", "sample": "oracle.build_ref on the same full matrix, "
+                               "test matrices and settings (float64 NumPy, Householder QR and SVD)"}
+    else:
+        res["cpu_baseline"] = None
+    del out
+    print(json.dumps(res))
 
 
 def bench_c1(args, m, cfg):

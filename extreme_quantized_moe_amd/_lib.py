@@ -69,6 +69,11 @@ def lib():
         "milo_lr_u_words": (i64, [i64, i32]),
         "milo_lr_u_sz_words": (i64, [i64]),
         "milo_pack_lr_int3": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
+        "milo_lowrank_svd_workspace_bytes": (sz, [i64, i64, i32, i32]),
+        "milo_lowrank_svd": (i32, [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "milo_build_compensator_workspace_bytes": (sz, [i64, i64, i32, i32]),
+        "milo_build_compensator": (i32, [vp, i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                          vp, sz, vp]),
         "milo_route_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "milo_route_sort": (i32, [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "milo_moe_gemm_workspace_bytes": (sz, [C.POINTER(MiloGemmDesc)]),

@@ -264,6 +264,69 @@ int32_t milo_pack_int3(const uint8_t* codes, const uint16_t* scale, const uint16
   return launch_pack(codes, scale, zero, rows, K, packed, sz, (hipStream_t)stream);
 }
 
+static int32_t check_lowrank_shape(int64_t N, int64_t K, int32_t rank, int32_t oversample) {
+  if (N < 1 || K < 1 || N > (1 << 20) || K > (1 << 20))
+    MILO_FAIL(MILO_ERR_SHAPE, "N=%lld K=%lld outside 1..1048576", (long long)N, (long long)K);
+  if (rank < 0 || rank > kMaxRank) MILO_FAIL(MILO_ERR_RANK, "rank=%d outside 0..64", rank);
+  if (oversample < 0 || rank + oversample > 80)
+    MILO_FAIL(MILO_ERR_RANK, "rank + oversample = %d outside rank..80", rank + oversample);
+  if (rank > 0 && (rank + oversample > N || rank + oversample > K))
+    MILO_FAIL(MILO_ERR_SHAPE, "rank + oversample = %d exceeds min(N, K)", rank + oversample);
+  return MILO_OK;
+}
+
+size_t milo_lowrank_svd_workspace_bytes(int64_t N, int64_t K, int32_t rank, int32_t oversample) {
+  if (check_lowrank_shape(N, K, rank, oversample) != MILO_OK || rank == 0) return 0;
+  return svd_workspace_bytes(N, K, rank + oversample);
+}
+
+int32_t milo_lowrank_svd(const float* R, int64_t N, int64_t K, int32_t rank, int32_t oversample,
+                         int32_t power_iters, const float* omega, float* U, float* V, float* sigma,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int32_t rc = check_lowrank_shape(N, K, rank, oversample);
+  if (rc != MILO_OK) return rc;
+  if (power_iters < 0 || power_iters > 8) MILO_FAIL(MILO_ERR_ARG, "power_iters=%d outside 0..8", power_iters);
+  if (rank == 0) return MILO_OK;
+  if (!R || !omega || !U || !V || !sigma) MILO_FAIL(MILO_ERR_NULL, "R, omega, U, V, sigma are required");
+  if (!aligned(R, 4) || !aligned(omega, 4) || !aligned(U, 4) || !aligned(V, 4) || !aligned(sigma, 4))
+    MILO_FAIL(MILO_ERR_ALIGN, "float arrays must be 4-byte aligned");
+  const size_t need = svd_workspace_bytes(N, K, rank + oversample);
+  if (!workspace || ws_bytes < need) MILO_FAIL(MILO_ERR_WORKSPACE, "svd workspace %zu bytes < required %zu", ws_bytes, need);
+  if (!aligned(workspace, 256)) MILO_FAIL(MILO_ERR_ALIGN, "workspace must be 256-byte aligned");
+  return run_lowrank_svd(R, N, K, rank, rank + oversample, power_iters, omega, U, V, sigma, (char*)workspace,
+                         (hipStream_t)stream);
+}
+
+size_t milo_build_compensator_workspace_bytes(int64_t N, int64_t K, int32_t rank, int32_t oversample) {
+  if (check_lowrank_shape(N, K, rank, oversample) != MILO_OK) return 0;
+  return build_workspace_bytes(N, K, rank + oversample);
+}
+
+int32_t milo_build_compensator(const float* W, int64_t N, int64_t K, int32_t rank, int32_t iters,
+                               int32_t oversample, int32_t power_iters, const float* omega, uint8_t* codes,
+                               uint16_t* scale, uint16_t* zero, float* U, float* V, float* sigma,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int32_t rc = check_lowrank_shape(N, K, rank, oversample);
+  if (rc != MILO_OK) return rc;
+  if (K % kGroup) MILO_FAIL(MILO_ERR_SHAPE, "K=%lld must be a multiple of 64", (long long)K);
+  if (iters < 1 || iters > 16) MILO_FAIL(MILO_ERR_ARG, "iters=%d outside 1..16", iters);
+  if (power_iters < 0 || power_iters > 8) MILO_FAIL(MILO_ERR_ARG, "power_iters=%d outside 0..8", power_iters);
+  if (!W || !codes || !scale || !zero) MILO_FAIL(MILO_ERR_NULL, "W, codes, scale, zero are required");
+  if (rank > 0 && (!omega || !U || !V || !sigma))
+    MILO_FAIL(MILO_ERR_NULL, "omega, U, V, sigma are required when rank > 0");
+  if (!aligned(W, 4) || !aligned(scale, 2) || !aligned(zero, 2) || !aligned(omega, 4) || !aligned(U, 4) ||
+      !aligned(V, 4) || !aligned(sigma, 4))
+    MILO_FAIL(MILO_ERR_ALIGN, "W, omega, U, V, sigma 4-byte and scale, zero 2-byte aligned");
+  const size_t need = build_workspace_bytes(N, K, rank + oversample);
+  if (!workspace || ws_bytes < need)
+    MILO_FAIL(MILO_ERR_WORKSPACE, "build workspace %zu bytes < required %zu", ws_bytes, need);
+  if (!aligned(workspace, 256)) MILO_FAIL(MILO_ERR_ALIGN, "workspace must be 256-byte aligned");
+  return run_build(W, N, K, rank, iters, rank + oversample, power_iters, omega, codes, scale, zero, U, V, sigma,
+                   (char*)workspace, (hipStream_t)stream);
+}
+
 size_t milo_route_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t S) {
   (void)k;
   if (T <= 256) return 0;

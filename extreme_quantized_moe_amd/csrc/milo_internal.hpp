@@ -201,6 +201,15 @@ int32_t launch_route(const float* logits, int T, int E, int k, int S, int renorm
                      int32_t* pair_pos, int32_t* offsets, void* ws, hipStream_t st);
 int32_t launch_combine(const float* y, int T, int slots, int H, uint16_t* out, hipStream_t st);
 
+// compensator construction (builder.hip)
+size_t svd_workspace_bytes(int64_t N, int64_t K, int l);
+size_t build_workspace_bytes(int64_t N, int64_t K, int l);
+int32_t run_lowrank_svd(const float* R, int64_t N, int64_t K, int r, int l, int q, const float* omega_t,
+                        float* U, float* V, float* sigma, char* ws, hipStream_t st);
+int32_t run_build(const float* W, int64_t N, int64_t K, int r, int iters, int l, int q, const float* omega,
+                  uint8_t* codes, uint16_t* scale, uint16_t* zero, float* U, float* V, float* sigma,
+                  char* ws, hipStream_t st);
+
 // Resolved plan of one grouped-GEMM call (host side).
 struct GemmPlan {
   int n_tiles;       // N / 64

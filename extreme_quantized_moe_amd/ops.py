@@ -88,6 +88,55 @@ def pack_int3(codes, scale, zero):
     return packed, sz
 
 
+def lowrank_svd(R, rank, omega, power_iters=2):
+    """Rank-r approximation R ~ U V (randomized subspace iteration, see
+    include/milo.h).  R fp32 [N][K]; omega fp32 [rank + oversample][K].
+    Returns (U [N][rank], V [rank][K], sigma [rank])."""
+    R = R.contiguous()
+    omega = omega.contiguous()
+    _cuda(R, omega)
+    N, K = R.shape
+    p = omega.shape[0] - rank
+    dev = R.device
+    U = torch.empty((N, rank), dtype=torch.float32, device=dev)
+    V = torch.empty((rank, K), dtype=torch.float32, device=dev)
+    sigma = torch.empty(rank, dtype=torch.float32, device=dev)
+    nbytes = int(L.lib().milo_lowrank_svd_workspace_bytes(N, K, rank, p))
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    check("milo_lowrank_svd", L.lib().milo_lowrank_svd(
+        _p(R), N, K, rank, p, power_iters, _p(omega), _p(U), _p(V), _p(sigma), _p(ws), ws.numel(), _stream()))
+    return U, V, sigma
+
+
+def build_compensator(W, rank, iters, omega, power_iters=2):
+    """Quantize-and-compensate refinement of one weight matrix (see
+    include/milo.h).  W fp32 [N][K]; omega fp32 [iters][rank + oversample][K]
+    (ignored when rank == 0).  Returns (codes, scale, zero, U, V, sigma)."""
+    W = W.contiguous()
+    _cuda(W)
+    N, K = W.shape
+    dev = W.device
+    if rank > 0:
+        omega = omega.contiguous()
+        _cuda(omega)
+        p = omega.shape[1] - rank
+    else:
+        p = 0
+    codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    scale = torch.empty((N, K // 64), dtype=torch.float16, device=dev)
+    zero = torch.empty_like(scale)
+    U = torch.empty((N, rank), dtype=torch.float32, device=dev)
+    V = torch.empty((rank, K), dtype=torch.float32, device=dev)
+    sigma = torch.empty(rank, dtype=torch.float32, device=dev)
+    nbytes = int(L.lib().milo_build_compensator_workspace_bytes(N, K, rank, p))
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    check("milo_build_compensator", L.lib().milo_build_compensator(
+        _p(W), N, K, rank, iters, p, power_iters, _p(omega) if rank > 0 else None, _p(codes), _p(scale),
+        _p(zero), _p(U) if rank else None, _p(V) if rank else None, _p(sigma) if rank else None,
+        _p(ws), ws.numel(), _stream()))
+    return codes, scale, zero, U, V, sigma
+
+
 _route_ws = {}
 
 

@@ -177,6 +177,68 @@ int32_t milo_pack_lr_int3(const uint8_t* v_codes, const uint16_t* v_scale,
                           uint32_t* usz, void* stream);
 
 /* ======================================================================
+ * Offline compensator construction
+ * ====================================================================== */
+
+/*
+ * Rank-r approximation of a residual matrix, R ~ U V, by randomized subspace
+ * iteration (Halko, Martinsson & Tropp, "Finding structure with randomness",
+ * SIAM Review 2011, Algorithm 4.4) -- the "SVD of the residual" step of
+ * [talk] MiLo Algorithm, Compensation Generation, which keeps the top-R
+ * singular values and vectors.  With l = rank + oversample:
+ *     Y = R Omega;  Q = orth(Y);  power_iters times: Z = orth(R^T Q), Q = orth(R Z)
+ *     B = Q^T R;  B B^T = W diag(lambda) W^T (eigenvalues descending)
+ *     sigma = lambda^(1/2) of the top rank;  U = Q W_r diag(sigma^(1/2));
+ *     V = diag(sigma^(-1/2)) W_r^T B
+ * orth() is CholeskyQR2; fp32 data, fp64 for the l x l factorizations.
+ * U V is the rank-r approximation; the split is balanced (column norms of U =
+ * row norms of V = sigma^(1/2)); directions with sigma = 0 give zero factors.
+ *
+ * R     : float32 [N][K].
+ * omega : float32 [l][K], the Gaussian test matrix, transposed (the caller
+ *         draws it, e.g. N(0, 1)).
+ * U     : out, float32 [N][rank];  V : out, float32 [rank][K];
+ * sigma : out, float32 [rank], descending.
+ * workspace : milo_lowrank_svd_workspace_bytes(...) bytes, 256-byte aligned.
+ * Constraints: 0 <= rank <= 64, oversample >= 0, rank + oversample <= 80 and
+ *   <= min(N, K), N, K <= 2^20, 0 <= power_iters <= 8.  rank == 0 is a no-op.
+ */
+size_t milo_lowrank_svd_workspace_bytes(int64_t N, int64_t K, int32_t rank,
+                                        int32_t oversample);
+int32_t milo_lowrank_svd(const float* R, int64_t N, int64_t K, int32_t rank,
+                         int32_t oversample, int32_t power_iters,
+                         const float* omega, float* U, float* V, float* sigma,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Quantize-and-compensate refinement of one weight matrix, [talk] MiLo
+ * Algorithm (Compensation Generation; the iterative optimization that
+ * recomputes W_quant from U V and U V from the new residual):
+ *     L_0 = 0;  for t = 1..iters:
+ *         (codes, scale, zero) = milo_quantize_rtn_int3(W - L_{t-1})
+ *         R_t = W - (codes - zero) scale
+ *         (U, V, sigma) = milo_lowrank_svd(R_t, test matrix omega[t-1]);  L_t = U V
+ * and returns the last quantization and factors: W ~ deq(codes) + U V, i.e.
+ * the compensator of milo_weights with U [N][rank] and V [rank][K].
+ *
+ * W     : float32 [N][K].
+ * omega : float32 [iters][l][K] test matrices (NULL when rank == 0).
+ * codes : out, uint8 [N][K];  scale, zero : out, fp16 bits [N][K/64].
+ * U, V, sigma : out as in milo_lowrank_svd (unused when rank == 0).
+ * workspace : milo_build_compensator_workspace_bytes(...) bytes (holds one
+ *   N x K float32 residual), 256-byte aligned.
+ * Constraints: those of milo_lowrank_svd, K % 64 == 0, 1 <= iters <= 16.
+ */
+size_t milo_build_compensator_workspace_bytes(int64_t N, int64_t K, int32_t rank,
+                                              int32_t oversample);
+int32_t milo_build_compensator(const float* W, int64_t N, int64_t K, int32_t rank,
+                               int32_t iters, int32_t oversample,
+                               int32_t power_iters, const float* omega,
+                               uint8_t* codes, uint16_t* scale, uint16_t* zero,
+                               float* U, float* V, float* sigma, void* workspace,
+                               size_t ws_bytes, void* stream);
+
+/* ======================================================================
  * Routing
  * ====================================================================== */
 

@@ -175,3 +175,26 @@ def test_combine_rejects(L):
     assert lib.milo_moe_combine(f, 4, 2, 66, f, None) == 2
     assert lib.milo_moe_combine(f, 4, 0, 64, f, None) == 2
     assert lib.milo_moe_combine(C.c_void_p(0x1004), 4, 2, 64, f, None) == 3
+
+
+def test_lowrank_and_build_reject_before_launch(L):
+    lib = L.lib()
+    f = C.c_void_p(0x1000)
+    ws = C.c_void_p(0x100000)
+    svd = lambda N, K, r, p, q=2, R=f, ws=ws, wsb=1 << 30: lib.milo_lowrank_svd(R, N, K, r, p, q, f, f, f, f, ws, wsb, None)
+    assert svd(512, 256, 65, 0) == 4            # rank above 64
+    assert svd(512, 256, 64, 17) == 4           # rank + oversample above 80
+    assert svd(16, 256, 16, 8) == 2             # l above min(N, K)
+    assert svd(512, 256, 16, 8, q=9) == 6
+    assert svd(512, 256, 16, 8, R=None) == 1
+    assert svd(512, 256, 16, 8, wsb=16) == 5
+    assert svd(512, 256, 16, 8, ws=C.c_void_p(0x100010)) == 3
+    assert svd(512, 256, 0, 8) == 0             # rank 0: nothing to do
+    assert lib.milo_lowrank_svd_workspace_bytes(512, 256, 16, 8) > 0
+    b = lambda N, K, r, it, W=f: lib.milo_build_compensator(W, N, K, r, it, 8, 2, f, f, f, f, f, f, f, ws, 1 << 30, None)
+    assert b(512, 200, 16, 1) == 2              # K not a multiple of 64
+    assert b(512, 256, 16, 0) == 6
+    assert b(512, 256, 16, 17) == 6
+    assert b(512, 256, 16, 1, W=None) == 1
+    need = lib.milo_build_compensator_workspace_bytes(14336, 4096, 64, 16)
+    assert need >= 14336 * 4096 * 4
