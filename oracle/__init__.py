@@ -52,6 +52,13 @@ from .builder import (  # noqa: F401
     rsvd_ref,
     build_ref,
 )
+from .rank_policy import (  # noqa: F401
+    kurtosis_ref,
+    expert_frequency_ref,
+    rank_scores_ref,
+    apportion_ranks_ref,
+    rank_policy_ref,
+)
 from .moe import (  # noqa: F401
     linear_ref,
     quantize_expert,
