@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--build", action="store_true",
                     help="time the offline compensator construction (quantize <-> rank-64 SVD refinement) of "
                          "one Mixtral-shaped 14336x4096 weight matrix instead of the MoE layer")
+    ap.add_argument("--ranks", action="store_true",
+                    help="time the adaptive-rank inputs (kurtosis of all 24 expert matrices of a "
+                         "Mixtral-shaped layer, routed pairs per expert) and run the rank policy")
     ap.add_argument("--hbm-probe", action="store_true",
                     help="only measure plain device read (sum) and copy bandwidth on 4 GiB")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -307,6 +310,8 @@ def main():
         return
     if args.build:
         return bench_build(args, m)
+    if args.ranks:
+        return bench_ranks(args, m)
     cfg = SC.get_config(args.config)
     if args.config == "C1":
         return bench_c1(args, m, cfg)
@@ -502,6 +507,73 @@ def bench_build(args, m):
     else:
         res["cpu_baseline"] = None
     del out
+    print(json.dumps(res))
+
+
+def bench_ranks(args, m):
+    """Adaptive rank policy on a Mixtral-shaped layer: per-matrix weight
+    kurtosis of the 8 experts' W1, W3, W2 (24 x 58.7 M fp32 weights, two
+    streaming passes: the HBM-bound part), pairs per expert from routing
+    4096 tokens, then the host apportionment of an average rank of 32."""
+    import torch
+    import synth
+    from synth import configs as SC
+    cfg = SC.get_config("C2")
+    mats = []
+    for e in range(cfg.E):
+        d = synth.gen_expert(cfg, 0, e, 8, device="cuda", which=("W1", "W3", "W2"))
+        mats += [d["W1"].reshape(-1), d["W3"].reshape(-1), d["W2"].reshape(-1)]
+    W = torch.stack(mats)
+    del mats
+    count, elems = W.shape
+    steps = max(1, min(args.steps, 20))
+    for _ in range(max(1, args.warmup)):
+        kurt, _ = m.weight_kurtosis(W, count=count)
+    torch.cuda.synchronize()
+    global TIMER
+    TIMER = HipTimer()
+    a, b = TIMER.event(), TIMER.event()
+    stream = torch.cuda.current_stream().cuda_stream
+    TIMER.record(a, stream)
+    for _ in range(steps):
+        kurt, _ = m.weight_kurtosis(W, count=count)
+    TIMER.record(b, stream)
+    torch.cuda.synchronize()
+    ms = TIMER.ms(a, b) / steps
+    nbytes = 2 * count * elems * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    big = cfg.with_(T=4096)
+    counts = torch.zeros(cfg.E, dtype=torch.int64, device="cuda")
+    r = m.route_sort(synth.gen_logits(big, 0, device="cuda"), cfg.k, 0, True)
+    m.expert_counts(r["offsets"], counts)
+    freq = (counts.double() / big.T).cpu().tolist()
+    kh = kurt.cpu().tolist()
+    ranks = m.rank_policy(kh, [freq[i // 3] for i in range(count)], [False] * count, 32 * count, 8, 64, 8)
+    res = {
+        "metric": "adaptive-rank inputs: weight kurtosis of one Mixtral-shaped MoE layer", "value": round(ms, 3),
+        "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": max(1, args.warmup), "ms_per_step": round(ms, 3),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"kurtosis of {count} fp32 matrices of {elems} weights (8 experts x W1, W3, W2, "
+                               "N(0,0.02)); pairs per expert of 4096 routed tokens; rank budget 32 per matrix",
+                   "ranks": ranks, "kurtosis_range": [round(min(kh), 4), round(max(kh), 4)]},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "moments_kernel (two passes; algorithmic bytes = 2 x 4 B per weight)"},
+    }
+    if not args.no_cpu:
+        import oracle
+        from threadpoolctl import threadpool_info
+        Wh = W[:2].cpu().numpy()
+        t0 = time.perf_counter()
+        for i in range(2):
+            oracle.kurtosis_ref(Wh[i])
+        cpu_s = (time.perf_counter() - t0) * count / 2
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        res["cpu_baseline"] = {"value": round(cpu_s * 1000, 1), "unit": "ms", "cores": int(threads),
+                               "kind": "oracle", "sample": f"oracle.kurtosis_ref on 2 of the {count} matrices, "
+                               f"scaled x{count / 2:.0f}"}
+    else:
+        res["cpu_baseline"] = None
     print(json.dumps(res))
 
 

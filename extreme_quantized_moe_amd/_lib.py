@@ -74,6 +74,10 @@ def lib():
         "milo_build_compensator_workspace_bytes": (sz, [i64, i64, i32, i32]),
         "milo_build_compensator": (i32, [vp, i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                           vp, sz, vp]),
+        "milo_weight_kurtosis_workspace_bytes": (sz, [i64]),
+        "milo_weight_kurtosis": (i32, [vp, i64, i64, vp, vp, vp, sz, vp]),
+        "milo_expert_counts": (i32, [vp, i32, vp, vp]),
+        "milo_rank_policy": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp]),
         "milo_route_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "milo_route_sort": (i32, [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "milo_moe_gemm_workspace_bytes": (sz, [C.POINTER(MiloGemmDesc)]),

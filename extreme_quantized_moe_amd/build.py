@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmilo.so")
 SOURCES = ["abi.cpp", "quant_pack.hip", "route.hip", "combine.hip", "lowrank.hip",
-           "gemm_decode.hip", "gemm_prefill.hip", "builder.hip"]
+           "gemm_decode.hip", "gemm_prefill.hip", "builder.hip", "rank_policy.hip"]
 ARCH = os.environ.get("MILO_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -327,6 +327,48 @@ int32_t milo_build_compensator(const float* W, int64_t N, int64_t K, int32_t ran
                    (char*)workspace, (hipStream_t)stream);
 }
 
+size_t milo_weight_kurtosis_workspace_bytes(int64_t count) {
+  return count >= 1 && count <= 65535 ? kurtosis_workspace_bytes(count) : 0;
+}
+
+int32_t milo_weight_kurtosis(const float* W, int64_t count, int64_t elems, double* kurtosis, double* mean,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!W || !kurtosis) MILO_FAIL(MILO_ERR_NULL, "W and kurtosis are required");
+  if (count < 1 || count > 65535 || elems < 4 || elems % 4 || elems > (1ll << 40))
+    MILO_FAIL(MILO_ERR_SHAPE, "count=%lld elems=%lld: need 1 <= count <= 65535, elems >= 4, elems %% 4 == 0",
+              (long long)count, (long long)elems);
+  if (!aligned(W, 16) || !aligned(kurtosis, 8) || !aligned(mean, 8))
+    MILO_FAIL(MILO_ERR_ALIGN, "W must be 16-byte and kurtosis/mean 8-byte aligned");
+  const size_t need = kurtosis_workspace_bytes(count);
+  if (!workspace || ws_bytes < need)
+    MILO_FAIL(MILO_ERR_WORKSPACE, "kurtosis workspace %zu bytes < required %zu", ws_bytes, need);
+  if (!aligned(workspace, 8)) MILO_FAIL(MILO_ERR_ALIGN, "workspace must be 8-byte aligned");
+  return launch_kurtosis(W, count, elems, kurtosis, mean, (char*)workspace, (hipStream_t)stream);
+}
+
+int32_t milo_expert_counts(const int32_t* offsets, int32_t num_experts, int64_t* counts, void* stream) {
+  g_err[0] = 0;
+  if (!offsets || !counts) MILO_FAIL(MILO_ERR_NULL, "offsets and counts are required");
+  if (num_experts < 1 || num_experts > 256) MILO_FAIL(MILO_ERR_SHAPE, "num_experts=%d outside 1..256", num_experts);
+  if (!aligned(offsets, 4) || !aligned(counts, 8)) MILO_FAIL(MILO_ERR_ALIGN, "offsets 4-, counts 8-byte aligned");
+  return launch_expert_counts(offsets, num_experts, counts, (hipStream_t)stream);
+}
+
+int32_t milo_rank_policy(const double* kurtosis, const double* frequency, const int32_t* dense, int32_t n,
+                         int32_t total_rank, int32_t r_min, int32_t r_max, int32_t step, int32_t* ranks) {
+  g_err[0] = 0;
+  if (n < 0) MILO_FAIL(MILO_ERR_SHAPE, "n=%d < 0", n);
+  if (n == 0) return MILO_OK;
+  if (!kurtosis || !frequency || !dense || !ranks) MILO_FAIL(MILO_ERR_NULL, "all arrays are required");
+  if (step < 1 || r_min < 0 || r_min > r_max || r_max > kMaxRank || r_min % step || r_max % step ||
+      total_rank < 0 || total_rank % step)
+    MILO_FAIL(MILO_ERR_RANK, "step=%d r_min=%d r_max=%d total_rank=%d: need multiples of step, "
+              "0 <= r_min <= r_max <= 64", step, r_min, r_max, total_rank);
+  rank_policy_host(kurtosis, frequency, dense, n, total_rank, r_min, r_max, step, ranks);
+  return MILO_OK;
+}
+
 size_t milo_route_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t S) {
   (void)k;
   if (T <= 256) return 0;

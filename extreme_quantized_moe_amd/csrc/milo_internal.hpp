@@ -210,6 +210,14 @@ int32_t run_build(const float* W, int64_t N, int64_t K, int r, int iters, int l,
                   uint8_t* codes, uint16_t* scale, uint16_t* zero, float* U, float* V, float* sigma,
                   char* ws, hipStream_t st);
 
+// adaptive rank policy (rank_policy.hip)
+size_t kurtosis_workspace_bytes(int64_t count);
+int32_t launch_kurtosis(const float* W, int64_t count, int64_t elems, double* kurt, double* mean_out,
+                        char* ws, hipStream_t st);
+int32_t launch_expert_counts(const int32_t* offsets, int E, int64_t* counts, hipStream_t st);
+void rank_policy_host(const double* kurt, const double* freq, const int32_t* dense, int n, int total_rank,
+                      int r_min, int r_max, int step, int32_t* ranks);
+
 // Resolved plan of one grouped-GEMM call (host side).
 struct GemmPlan {
   int n_tiles;       // N / 64

@@ -137,6 +137,46 @@ def build_compensator(W, rank, iters, omega, power_iters=2):
     return codes, scale, zero, U, V, sigma
 
 
+def weight_kurtosis(W, count=None):
+    """W: fp32, `count` matrices stored back to back (default: the leading
+    dimension of a 3-D tensor, else one matrix).  Returns (kurtosis, mean) as
+    float64 device tensors [count]."""
+    W = W.contiguous()
+    _cuda(W)
+    if count is None:
+        count = W.shape[0] if W.dim() > 2 else 1
+    elems = W.numel() // count
+    kurt = torch.empty(count, dtype=torch.float64, device=W.device)
+    mean = torch.empty(count, dtype=torch.float64, device=W.device)
+    nbytes = int(L.lib().milo_weight_kurtosis_workspace_bytes(count))
+    ws = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=W.device)
+    check("milo_weight_kurtosis", L.lib().milo_weight_kurtosis(
+        _p(W), count, elems, _p(kurt), _p(mean), _p(ws), ws.numel(), _stream()))
+    return kurt, mean
+
+
+def expert_counts(offsets, counts):
+    """counts (int64 device [E]) += pairs per expert of one routing call."""
+    _cuda(offsets, counts)
+    check("milo_expert_counts", L.lib().milo_expert_counts(
+        _p(offsets), counts.numel(), _p(counts), _stream()))
+    return counts
+
+
+def rank_policy(kurtosis, frequency, dense, total_rank, r_min=0, r_max=64, step=8):
+    """Host rank apportionment (see include/milo.h); sequences of floats /
+    bools in, list of ints out."""
+    n = len(kurtosis)
+    k = (C.c_double * n)(*[float(v) for v in kurtosis])
+    f = (C.c_double * n)(*[float(v) for v in frequency])
+    d = (C.c_int32 * n)(*[1 if v else 0 for v in dense])
+    out = (C.c_int32 * n)()
+    check("milo_rank_policy", L.lib().milo_rank_policy(
+        C.cast(k, C.c_void_p), C.cast(f, C.c_void_p), C.cast(d, C.c_void_p), n, total_rank, r_min, r_max,
+        step, C.cast(out, C.c_void_p)))
+    return list(out)
+
+
 _route_ws = {}
 
 

@@ -238,6 +238,48 @@ int32_t milo_build_compensator(const float* W, int64_t N, int64_t K, int32_t ran
                                float* U, float* V, float* sigma, void* workspace,
                                size_t ws_bytes, void* stream);
 
+/*
+ * Adaptive compensator ranks, [talk] MiLo Algorithm, "Mixture of Low-Rank
+ * Compensators and Adaptive Rank Selection": dense (always-activated) parts,
+ * frequently activated experts and weights with a higher kurtosis get higher
+ * ranks.  The pages give no formula; the policy implemented is
+ *     score_m = (dense_m ? 1 : frequency_m) * kurtosis_m / 3
+ * and a budget of total_rank rank units is apportioned in proportion to the
+ * scores in steps of `step`, each rank clipped to [r_min, r_max], by the
+ * largest-remainder method (units handed out, or taken back when r_min
+ * forces it, one at a time by remainder, ties to the lower index; the score
+ * sum runs left to right).
+ */
+
+/* Population kurtosis E[(w - mu)^4] / E[(w - mu)^2]^2 of each of `count`
+   matrices of `elems` float32 values stored back to back (W: device,
+   16-byte aligned; elems % 4 == 0).  Two streaming passes, float64
+   accumulation, deterministic.  kurtosis: out, device double [count] (0 for
+   a constant matrix); mean: optional out, device double [count].
+   workspace: milo_weight_kurtosis_workspace_bytes(count) bytes, device. */
+size_t milo_weight_kurtosis_workspace_bytes(int64_t count);
+int32_t milo_weight_kurtosis(const float* W, int64_t count, int64_t elems,
+                             double* kurtosis, double* mean, void* workspace,
+                             size_t ws_bytes, void* stream);
+
+/* counts[e] += offsets[e + 1] - offsets[e] for e < num_experts (device
+   arrays; counts int64, caller-initialised): routed pairs per expert,
+   accumulated over routing calls -- the activation frequency is counts /
+   tokens. */
+int32_t milo_expert_counts(const int32_t* offsets, int32_t num_experts,
+                           int64_t* counts, void* stream);
+
+/* The apportionment above on HOST arrays of n matrices (kurtosis,
+   frequency: double; dense: int32 0/1) into ranks (host int32 [n]).
+   Synchronous, touches no device.  Constraints: step >= 1; r_min, r_max,
+   total_rank multiples of step; 0 <= r_min <= r_max <= 64.  When
+   n r_min > total_rank or n r_max < total_rank the ranks sum to the nearest
+   feasible total. */
+int32_t milo_rank_policy(const double* kurtosis, const double* frequency,
+                         const int32_t* dense, int32_t n, int32_t total_rank,
+                         int32_t r_min, int32_t r_max, int32_t step,
+                         int32_t* ranks);
+
 /* ======================================================================
  * Routing
  * ====================================================================== */

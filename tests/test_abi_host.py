@@ -198,3 +198,37 @@ def test_lowrank_and_build_reject_before_launch(L):
     assert b(512, 256, 16, 1, W=None) == 1
     need = lib.milo_build_compensator_workspace_bytes(14336, 4096, 64, 16)
     assert need >= 14336 * 4096 * 4
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_rank_policy_host_matches_oracle(L, seed):
+    """milo_rank_policy is host code: same integers as the oracle for the
+    same inputs (random kurtosis, frequency, dense flags, budgets, caps)."""
+    import numpy as np
+    import oracle
+    import extreme_quantized_moe_amd as m
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 70))
+    kurt = list(rng.uniform(2.0, 9.0, n))
+    freq = list(rng.uniform(0.0, 0.5, n))
+    dense = list(rng.random(n) < 0.1)
+    r_min = 8 * int(rng.integers(0, 2))
+    total = 8 * int(rng.integers(n * r_min // 8, n * 8 + 1))
+    got = m.rank_policy(kurt, freq, dense, total, r_min, 64, 8)
+    assert got == oracle.rank_policy_ref(kurt, freq, dense, total, r_min, 64, 8)
+
+
+def test_rank_policy_hand_case_and_rejects(L):
+    import extreme_quantized_moe_amd as m
+    assert m.rank_policy([3.0, 3.0], [0.25, 0.25], [True, False], 64) == [48, 16]
+    with pytest.raises(m.MiloError):
+        m.rank_policy([3.0], [1.0], [False], 12)           # budget not a multiple of the step
+    with pytest.raises(m.MiloError):
+        m.rank_policy([3.0], [1.0], [False], 64, r_min=16, r_max=8)
+    lib = L.lib()
+    f = C.c_void_p(0x1000)
+    assert lib.milo_weight_kurtosis(f, 4, 6, f, None, f, 1 << 20, None) == 2       # elems % 4
+    assert lib.milo_weight_kurtosis(C.c_void_p(0x1004), 4, 64, f, None, f, 1 << 20, None) == 3
+    assert lib.milo_weight_kurtosis(f, 4, 64, f, None, f, 8, None) == 5
+    assert lib.milo_expert_counts(None, 8, f, None) == 1
+    assert lib.milo_expert_counts(f, 0, f, None) == 2
