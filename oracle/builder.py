@@ -9,9 +9,9 @@ same section: quantization and compensation are then refined iteratively --
 W_quant is recomputed from U V and U V from the new residual.
 
 Readings (the pages give no formulas):
-* quantizer: the RTN int3 g64 rule of oracle.quant (the pages' initial HQQ
-  step is a separate row);
-* iteration t = 1..iters:  Wq_t = RTN(W - L_{t-1}) with L_0 = 0;
+* quantizer: the RTN int3 g64 rule of oracle.quant, or the HQQ-style
+  zero-point optimization of oracle.hqq (the pages' initial quantizer);
+* iteration t = 1..iters:  Wq_t = quantize(W - L_{t-1}) with L_0 = 0;
   R_t = W - deq(Wq_t);  L_t = best rank-r approximation of R_t;
   the output is (Wq_T, L_T);
 * factor split: L = U V with U = U_r diag(sqrt(sigma)), V = diag(sqrt(sigma))
@@ -25,6 +25,7 @@ Readings (the pages give no formulas):
 """
 import numpy as np
 
+from .hqq import quantize_hqq_int3
 from .quant import dequant_int3, quantize_rtn_int3
 
 
@@ -73,7 +74,7 @@ def rsvd_ref(R, r, omega_t, power_iters):
     return U, V, s[:r]
 
 
-def build_ref(W, r, iters, omegas_t, power_iters, group=64):
+def build_ref(W, r, iters, omegas_t, power_iters, group=64, quantizer="rtn"):
     """The refinement loop above with the randomized SVD; omegas_t[t] is the
     test matrix of iteration t ([iters][l][K]).  Returns a dict with the last
     codes/scale/zero, U, V, sigma, and the per-iteration errors
@@ -87,7 +88,8 @@ def build_ref(W, r, iters, omegas_t, power_iters, group=64):
     errs, res_norms = [], []
     codes = scale = zero = None
     for t in range(iters):
-        codes, scale, zero = quantize_rtn_int3(W - L, group)
+        quantize = quantize_hqq_int3 if quantizer == "hqq" else quantize_rtn_int3
+        codes, scale, zero = quantize(W - L, group)
         R = residual_ref(W, codes, scale, zero, group)
         U, V, sigma = rsvd_ref(R, r, omegas_t[t], power_iters)
         L = U @ V

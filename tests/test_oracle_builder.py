@@ -139,3 +139,28 @@ def test_build_fixed_point_on_grid_weights():
     assert np.all(out["scale"] == 0.25) and np.all(out["zero"] == 3.0)
     assert max(out["residual_norms"]) == 0.0 and max(out["errors"]) == 0.0
     assert np.all(out["sigma"] == 0.0)
+
+
+def test_build_with_hqq_quantizer():
+    """quantizer "hqq": the first iteration quantizes W with the HQQ-style
+    quantizer of oracle/hqq.py and compensates its residual; grid weights are
+    still a fixed point; the compensated error stays below HQQ's own error."""
+    W = _weights(128, 256, 16)
+    om = np.stack([_omega(24, 256, 17 + t) for t in range(2)])
+    one = OB.build_ref(W, 16, 1, om[:1], power_iters=2, quantizer="hqq")
+    from oracle import hqq as HQ
+    q, s, z = HQ.quantize_hqq_int3(W)
+    np.testing.assert_array_equal(one["codes"], q)
+    np.testing.assert_array_equal(one["zero"].view(np.uint16), z.view(np.uint16))
+    U, V, sg = OB.rsvd_ref(OB.residual_ref(W, q, s, z), 16, om[0], 2)
+    np.testing.assert_allclose(one["U"] @ one["V"], U @ V, rtol=0, atol=1e-15)
+    two = OB.build_ref(W, 16, 2, om, power_iters=2, quantizer="hqq")
+    assert two["errors"][-1] < two["residual_norms"][0]
+    rng = np.random.default_rng(18)
+    codes = rng.integers(0, 8, (64, 128)).astype(np.uint8)
+    codes[:, ::64] = 0
+    codes[:, 1::64] = 7
+    G = ((codes.astype(np.float64) - 3.0) * 0.25).astype(np.float32)
+    out = OB.build_ref(G, 8, 2, np.stack([_omega(12, 128, 19 + t) for t in range(2)]), 1, quantizer="hqq")
+    np.testing.assert_array_equal(out["codes"], codes)
+    assert max(out["errors"]) == 0.0
