@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--ranks", action="store_true",
                     help="time the adaptive-rank inputs (kurtosis of all 24 expert matrices of a "
                          "Mixtral-shaped layer, routed pairs per expert) and run the rank policy")
+    ap.add_argument("--quantizer", default="rtn", choices=["rtn", "hqq"],
+                    help="--build: quantizer of the refinement rounds")
+    ap.add_argument("--hqq", action="store_true",
+                    help="time the HQQ-style int3 quantizer on one Mixtral-shaped 14336x4096 matrix")
     ap.add_argument("--hbm-probe", action="store_true",
                     help="only measure plain device read (sum) and copy bandwidth on 4 GiB")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -312,6 +316,8 @@ def main():
         return bench_build(args, m)
     if args.ranks:
         return bench_ranks(args, m)
+    if args.hqq:
+        return bench_hqq(args, m)
     cfg = SC.get_config(args.config)
     if args.config == "C1":
         return bench_c1(args, m, cfg)
@@ -461,7 +467,7 @@ def bench_build(args, m):
     steps = max(1, min(args.steps, 5))
     warm = max(1, min(args.warmup, 2))
     for _ in range(warm):
-        m.build_compensator(W, r, iters, omega, power_iters=q)
+        m.build_compensator(W, r, iters, omega, power_iters=q, quantizer=args.quantizer)
     torch.cuda.synchronize()
     global TIMER
     TIMER = HipTimer()
@@ -469,7 +475,7 @@ def bench_build(args, m):
     stream = torch.cuda.current_stream().cuda_stream
     TIMER.record(a, stream)
     for _ in range(steps):
-        out = m.build_compensator(W, r, iters, omega, power_iters=q)
+        out = m.build_compensator(W, r, iters, omega, power_iters=q, quantizer=args.quantizer)
     TIMER.record(b, stream)
     torch.cuda.synchronize()
     ms = TIMER.ms(a, b) / steps
@@ -484,7 +490,8 @@ def bench_build(args, m):
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"compensator build: W {N}x{K} ~N(0,0.02), rank {r}, oversampling {p}, "
-                               f"{q} power iterations, {iters} quantize/compensate rounds",
+                               f"{q} power iterations, {iters} quantize/compensate rounds, "
+                               f"{args.quantizer} quantizer",
                    "alg_flops": int(flops)},
         "roofline": {"bound": "alu", "achieved": round(tfl, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tfl / peak, 4), "traffic": None,
@@ -498,7 +505,7 @@ def bench_build(args, m):
         Wh = W.cpu().numpy()
         om = omega.cpu().numpy()
         t0 = time.perf_counter()
-        oracle.build_ref(Wh, r, iters, om, q)
+        oracle.build_ref(Wh, r, iters, om, q, quantizer=args.quantizer)
         cpu_s = time.perf_counter() - t0
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
         res["cpu_baseline"] = {"value": round(cpu_s * 1000, 1), "unit": "ms", "cores": int(threads),
@@ -572,6 +579,74 @@ def bench_ranks(args, m):
         res["cpu_baseline"] = {"value": round(cpu_s * 1000, 1), "unit": "ms", "cores": int(threads),
                                "kind": "oracle", "sample": f"oracle.kurtosis_ref on 2 of the {count} matrices, "
                                f"scaled x{count / 2:.0f}"}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res))
+
+
+def bench_hqq(args, m):
+    """HQQ-style quantization (RTN scale, 20 half-quadratic zero-point
+    iterations, float64) of one Mixtral-shaped gate matrix.  The roofline line
+    counts 16 float64 operations per weight and iteration (codes at z, the
+    error, the threshold test, the update term and its sum, codes and error
+    at the fp16 candidate and that sum; the threshold's power is not counted:
+    it is needed only where the threshold can fire, which on weights of this
+    magnitude is nowhere) against the fp64 vector peak."""
+    import torch
+    import numpy as np
+    import synth
+    from synth import configs as SC
+    cfg = SC.get_config("C2")
+    W = synth.gen_expert(cfg, 0, 0, 8, device="cuda", which=("W1",))["W1"].contiguous()
+    rows, K = W.shape
+    iters = 20
+    steps = max(1, min(args.steps, 10))
+    for _ in range(max(1, args.warmup)):
+        m.quantize_hqq_int3(W, iters=iters)
+    torch.cuda.synchronize()
+    global TIMER
+    TIMER = HipTimer()
+    a, b = TIMER.event(), TIMER.event()
+    stream = torch.cuda.current_stream().cuda_stream
+    TIMER.record(a, stream)
+    for _ in range(steps):
+        c, s, z = m.quantize_hqq_int3(W, iters=iters)
+    TIMER.record(b, stream)
+    torch.cuda.synchronize()
+    ms = TIMER.ms(a, b) / steps
+    ops = 16.0 * rows * K * iters
+    tfl = ops / (ms * 1e-3) / 1e12
+    peak = 78.6
+    # quality against RTN on the same matrix (sampled rows, float64 on the host)
+    rows_s = np.random.default_rng(0).choice(rows, 512, replace=False)
+    import oracle
+    Wh = W[torch.from_numpy(rows_s).cuda()].cpu().numpy().astype(np.float64)
+    q0, s0, z0 = m.quantize_rtn_int3(W)
+    dh = oracle.dequant_int3(c.cpu().numpy()[rows_s], s.cpu().numpy()[rows_s], z.cpu().numpy()[rows_s])
+    dr = oracle.dequant_int3(q0.cpu().numpy()[rows_s], s0.cpu().numpy()[rows_s], z0.cpu().numpy()[rows_s])
+    res = {
+        "metric": "HQQ-style int3 quantization time per weight matrix", "value": round(ms, 3), "unit": "ms",
+        "n_gpus": 1, "steps": steps, "warmup": max(1, args.warmup), "ms_per_step": round(ms, 3),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"HQQ-style quantization of W {rows}x{K} ~N(0,0.02), groups of 64, p 0.7, "
+                               f"beta 10, kappa 1.01, {iters} iterations",
+                   "mae_vs_rtn": round(float(np.abs(Wh - dh).mean() / np.abs(Wh - dr).mean()), 4),
+                   "mse_vs_rtn": round(float(((Wh - dh) ** 2).mean() / ((Wh - dr) ** 2).mean()), 4)},
+        "roofline": {"bound": "alu", "achieved": round(tfl, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tfl / peak, 4), "traffic": None,
+                     "kernel": "hqq_kernel (16 fp64 operations per weight and iteration counted)"},
+    }
+    if not args.no_cpu:
+        from oracle import hqq as HQ
+        from threadpoolctl import threadpool_info
+        n = 512
+        t0 = time.perf_counter()
+        HQ.quantize_hqq_int3(W[:n].cpu().numpy(), iters=iters)
+        cpu_s = (time.perf_counter() - t0) * rows / n
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        res["cpu_baseline"] = {"value": round(cpu_s * 1000, 1), "unit": "ms", "cores": int(threads),
+                               "kind": "oracle", "sample": f"oracle.hqq.quantize_hqq_int3 on {n} of the {rows} rows, "
+                               f"scaled x{rows / n:.0f}"}
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res))

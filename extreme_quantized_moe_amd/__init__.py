@@ -14,5 +14,5 @@ lib()  # fail loudly at import if libmilo.so is missing
 from .ops import (  # noqa: E402,F401
     Family, MoELayer, build_compensator, expert_counts, lowrank_svd, lr_words, moe_combine, rank_policy,
     weight_kurtosis, moe_lowrank_prepass, moe_w3a16_lowrank_gemm, pack_int3,
-    pack_lr_int3, packed_words, quantize_rtn_int3, route_sort, sz_words,
+    pack_lr_int3, packed_words, quantize_hqq_int3, quantize_rtn_int3, route_sort, sz_words,
 )

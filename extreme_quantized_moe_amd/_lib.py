@@ -12,6 +12,7 @@ EPI_NONE, EPI_SWIGLU, EPI_ROUTE_SCALE = 0, 1, 2
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 GEMM_PREPASS_DONE = 1
 LR_FP16, LR_INT3 = 0, 1
+QUANT_RTN, QUANT_HQQ = 0, 1
 
 
 class MiloWeights(C.Structure):
@@ -64,6 +65,8 @@ def lib():
         "milo_quantize_rtn_int3": (i32, [vp, i64, i64, vp, vp, vp, vp]),
         "milo_quantize_rtn_int3_grouped": (i32, [vp, i64, i64, i32, vp, vp, vp, vp]),
         "milo_pack_int3": (i32, [vp, vp, vp, i64, i64, vp, vp, vp]),
+        "milo_quantize_hqq_int3": (i32, [vp, i64, i64, i32, C.c_double, C.c_double, C.c_double, vp, vp, vp,
+                                          vp]),
         "milo_lr_v_words": (i64, [i32, i64]),
         "milo_lr_v_sz_words": (i64, [i32, i64]),
         "milo_lr_u_words": (i64, [i64, i32]),
@@ -72,8 +75,8 @@ def lib():
         "milo_lowrank_svd_workspace_bytes": (sz, [i64, i64, i32, i32]),
         "milo_lowrank_svd": (i32, [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
         "milo_build_compensator_workspace_bytes": (sz, [i64, i64, i32, i32]),
-        "milo_build_compensator": (i32, [vp, i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
-                                          vp, sz, vp]),
+        "milo_build_compensator": (i32, [vp, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, sz, vp]),
         "milo_weight_kurtosis_workspace_bytes": (sz, [i64]),
         "milo_weight_kurtosis": (i32, [vp, i64, i64, vp, vp, vp, sz, vp]),
         "milo_expert_counts": (i32, [vp, i32, vp, vp]),

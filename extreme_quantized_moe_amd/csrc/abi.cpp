@@ -224,6 +224,22 @@ int32_t milo_quantize_rtn_int3(const float* W, int64_t rows, int64_t K, uint8_t*
   return milo_quantize_rtn_int3_grouped(W, rows, K, kGroup, codes, scale, zero, stream);
 }
 
+int32_t milo_quantize_hqq_int3(const float* W, int64_t rows, int64_t K, int32_t iters, double p_norm,
+                               double beta, double kappa, uint8_t* codes, uint16_t* scale, uint16_t* zero,
+                               void* stream) {
+  g_err[0] = 0;
+  if (!W || !codes || !scale || !zero) MILO_FAIL(MILO_ERR_NULL, "W, codes, scale, zero are required");
+  if (rows < 1 || K < 64 || K % 64 || rows > (1ll << 31) || K > (1ll << 31))
+    MILO_FAIL(MILO_ERR_SHAPE, "rows=%lld K=%lld: need rows >= 1, K >= 64, K %% 64 == 0", (long long)rows,
+              (long long)K);
+  if (iters < 0 || iters > 1000 || !(p_norm > 0.0 && p_norm <= 1.0) || !(beta > 0.0) || !(kappa >= 1.0))
+    MILO_FAIL(MILO_ERR_ARG, "iters=%d p=%g beta=%g kappa=%g: need 0 <= iters <= 1000, 0 < p <= 1, beta > 0, "
+              "kappa >= 1", iters, p_norm, beta, kappa);
+  if (!aligned(W, 4) || !aligned(scale, 2) || !aligned(zero, 2))
+    MILO_FAIL(MILO_ERR_ALIGN, "W must be 4-byte and scale/zero 2-byte aligned");
+  return launch_hqq(W, rows, K, iters, p_norm, beta, kappa, codes, scale, zero, (hipStream_t)stream);
+}
+
 int64_t milo_lr_v_words(int32_t max_rank, int64_t K) { return 3 * (int64_t)max_rank * K / 32; }
 int64_t milo_lr_v_sz_words(int32_t max_rank, int64_t K) { return (int64_t)max_rank * K / 64; }
 int64_t milo_lr_u_words(int64_t N, int32_t max_rank) { return 3 * N * (int64_t)round_up(max_rank, 32) / 32; }
@@ -304,7 +320,8 @@ size_t milo_build_compensator_workspace_bytes(int64_t N, int64_t K, int32_t rank
 }
 
 int32_t milo_build_compensator(const float* W, int64_t N, int64_t K, int32_t rank, int32_t iters,
-                               int32_t oversample, int32_t power_iters, const float* omega, uint8_t* codes,
+                               int32_t oversample, int32_t power_iters, int32_t quantizer,
+                               const float* omega, uint8_t* codes,
                                uint16_t* scale, uint16_t* zero, float* U, float* V, float* sigma,
                                void* workspace, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
@@ -313,6 +330,8 @@ int32_t milo_build_compensator(const float* W, int64_t N, int64_t K, int32_t ran
   if (K % kGroup) MILO_FAIL(MILO_ERR_SHAPE, "K=%lld must be a multiple of 64", (long long)K);
   if (iters < 1 || iters > 16) MILO_FAIL(MILO_ERR_ARG, "iters=%d outside 1..16", iters);
   if (power_iters < 0 || power_iters > 8) MILO_FAIL(MILO_ERR_ARG, "power_iters=%d outside 0..8", power_iters);
+  if (quantizer != MILO_QUANT_RTN && quantizer != MILO_QUANT_HQQ)
+    MILO_FAIL(MILO_ERR_ARG, "unknown quantizer %d", quantizer);
   if (!W || !codes || !scale || !zero) MILO_FAIL(MILO_ERR_NULL, "W, codes, scale, zero are required");
   if (rank > 0 && (!omega || !U || !V || !sigma))
     MILO_FAIL(MILO_ERR_NULL, "omega, U, V, sigma are required when rank > 0");
@@ -323,7 +342,8 @@ int32_t milo_build_compensator(const float* W, int64_t N, int64_t K, int32_t ran
   if (!workspace || ws_bytes < need)
     MILO_FAIL(MILO_ERR_WORKSPACE, "build workspace %zu bytes < required %zu", ws_bytes, need);
   if (!aligned(workspace, 256)) MILO_FAIL(MILO_ERR_ALIGN, "workspace must be 256-byte aligned");
-  return run_build(W, N, K, rank, iters, rank + oversample, power_iters, omega, codes, scale, zero, U, V, sigma,
+  return run_build(W, N, K, rank, iters, rank + oversample, power_iters, omega, quantizer, codes, scale, zero, U,
+                   V, sigma,
                    (char*)workspace, (hipStream_t)stream);
 }
 

@@ -28,6 +28,9 @@
 namespace milo {
 
 constexpr int kMaxL = 80;          // rank + oversampling
+// HQQ settings of the refinement (the method's published defaults)
+constexpr int kHqqIters = 20;
+constexpr double kHqqP = 0.7, kHqqBeta = 10.0, kHqqKappa = 1.01;
 constexpr int kSplitRows = 512;    // target rows per gemm_tn split
 
 // ---------------------------------------------------------------- elementwise
@@ -528,8 +531,8 @@ size_t build_workspace_bytes(int64_t N, int64_t K, int l) {
 }
 
 int32_t run_build(const float* W, int64_t N, int64_t K, int r, int iters, int l, int q, const float* omega,
-                  uint8_t* codes, uint16_t* scale, uint16_t* zero, float* U, float* V, float* sigma,
-                  char* ws, hipStream_t st) {
+                  int quantizer, uint8_t* codes, uint16_t* scale, uint16_t* zero, float* U, float* V,
+                  float* sigma, char* ws, hipStream_t st) {
   float* Rm = (float*)ws;
   char* svd_ws = ws + align256((size_t)N * K * 4);
   for (int it = 0; it < iters; ++it) {
@@ -539,7 +542,9 @@ int32_t run_build(const float* W, int64_t N, int64_t K, int r, int iters, int l,
                          dim3(256), 0, st, W, U, V, N, K, r, Rm);
       target = Rm;
     }
-    int32_t rc = launch_quantize(target, N, K, kGroup, codes, scale, zero, st);
+    int32_t rc = quantizer == MILO_QUANT_HQQ
+                     ? launch_hqq(target, N, K, kHqqIters, kHqqP, kHqqBeta, kHqqKappa, codes, scale, zero, st)
+                     : launch_quantize(target, N, K, kGroup, codes, scale, zero, st);
     if (rc != MILO_OK) return rc;
     if (r == 0) continue;
     hipLaunchKernelGGL(residual_kernel, dim3(grid_1d(N * K)), dim3(256), 0, st, W, codes, scale, zero, N, K,

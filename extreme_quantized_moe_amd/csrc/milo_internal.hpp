@@ -194,6 +194,8 @@ int32_t launch_pack_lr(const uint8_t* v_codes, const uint16_t* v_scale, const ui
                        const uint8_t* u_codes, const uint16_t* u_scale, const uint16_t* u_zero,
                        int64_t N, int64_t K, int rank, int max_rank, uint32_t* vq, uint32_t* vsz,
                        uint32_t* uq, uint32_t* usz, hipStream_t st);
+int32_t launch_hqq(const float* W, int64_t rows, int64_t K, int iters, double p, double beta, double kappa,
+                   uint8_t* codes, uint16_t* scale, uint16_t* zero, hipStream_t st);
 int32_t launch_pack(const uint8_t* codes, const uint16_t* scale, const uint16_t* zero,
                     int64_t rows, int64_t K, uint32_t* packed, uint32_t* sz, hipStream_t st);
 int32_t launch_route(const float* logits, int T, int E, int k, int S, int renorm,
@@ -207,8 +209,8 @@ size_t build_workspace_bytes(int64_t N, int64_t K, int l);
 int32_t run_lowrank_svd(const float* R, int64_t N, int64_t K, int r, int l, int q, const float* omega_t,
                         float* U, float* V, float* sigma, char* ws, hipStream_t st);
 int32_t run_build(const float* W, int64_t N, int64_t K, int r, int iters, int l, int q, const float* omega,
-                  uint8_t* codes, uint16_t* scale, uint16_t* zero, float* U, float* V, float* sigma,
-                  char* ws, hipStream_t st);
+                  int quantizer, uint8_t* codes, uint16_t* scale, uint16_t* zero, float* U, float* V,
+                  float* sigma, char* ws, hipStream_t st);
 
 // adaptive rank policy (rank_policy.hip)
 size_t kurtosis_workspace_bytes(int64_t count);

@@ -51,6 +51,20 @@ def quantize_rtn_int3(W, group=64):
     return codes, scale, zero
 
 
+def quantize_hqq_int3(W, iters=20, p_norm=0.7, beta=10.0, kappa=1.01):
+    """HQQ-style zero-point optimization on top of the RTN scale (see
+    include/milo.h).  fp32 [rows][K] -> (codes, scale fp16, zero fp16)."""
+    W = W.contiguous()
+    _cuda(W)
+    rows, K = W.shape
+    codes = torch.empty((rows, K), dtype=torch.uint8, device=W.device)
+    scale = torch.empty((rows, K // 64), dtype=torch.float16, device=W.device)
+    zero = torch.empty_like(scale)
+    check("milo_quantize_hqq_int3", L.lib().milo_quantize_hqq_int3(
+        _p(W), rows, K, iters, p_norm, beta, kappa, _p(codes), _p(scale), _p(zero), _stream()))
+    return codes, scale, zero
+
+
 def lr_words(N, K, max_rank):
     """Per-expert uint32 word counts of the int3 compensator layouts:
     (V codes, V scale/zero, U codes, U scale/zero)."""
@@ -108,10 +122,12 @@ def lowrank_svd(R, rank, omega, power_iters=2):
     return U, V, sigma
 
 
-def build_compensator(W, rank, iters, omega, power_iters=2):
+def build_compensator(W, rank, iters, omega, power_iters=2, quantizer="rtn"):
     """Quantize-and-compensate refinement of one weight matrix (see
     include/milo.h).  W fp32 [N][K]; omega fp32 [iters][rank + oversample][K]
-    (ignored when rank == 0).  Returns (codes, scale, zero, U, V, sigma)."""
+    (ignored when rank == 0); quantizer "rtn" or "hqq".  Returns (codes,
+    scale, zero, U, V, sigma)."""
+    qid = {"rtn": L.QUANT_RTN, "hqq": L.QUANT_HQQ}[quantizer]
     W = W.contiguous()
     _cuda(W)
     N, K = W.shape
@@ -131,7 +147,7 @@ def build_compensator(W, rank, iters, omega, power_iters=2):
     nbytes = int(L.lib().milo_build_compensator_workspace_bytes(N, K, rank, p))
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     check("milo_build_compensator", L.lib().milo_build_compensator(
-        _p(W), N, K, rank, iters, p, power_iters, _p(omega) if rank > 0 else None, _p(codes), _p(scale),
+        _p(W), N, K, rank, iters, p, power_iters, qid, _p(omega) if rank > 0 else None, _p(codes), _p(scale),
         _p(zero), _p(U) if rank else None, _p(V) if rank else None, _p(sigma) if rank else None,
         _p(ws), ws.numel(), _stream()))
     return codes, scale, zero, U, V, sigma
@@ -227,10 +243,11 @@ class Family:
         self.lrq = lrq            # (Vq, Vsz, Uq, Usz) for int3 factors
 
     @staticmethod
-    def from_dense(Ws, As, Bs, max_rank=None, device="cuda", lr_format="fp16"):
+    def from_dense(Ws, As, Bs, max_rank=None, device="cuda", lr_format="fp16", quantizer="rtn"):
         """Ws: list of fp32 [N][K]; As: list of fp16 [K][r_e]; Bs: fp16 [r_e][N]
         (the compensator as X A B, i.e. V = A^T, U = B^T).  Quantizes each W on
-        the GPU (RTN int3, group 64) and packs all experts in one call.  With
+        the GPU (int3, group 64; quantizer "rtn" or "hqq") and packs all
+        experts in one call.  With
         lr_format "int3" the factors are quantized on the GPU as well (V rows
         in groups of 64 along K, U rows in one group of r_e) and packed per
         expert."""
@@ -242,7 +259,8 @@ class Family:
         scale = torch.empty((E * N, K // 64), dtype=torch.float16, device=device)
         zero = torch.empty_like(scale)
         for e, W in enumerate(Ws):
-            c, s, z = quantize_rtn_int3(W.to(device=device, dtype=torch.float32))
+            Wd = W.to(device=device, dtype=torch.float32)
+            c, s, z = quantize_hqq_int3(Wd) if quantizer == "hqq" else quantize_rtn_int3(Wd)
             codes[e * N:(e + 1) * N] = c
             scale[e * N:(e + 1) * N] = s
             zero[e * N:(e + 1) * N] = z

@@ -92,6 +92,29 @@ int32_t milo_quantize_rtn_int3_grouped(const float* W, int64_t rows, int64_t K,
                                        uint16_t* scale, uint16_t* zero,
                                        void* stream);
 
+/*
+ * HQQ-style int3 quantization ([talk] Key Findings / MiLo Algorithm: MiLo's
+ * initial, calibration-free quantizer is HQQ; the method is Badri & Shaji,
+ * "Half-Quadratic Quantization of Large Machine Learning Models", 2023):
+ * per row and group of 64 columns, the RTN scale of milo_quantize_rtn_int3
+ * is kept and the zero point is optimized for a sparsity-promoting l_p error
+ * by half-quadratic splitting, in float64:
+ *     z_0 = RTN zero point;  repeat iters times:
+ *         q = clamp(rint(w / s + z), 0, 7);  x = w - (q - z) s
+ *         W_e = sign(x) max(|x| - |x|^(p_norm - 1) / beta, 0)
+ *         z = mean over the group of (q - (w - W_e) / s);  beta *= kappa
+ *     after each iteration the fp16 value of z is a candidate, scored by the
+ *     group's mean absolute error with codes chosen at it; the best
+ *     candidate (RTN's zero point first) is stored, with its codes.
+ * So no group's mean absolute error exceeds RTN's.  Published defaults:
+ * p_norm 0.7, beta 10, kappa 1.01, 20 iterations; iters 0 reproduces RTN.
+ * Arguments and outputs as milo_quantize_rtn_int3.
+ */
+int32_t milo_quantize_hqq_int3(const float* W, int64_t rows, int64_t K,
+                               int32_t iters, double p_norm, double beta,
+                               double kappa, uint8_t* codes, uint16_t* scale,
+                               uint16_t* zero, void* stream);
+
 /* Number of uint32 words of the packed codes of a rows x K matrix: 3*rows*K/32. */
 int64_t milo_packed_words(int64_t rows, int64_t K);
 /* Number of uint32 words of the tiled scale/zero of a rows x K matrix: rows*K/64. */
@@ -215,7 +238,10 @@ int32_t milo_lowrank_svd(const float* R, int64_t N, int64_t K, int32_t rank,
  * Algorithm (Compensation Generation; the iterative optimization that
  * recomputes W_quant from U V and U V from the new residual):
  *     L_0 = 0;  for t = 1..iters:
- *         (codes, scale, zero) = milo_quantize_rtn_int3(W - L_{t-1})
+ *         (codes, scale, zero) = quantize(W - L_{t-1}), quantize =
+ *             milo_quantize_rtn_int3 (quantizer MILO_QUANT_RTN) or
+ *             milo_quantize_hqq_int3 with its published defaults
+ *             (MILO_QUANT_HQQ, the pages' initial quantizer)
  *         R_t = W - (codes - zero) scale
  *         (U, V, sigma) = milo_lowrank_svd(R_t, test matrix omega[t-1]);  L_t = U V
  * and returns the last quantization and factors: W ~ deq(codes) + U V, i.e.
@@ -229,11 +255,13 @@ int32_t milo_lowrank_svd(const float* R, int64_t N, int64_t K, int32_t rank,
  *   N x K float32 residual), 256-byte aligned.
  * Constraints: those of milo_lowrank_svd, K % 64 == 0, 1 <= iters <= 16.
  */
+enum { MILO_QUANT_RTN = 0, MILO_QUANT_HQQ = 1 };
 size_t milo_build_compensator_workspace_bytes(int64_t N, int64_t K, int32_t rank,
                                               int32_t oversample);
 int32_t milo_build_compensator(const float* W, int64_t N, int64_t K, int32_t rank,
                                int32_t iters, int32_t oversample,
-                               int32_t power_iters, const float* omega,
+                               int32_t power_iters, int32_t quantizer,
+                               const float* omega,
                                uint8_t* codes, uint16_t* scale, uint16_t* zero,
                                float* U, float* V, float* sigma, void* workspace,
                                size_t ws_bytes, void* stream);

@@ -191,7 +191,9 @@ def test_lowrank_and_build_reject_before_launch(L):
     assert svd(512, 256, 16, 8, ws=C.c_void_p(0x100010)) == 3
     assert svd(512, 256, 0, 8) == 0             # rank 0: nothing to do
     assert lib.milo_lowrank_svd_workspace_bytes(512, 256, 16, 8) > 0
-    b = lambda N, K, r, it, W=f: lib.milo_build_compensator(W, N, K, r, it, 8, 2, f, f, f, f, f, f, f, ws, 1 << 30, None)
+    b = lambda N, K, r, it, W=f, qz=0: lib.milo_build_compensator(W, N, K, r, it, 8, 2, qz, f, f, f, f, f, f, f, ws,
+                                                                  1 << 30, None)
+    assert b(512, 256, 16, 1, qz=2) == 6
     assert b(512, 200, 16, 1) == 2              # K not a multiple of 64
     assert b(512, 256, 16, 0) == 6
     assert b(512, 256, 16, 17) == 6

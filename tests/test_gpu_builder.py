@@ -151,6 +151,29 @@ def test_build_rank_zero_is_rtn():
     np.testing.assert_array_equal(to_np(c), q)
 
 
+def test_build_with_hqq_quantizer():
+    """quantizer "hqq", 2 iterations: the first iteration's codes follow the
+    HQQ-style quantizer (against the oracle's float64 run, by share: zero
+    candidates whose errors tie to the last bits may differ), and the final
+    codes and compensated error follow the oracle's refinement."""
+    m = _m()
+    N, K, r, p = 512, 512, 16, 8
+    W = _weights(N, K, 50)
+    om = torch.stack([_omega(r + p, K, 60 + t) for t in range(2)])
+    c1 = m.build_compensator(W.cuda(), r, 1, om[:1].cuda(), power_iters=2, quantizer="hqq")[0]
+    out = m.build_compensator(W.cuda(), r, 2, om.cuda(), power_iters=2, quantizer="hqq")
+    torch.cuda.synchronize()
+    from oracle import hqq as HQ
+    q, _, _ = HQ.quantize_hqq_int3(W.numpy())
+    assert np.mean(to_np(c1) == q) >= 0.9999
+    ref = OB.build_ref(W.numpy(), r, 2, om.numpy(), 2, quantizer="hqq")
+    codes, scale, zero, U, V, s = (to_np(t) for t in out)
+    assert np.mean(codes == ref["codes"]) >= 0.999
+    Wd = oracle.dequant_int3(codes, scale, zero)
+    err = np.linalg.norm(W.numpy().astype(np.float64) - Wd - U.astype(np.float64) @ V.astype(np.float64))
+    assert abs(err - ref["errors"][-1]) <= 1e-3 * ref["errors"][-1]
+
+
 def test_build_full_size_mixtral_matrix():
     """A Mixtral-shaped gate matrix (14336 x 4096, N(0, 0.02)) at the rank the
     benchmark uses (64, oversampling 16, 2 power iterations): RTN codes
