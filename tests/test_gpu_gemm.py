@@ -48,10 +48,11 @@ def _route(T, E, k, S, seed, skew=None):
 
 
 def _moe_case(E, S, N, K, ranks, T, k, epilogue, path, seed, skew=None, zero_w=False, zero_lr=False,
-              lr_format="fp16"):
+              lr_format="fp16", logits=None, max_rows=None, workspace=None):
     m = _m()
     ET = E + S
-    logits = _route(T, E, k, S, seed, skew)
+    if logits is None:
+        logits = _route(T, E, k, S, seed, skew)
     r = m.route_sort(logits.cuda(), k, S, True)
     ref_r = oracle.route_ref(logits.numpy(), k, S, True)
     slots = k + S
@@ -77,7 +78,8 @@ def _moe_case(E, S, N, K, ranks, T, k, epilogue, path, seed, skew=None, zero_w=F
         y = torch.empty((P, N), dtype=torch.float16, device="cuda")
     m.moe_w3a16_lowrank_gemm(tuple(fams), x.cuda(), r["offsets"], P, epilogue, y,
                              sorted_pairs=r["sorted_pairs"], gather_div=gather, slot_w=r["slot_w"],
-                             y_rows=P, max_rows_per_expert=T, path=path)
+                             y_rows=P, max_rows_per_expert=T if max_rows is None else max_rows, path=path,
+                             workspace=workspace)
     torch.cuda.synchronize()
     got = to_np(y).astype(np.float64)
     xs = x.numpy()
@@ -121,6 +123,35 @@ def test_decode_row_counts(T, path):
     got, want = _moe_case(E=4, S=0, N=128, K=256, ranks=[16, 32, 48, 64], T=T, k=2,
                           epilogue=m.EPI_SWIGLU, path=PATHS[path], seed=T)
     assert_close(got, want, f"{path} T={T}")
+
+
+def _counts_logits(counts, E):
+    """k = 1 logits that send counts[e] consecutive tokens to expert e."""
+    T = sum(counts)
+    logits = torch.randn((T, E), generator=torch.Generator().manual_seed(T))
+    t = 0
+    for e, c in enumerate(counts):
+        logits[t:t + c, e] += 20.0
+        t += c
+    return logits
+
+
+@pytest.mark.parametrize("counts,K,epi,lr", [
+    ([8, 9, 1, 0, 16, 7], 256, "swiglu", "fp16"),
+    ([8, 9, 1, 0, 16, 7], 384, "route", "int3"),
+    ([3, 12], 4096, "swiglu", "fp16"),          # split K with both kinds of expert
+    ([5, 2, 8, 1], 4096, "route", "fp16"),      # split K, stacked experts only
+])
+def test_decode_exact_row_counts(counts, K, epi, lr):
+    """One decode launch over experts with exactly the given row counts
+    (empty, 1, 8, 9, 16 rows; with and without split K)."""
+    m = _m()
+    E = len(counts)
+    epilogue = {"swiglu": m.EPI_SWIGLU, "route": m.EPI_ROUTE_SCALE}[epi]
+    got, want = _moe_case(E=E, S=0, N=128, K=K, ranks=[16, 64, 32, 8, 48, 24][:E], T=sum(counts), k=1,
+                          epilogue=epilogue, path=PATHS["decode"], seed=200 + K, lr_format=lr,
+                          logits=_counts_logits(counts, E), max_rows=max(counts))
+    assert_close(got, want, f"rows {counts} K={K} {epi} {lr}")
 
 
 @pytest.mark.parametrize("T,epi", [(4, "route"), (16, "swiglu"), (30, "route")])
