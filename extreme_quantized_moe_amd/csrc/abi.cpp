@@ -147,16 +147,25 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
   p->pre_tiles = (P + 127) / 128 + d->num_experts;
 
   if (p->dec_mt) {
-    // persistent grid: two blocks per CU; split K
-    // only when the (expert, n-tile) items cannot fill that grid, and keep at
-    // least four K blocks per split (one per wave)
+    // persistent grid: two blocks per CU.  Split K only when it shortens the
+    // busiest block's work (in items) to under 3/4 of the unsplit round: a
+    // split costs a reduce launch, and e.g. 448 items take one round whether
+    // split or not.  Keep at least four K blocks per split (one per wave).
     const int slots = 512;
     const int active = d->num_experts < P ? d->num_experts : P;
     const int items = active * p->n_tiles;
-    int ks = items >= slots ? 1 : (slots + items - 1) / items;
     int ks_max = p->kblocks / 4;
     if (ks_max < 1) ks_max = 1;
-    if (ks > ks_max) ks = ks_max;
+    int ks = 1;
+    const double span1 = (double)((items + slots - 1) / slots);
+    double best = span1;
+    for (int k = 2; k <= ks_max && items < slots; ++k) {
+      const double span = (double)((items * k + slots - 1) / slots) / k;
+      if (span < 0.75 * span1 && span < best) {
+        best = span;
+        ks = k;
+      }
+    }
     p->dec_ksplit = ks;
     p->dec_blocks = items * ks < slots ? items * ks : slots;
   }

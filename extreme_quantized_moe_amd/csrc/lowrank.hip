@@ -85,16 +85,19 @@ __device__ void prepass_aux(const PrepassArgs& a, int base, int m0, int M) {
 
 constexpr int kDotThreads = 512;
 
-// Decode form, fp16 V: block (16-row tile, rank j over all families), 512 threads.
+// Decode form, fp16 V: block (16-row tile, rank j over all families), THREADS
+// threads (256 for K <= 4096: the grid then fits the GPU in one round; 512
+// above, for more loads in flight per row).
 // The rows of the tile are rounded up to R2 (a power of two) and each row gets
-// 512 / R2 consecutive threads, which stride over the 16-byte chunks of V row j
+// THREADS / R2 consecutive threads, which stride over the 16-byte chunks of V row j
 // and of the token row, eight chunks per batch of loads.  The partial sums of a
 // row are reduced in a fixed order: a butterfly inside each wave, then the
 // waves of that row in ascending order.
 constexpr int kDotBatch = 8;
 
-__global__ void __launch_bounds__(kDotThreads) prepass_dot_kernel(PrepassArgs a) {
-  __shared__ float part[kDotThreads / 64];
+template <int THREADS>
+__global__ void __launch_bounds__(THREADS) prepass_dot_kernel(PrepassArgs a) {
+  __shared__ float part[THREADS / 64];
   RowTile rt;
   if (!find_tile16(a, &rt)) return;
   const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
@@ -112,7 +115,7 @@ __global__ void __launch_bounds__(kDotThreads) prepass_dot_kernel(PrepassArgs a)
     return;
   }
   const int R2 = rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : 16;
-  const int G = kDotThreads / R2;                 // threads per row, 32 .. 512
+  const int G = THREADS / R2;                     // threads per row, 16 .. THREADS
   const int r = tid / G, g = tid - r * G;
   const int chunks = a.K / 8;
   float acc = 0.f;
@@ -545,7 +548,8 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
     a.aux_y = aux_blocks ? rank_groups : -1;
     dim3 grid(p.lr_tiles, rank_groups + aux_blocks);
     if (lrq) hipLaunchKernelGGL(prepass_dotq_kernel<kNJ3>, grid, dim3(kDotThreads), 0, st, a);
-    else hipLaunchKernelGGL(prepass_dot_kernel, grid, dim3(kDotThreads), 0, st, a);
+    else if (d->K <= 4096) hipLaunchKernelGGL(prepass_dot_kernel<256>, grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(prepass_dot_kernel<512>, grid, dim3(512), 0, st, a);
     return hip_status(hipGetLastError(), "prepass_dot_kernel launch");
   }
   if (lrq) {

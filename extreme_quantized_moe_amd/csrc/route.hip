@@ -120,7 +120,7 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
   const int tid = threadIdx.x;
   const int t = blockIdx.x * kRouteBlock + tid;
   const int ET = E + S, slots = k + S;
-  for (int x = tid; x < kMaxExperts * kBitWords; x += kRouteBlock) (&bits[0][0])[x] = 0u;
+  for (int x = tid; x < ET * kBitWords; x += kRouteBlock) (&bits[0][0])[x] = 0u;
   __syncthreads();
 
   // per-thread arrays are indexed only by unrolled loop counters (registers)
@@ -189,13 +189,32 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
     for (int w = 0; w < kBitWords; ++w) count += __popc(bits[tid][w]);
   }
   if (gridDim.x == 1) {
-    int total;
-    const int off = block_exclusive_scan(tid < ET ? count : 0, scan_lds, &total);
-    // scan_lds is free again; keep each expert's offset in it
-    if (tid < ET) scan_lds[tid] = off;
-    if (tid == 0) offsets[ET] = total;
-    __syncthreads();
-    if (tid < ET) offsets[tid] = scan_lds[tid];
+    if (ET <= 64) {
+      // one wave scans the expert counts (lane shuffles, no block barriers)
+      if (tid < 64) {
+        const int v = tid < ET ? count : 0;
+        int incl = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int u = __shfl_up(incl, o);
+          if (tid >= o) incl += u;
+        }
+        if (tid < ET) {
+          scan_lds[tid] = incl - v;
+          offsets[tid] = incl - v;
+        }
+        if (tid == 63) offsets[ET] = incl;
+      }
+      __syncthreads();
+    } else {
+      int total;
+      const int off = block_exclusive_scan(tid < ET ? count : 0, scan_lds, &total);
+      // scan_lds is free again; keep each expert's offset in it
+      if (tid < ET) scan_lds[tid] = off;
+      if (tid == 0) offsets[ET] = total;
+      __syncthreads();
+      if (tid < ET) offsets[tid] = scan_lds[tid];
+    }
     if (t < T) {
 #pragma unroll
       for (int j = 0; j < kMaxSlots; ++j) {

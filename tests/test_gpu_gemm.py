@@ -139,8 +139,8 @@ def _counts_logits(counts, E):
 @pytest.mark.parametrize("counts,K,epi,lr", [
     ([8, 9, 1, 0, 16, 7], 256, "swiglu", "fp16"),
     ([8, 9, 1, 0, 16, 7], 384, "route", "int3"),
-    ([3, 12], 4096, "swiglu", "fp16"),          # split K with both kinds of expert
-    ([5, 2, 8, 1], 4096, "route", "fp16"),      # split K, stacked experts only
+    ([3, 12], 4096, "swiglu", "fp16"),          # split K
+    ([5, 2, 8, 1], 4096, "route", "fp16"),      # split K, experts of at most 8 rows
 ])
 def test_decode_exact_row_counts(counts, K, epi, lr):
     """One decode launch over experts with exactly the given row counts
