@@ -5,6 +5,8 @@
 // with fused dequantization; asynchronous global loads overlap memory with
 // compute.  MiLo Algorithm: W_out = W_quant + U V.
 //
+// Grid: x = n-tile groups (fastest), y = 128-row tiles, so the blocks that
+// run together share activation rows (L2 hits) while the weights stream.
 // Block = 128 rows of one expert (pairs in sorted order) x 4 waves.  Each wave
 // owns one 64-wide output tile of one weight family (SWIGLU: waves (W1, W3) x
 // two n-tiles; otherwise four n-tiles of the one family), so every packed
@@ -13,8 +15,9 @@
 // 16 bytes against bank conflicts) and shared by the four waves; the next
 // K block's activations and weights are loaded into registers while the
 // current one is computed.  Weights are dequantized in registers (int3 pair
-// extraction + one fused multiply-add per value in fp32, rounded once to
-// fp16) and multiplied on v_mfma_f32_16x16x32_f16 with fp32 accumulation.
+// extraction, then packed fp16: subtract the offset, one fused multiply-add
+// by the scale with -z s) and multiplied on v_mfma_f32_16x16x32_f16 with fp32
+// accumulation.
 // Epilogue: low-rank term as two more matrix-core K-steps per 32 ranks, then
 // SWIGLU through LDS, or fp16 store, or route-weighted fp32 scatter.
 #include "gemm_common.hpp"
@@ -26,44 +29,72 @@ constexpr int kMT = kBM / 16;            // m-tiles per wave
 constexpr int kXStride = kTileK + 8;     // LDS row stride in halves (272 B)
 constexpr int kXBuf = kBM * kXStride;    // halves per buffer
 
+// Weight dequantization in packed fp16: from the extracted pair h = (off + q)
+// (exact), q = h - off is exact, and (q - z) s = fma(q, s, -z s) with -z s
+// rounded to fp16 once per group: two packed instructions per pair.  Error
+// per weight at most half an fp16 ulp of z s plus half an ulp of the result.
+struct GroupConstPk {
+  f16x2 s, nzs;
+};
+
+// -z s as one fp16 multiply: the product of two fp16 values is exact in fp32,
+// so this is the same correctly rounded value as rounding the fp32 product.
+__device__ __forceinline__ GroupConstPk group_const_pk(uint32_t szword) {
+  const f16x2 sz = __builtin_bit_cast(f16x2, szword);   // (s, z)
+  const _Float16 nz = -(sz[1] * sz[0]);
+  GroupConstPk g;
+  g.s = f16x2{sz[0], sz[0]};
+  g.nzs = f16x2{nz, nz};
+  return g;
+}
+
+__device__ __forceinline__ f16x8 dequant_step_pk(const uint32_t h[16], int step, const GroupConstPk& g) {
+  const f16x2 off64 = {(_Float16)64.f, (_Float16)64.f}, off8 = {(_Float16)8.f, (_Float16)8.f};
+  u32x4 u;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int pi = 4 * step + v;
+    const f16x2 q = __builtin_bit_cast(f16x2, h[pi]) - (pair_offset(pi) == 64 ? off64 : off8);
+    u[v] = __builtin_bit_cast(uint32_t, q * g.s + g.nzs);
+  }
+  return __builtin_bit_cast(f16x8, u);
+}
+
 template <int NW, bool LRQ>
-__global__ void __launch_bounds__(256) gemm_prefill_kernel(GemmArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_prefill_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
   const CodeConsts kc = make_code_consts();
   RowTile rt;
-  if (!find_row_tile(a.offsets, a.num_experts, a.pre_min_rows, kBM, blockIdx.x, a.rp ? a.rank[0] : nullptr,
+  if (!find_row_tile(a.offsets, a.num_experts, a.pre_min_rows, kBM, blockIdx.y, a.rp ? a.rank[0] : nullptr,
                      a.rp ? a.rank[1] : nullptr, &rt))
     return;
   const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
   const int f = (NW == 2) ? (wave & 1) : 0;
-  const int nt = (NW == 2) ? (2 * blockIdx.y + (wave >> 1)) : (4 * blockIdx.y + wave);
+  const int nt = (NW == 2) ? (2 * blockIdx.x + (wave >> 1)) : (4 * blockIdx.x + wave);
   const bool wave_on = nt < a.n_tiles;
 
-  // ---- activation staging: thread loads 8 chunks of 16 B per K block
-  const uint16_t* xsrc[8];
-  int xdst[8];
-  bool xok[8];
+  // ---- activation staging: thread loads 8 chunks of 16 B per K block, rows
+  // (tid / 16) + 16 j, column chunk tid % 16.  Rows past the expert's count
+  // read its first row instead: they only feed output rows that are not stored.
+  int xrow[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int c = tid + 256 * j;
-    const int row = c >> 4, kc = c & 15;
-    const int m = m0 + row;
-    xok[j] = m < M;
-    int xr = 0;
-    if (xok[j]) xr = a.gather_div > 0 ? a.sorted_pairs[base + m] / a.gather_div : base + m;
-    xsrc[j] = a.x + (size_t)xr * a.K + 8 * kc;
-    xdst[j] = row * kXStride + 8 * kc;
+    const int m = m0 + (tid >> 4) + 16 * j;
+    const int i = base + (m < M ? m : m0);
+    xrow[j] = a.gather_div > 0 ? a.sorted_pairs[i] / a.gather_div : i;
   }
+  const uint16_t* xcol = a.x + 8 * (tid & 15);
+  const int xdst = (tid >> 4) * kXStride + 8 * (tid & 15);
   u32x4 xreg[8];
   auto load_x = [&](int kb) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      xreg[j] = xok[j] ? *(const u32x4*)(xsrc[j] + (size_t)kb * kTileK) : u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < 8; ++j) xreg[j] = *(const u32x4*)(xcol + (size_t)xrow[j] * a.K + (size_t)kb * kTileK);
   };
   auto store_x = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *(u32x4*)(lds + buf * kXBuf + xdst[j]) = xreg[j];
+    for (int j = 0; j < 8; ++j) *(u32x4*)(lds + buf * kXBuf + xdst + 16 * j * kXStride) = xreg[j];
   };
 
   // ---- weights of this wave
@@ -94,35 +125,28 @@ __global__ void __launch_bounds__(256) gemm_prefill_kernel(GemmArgs a) {
   const int KB = a.kblocks;
   for (int kb = 0; kb < KB; ++kb) {
     const int buf = kb & 1;
-    // dequantize this K block's weights (registers) before the next loads land
-    f16x8 wf[4][4];
-    if (wave_on) {
+    if (kb + 1 < KB) load_x(kb + 1);
+    const uint16_t* xb = lds + buf * kXBuf + (lane & 15) * kXStride + 8 * (lane >> 4);
+    // K step by K step: dequantize the step's B operands of the four 16-row
+    // sub-tiles, then the m-tiles' products (keeps one step of operands live)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t h[16];
-        extract_triplet(wq[0][i], wq[1][i], wq[2][i], h, kc);
+    for (int s = 0; s < 4; ++s) {
+      if (wave_on) {
+        f16x8 wf[4];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int idx = 2 * i + g;
-          const GroupConst gc = group_const(idx < 4 ? wz[0][idx] : wz[1][idx - 4]);
-          wf[i][2 * g] = dequant_step(h, 2 * g, gc);
-          wf[i][2 * g + 1] = dequant_step(h, 2 * g + 1, gc);
+        for (int i = 0; i < 4; ++i) {
+          uint32_t h[16];
+          extract_triplet(wq[0][i], wq[1][i], wq[2][i], h, kc);
+          const int idx = 2 * i + (s >> 1);
+          const GroupConstPk gc = group_const_pk(idx < 4 ? wz[0][idx] : wz[1][idx - 4]);
+          wf[i] = dequant_step_pk(h, s, gc);
         }
-      }
-    }
-    if (kb + 1 < KB) {
-      load_x(kb + 1);
-      if (wave_on) load_w(kb + 1);
-    }
-    if (wave_on) {
-      const uint16_t* xb = lds + buf * kXBuf + (lane & 15) * kXStride + 8 * (lane >> 4);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
+        if (s == 3 && kb + 1 < KB) load_w(kb + 1);   // the codes of this block are consumed
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
           const f16x8 xa = *(const f16x8*)(xb + mt * 16 * kXStride + 32 * s);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][i] = mfma16x16x32(xa, wf[i][s], acc[mt][i]);
+          for (int i = 0; i < 4; ++i) acc[mt][i] = mfma16x16x32(xa, wf[i], acc[mt][i]);
         }
       }
     }
@@ -222,11 +246,11 @@ int32_t launch_gemm_prefill(const milo_gemm_desc* d, const GemmPlan& p, char* ws
   GemmArgs a = make_gemm_args(d, p, ws);
   const size_t lds_bytes = 2 * kXBuf * sizeof(uint16_t);   // >= 2 x 128 x 64 fp32 for SWIGLU
   if (d->n_w == 2) {
-    dim3 grid(p.pre_tiles, (p.n_tiles + 1) / 2);
+    dim3 grid((p.n_tiles + 1) / 2, p.pre_tiles);
     if (a.lrq) hipLaunchKernelGGL((gemm_prefill_kernel<2, true>), grid, dim3(256), lds_bytes, st, a);
     else hipLaunchKernelGGL((gemm_prefill_kernel<2, false>), grid, dim3(256), lds_bytes, st, a);
   } else {
-    dim3 grid(p.pre_tiles, (p.n_tiles + 3) / 4);
+    dim3 grid((p.n_tiles + 3) / 4, p.pre_tiles);
     if (a.lrq) hipLaunchKernelGGL((gemm_prefill_kernel<1, true>), grid, dim3(256), lds_bytes, st, a);
     else hipLaunchKernelGGL((gemm_prefill_kernel<1, false>), grid, dim3(256), lds_bytes, st, a);
   }
