@@ -35,8 +35,18 @@ template <int NE>
 __device__ __forceinline__ void topk_regs(const float* row, int E, int k, float (&bv)[kMaxK],
                                           int (&bi)[kMaxK], float& mx, float& den) {
   float v[NE];
+  if (E == NE && ((uintptr_t)row & 15) == 0) {
+    // whole 16-byte vectors: a quarter of the cache-line requests of scalar
+    // loads (the rows of neighbouring threads are E floats apart)
 #pragma unroll
-  for (int e = 0; e < NE; ++e) v[e] = e < E ? row[e] : -INFINITY;
+    for (int e = 0; e < NE; e += 4) {
+      const float4 q = *(const float4*)(row + e);
+      v[e] = q.x, v[e + 1] = q.y, v[e + 2] = q.z, v[e + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) v[e] = e < E ? row[e] : -INFINITY;
+  }
   mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < NE; ++e)
@@ -189,32 +199,37 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
     for (int w = 0; w < kBitWords; ++w) count += __popc(bits[tid][w]);
   }
   if (gridDim.x == 1) {
-    if (ET <= 64) {
-      // one wave scans the expert counts (lane shuffles, no block barriers)
-      if (tid < 64) {
-        const int v = tid < ET ? count : 0;
-        int incl = v;
+    // one wave scans the expert counts (ET <= 256: four experts per lane,
+    // then lane shuffles); scan_lds ends up holding each expert's offset
+    if (tid < ET) scan_lds[tid] = count;
+    __syncthreads();
+    if (tid < 64) {
+      int c[4], lsum = 0;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int u = __shfl_up(incl, o);
-          if (tid >= o) incl += u;
-        }
-        if (tid < ET) {
-          scan_lds[tid] = incl - v;
-          offsets[tid] = incl - v;
-        }
-        if (tid == 63) offsets[ET] = incl;
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * tid + q;
+        c[q] = e < ET ? scan_lds[e] : 0;
+        lsum += c[q];
       }
-      __syncthreads();
-    } else {
-      int total;
-      const int off = block_exclusive_scan(tid < ET ? count : 0, scan_lds, &total);
-      // scan_lds is free again; keep each expert's offset in it
-      if (tid < ET) scan_lds[tid] = off;
-      if (tid == 0) offsets[ET] = total;
-      __syncthreads();
-      if (tid < ET) offsets[tid] = scan_lds[tid];
+      int incl = lsum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o);
+        if (tid >= o) incl += u;
+      }
+      int run = incl - lsum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * tid + q;
+        if (e < ET) {
+          scan_lds[e] = run;
+          offsets[e] = run;
+        }
+        run += c[q];
+      }
+      if (tid == 63) offsets[ET] = incl;
     }
+    __syncthreads();
     if (t < T) {
 #pragma unroll
       for (int j = 0; j < kMaxSlots; ++j) {

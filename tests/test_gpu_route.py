@@ -32,7 +32,8 @@ def test_route_configs(cfg):
 
 @pytest.mark.parametrize("T,E,k,S,renorm", [
     (1, 8, 2, 0, True), (257, 8, 2, 0, True), (255, 64, 6, 2, False), (513, 256, 8, 0, True),
-    (1000, 16, 1, 1, False), (300, 240, 8, 8, True)])
+    (1000, 16, 1, 1, False), (300, 240, 8, 8, True),
+    (200, 250, 4, 6, True), (50, 12, 3, 1, False), (256, 32, 4, 0, False)])
 def test_route_shapes(T, E, k, S, renorm):
     g = torch.Generator().manual_seed(T * 7 + E)
     _check(torch.randn((T, E), generator=g), k, S, renorm)
