@@ -6,7 +6,8 @@
 // the pages; this is the usual softmax top-k (ties -> lower expert id).
 //
 // Three phases, each deterministic:
-//   1. route_topk  (one thread per token, 256 tokens per block): top-k,
+//   1. route_topk  (one thread per token up to 16 experts, four above;
+//      256 tokens per block): top-k,
 //      weights, and per-block stable ranks of each slot among the slots of the
 //      same expert, from an LDS bitmap [expert][token-in-block].
 //   2. route_scan  (one block): per expert, exclusive prefix of the block
@@ -17,7 +18,7 @@
 
 namespace milo {
 
-constexpr int kRouteBlock = 256;
+constexpr int kRouteBlock = 256;                 // tokens per block
 constexpr int kMaxExperts = 256;
 constexpr int kBitWords = kRouteBlock / 32;
 constexpr int kMaxK = 8;
@@ -27,10 +28,10 @@ __device__ __forceinline__ int slot_expert(const int32_t* ids_row, int j, int k,
   return j < k ? ids_row[j] : E + (j - k);
 }
 
-// Top-k of one token's logits: k passes, pass j picks the largest logit (lowest
-// id on ties) among the experts not picked before; also the row maximum and
-// the softmax denominator.  Up to 64 experts the row is held in registers
-// (NE >= E; all loads issued at once); beyond that it is re-read per pass.
+// Top-k of one token's logits by one thread (up to 16 experts): k passes,
+// pass j picks the largest logit (lowest id on ties) among the experts not
+// picked before; also the row maximum and the softmax denominator.  The row
+// is held in registers (NE >= E; all loads issued at once).
 template <int NE>
 __device__ __forceinline__ void topk_regs(const float* row, int E, int k, float (&bv)[kMaxK],
                                           int (&bi)[kMaxK], float& mx, float& den) {
@@ -78,29 +79,104 @@ __device__ __forceinline__ void topk_regs(const float* row, int E, int k, float 
     if (e < E) den += expf(v[e] - mx);
 }
 
-__device__ __forceinline__ void topk_loop(const float* row, int E, int k, float (&bv)[kMaxK],
-                                       int (&bi)[kMaxK], float& mx, float& den) {
-  mx = -INFINITY;
-  for (int e = 0; e < E; ++e) mx = fmaxf(mx, row[e]);
+// Top-k of one token's logits by its LANES threads (1 or 4).  Thread q of
+// the token holds experts [q NL, (q + 1) NL) in registers (16-byte loads when
+// the row is whole vectors: the threads read the row contiguously), takes its
+// own top-k (k passes, strictly greater replaces, so ties keep the lower id),
+// and with four threads the sorted lists are merged k times by a max over the
+// four (larger value, then lower id), the winner dropping its head.  The
+// softmax denominator: each thread's sum of exp(v - max) over its experts,
+// then (with four) the partial sums as (t0 + t1) + (t2 + t3).
+template <int LANES, int NL>
+__device__ __forceinline__ void topk_lanes(const float* row, int E, int k, int q, float (&bv)[kMaxK],
+                                           int (&bi)[kMaxK], float& den) {
+  float v[NL];
+  const int e0 = q * NL;
+  if (E == LANES * NL && NL % 4 == 0 && ((uintptr_t)row & 15) == 0) {
+#pragma unroll
+    for (int e = 0; e < NL; e += 4) {
+      const float4 x = *(const float4*)(row + e0 + e);
+      v[e] = x.x, v[e + 1] = x.y, v[e + 2] = x.z, v[e + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < NL; ++e) v[e] = e0 + e < E ? row[e0 + e] : -INFINITY;
+  }
+  // own list, best first; entries past the own experts are (-inf, E + 1)
+  float lv[kMaxK];
+  int li[kMaxK];
+  uint64_t taken = 0;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
-    bv[j] = -INFINITY;
-    bi[j] = -1;
+    lv[j] = -INFINITY;
+    li[j] = E + 1;
     if (j < k) {
-      for (int e = 0; e < E; ++e) {
-        bool taken = false;
+      int bidx = -1;
+      float best = -INFINITY;
 #pragma unroll
-        for (int jj = 0; jj < j; ++jj) taken |= (bi[jj] == e);
-        const float v = row[e];
-        if (!taken && (bi[j] < 0 || v > bv[j])) {
-          bv[j] = v;
-          bi[j] = e;
+      for (int e = 0; e < NL; ++e) {
+        const bool ok = e0 + e < E && !((taken >> e) & 1ull);
+        if (ok && (bidx < 0 || v[e] > best)) {
+          best = v[e];
+          bidx = e;
         }
+      }
+      if (bidx >= 0) {
+        lv[j] = best;
+        li[j] = e0 + bidx;
+        taken |= 1ull << bidx;
       }
     }
   }
-  den = 0.f;
-  for (int e = 0; e < E; ++e) den += expf(row[e] - mx);
+  if constexpr (LANES == 1) {
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      bv[j] = j < k ? lv[j] : -INFINITY;
+      bi[j] = j < k ? li[j] : -1;
+    }
+  }
+  // merge the four lists
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (LANES == 1) break;
+    bv[j] = -INFINITY;
+    bi[j] = -1;
+    if (j < k) {
+      float cv = lv[0];
+      int ci = li[0];
+#pragma unroll
+      for (int o = 1; o <= 2; o <<= 1) {
+        const float ov = __shfl_xor(cv, o);
+        const int oi = __shfl_xor(ci, o);
+        if (ov > cv || (ov == cv && oi < ci)) {
+          cv = ov;
+          ci = oi;
+        }
+      }
+      bv[j] = cv;
+      bi[j] = ci;
+      const bool mine = li[0] == ci;
+#pragma unroll
+      for (int u = 0; u + 1 < kMaxK; ++u) {
+        lv[u] = mine ? lv[u + 1] : lv[u];
+        li[u] = mine ? li[u + 1] : li[u];
+      }
+      if (mine) {
+        lv[kMaxK - 1] = -INFINITY;
+        li[kMaxK - 1] = E + 1;
+      }
+    }
+  }
+  const float mx = bv[0];
+  float part = 0.f;
+#pragma unroll
+  for (int e = 0; e < NL; ++e)
+    if (e0 + e < E) part += expf(v[e] - mx);
+  if (LANES == 4) {
+    part += __shfl_xor(part, 1);
+    part += __shfl_xor(part, 2);
+  }
+  den = part;
 }
 
 // Block-wide exclusive scan of one int per thread (blockDim == 256).
@@ -120,7 +196,8 @@ __device__ int block_exclusive_scan(int v, int* lds, int* total) {
   return incl - v;
 }
 
-__global__ void __launch_bounds__(kRouteBlock)
+template <int LANES>
+__global__ void __launch_bounds__(LANES * kRouteBlock)
 route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int renorm,
            int32_t* __restrict__ ids, float* __restrict__ topw, float* __restrict__ slot_w,
            int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
@@ -128,12 +205,14 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
   __shared__ uint32_t bits[kMaxExperts][kBitWords];
   __shared__ int scan_lds[kRouteBlock];
   const int tid = threadIdx.x;
-  const int t = blockIdx.x * kRouteBlock + tid;
+  const int tl = tid / LANES, q = tid % LANES;    // token in block, its thread
+  const int t = blockIdx.x * kRouteBlock + tl;
   const int ET = E + S, slots = k + S;
-  for (int x = tid; x < ET * kBitWords; x += kRouteBlock) (&bits[0][0])[x] = 0u;
+  for (int x = tid; x < ET * kBitWords; x += LANES * kRouteBlock) (&bits[0][0])[x] = 0u;
   __syncthreads();
 
-  // per-thread arrays are indexed only by unrolled loop counters (registers)
+  // per-thread arrays are indexed only by unrolled loop counters (registers);
+  // slot j of a token is handled by its thread j % LANES
   int my_ids[kMaxSlots];
   int rank[kMaxSlots];
 #pragma unroll
@@ -141,16 +220,25 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
     my_ids[j] = 0;
     rank[j] = 0;
   }
-  if (t < T) {
+  const bool live = t < T;
+  if (live) {
+    // the LANES threads of a token are all live or all not, so the shuffles
+    // inside topk_lanes only read live threads
     const float* row = logits + (size_t)t * E;
     float bv[kMaxK];
     int bi[kMaxK];
-    float mx, den;
-    if (E <= 8) topk_regs<8>(row, E, k, bv, bi, mx, den);
-    else if (E <= 16) topk_regs<16>(row, E, k, bv, bi, mx, den);
-    else if (E <= 32) topk_regs<32>(row, E, k, bv, bi, mx, den);
-    else if (E <= 64) topk_regs<64>(row, E, k, bv, bi, mx, den);
-    else topk_loop(row, E, k, bv, bi, mx, den);
+    float den;
+    float mx1 = 0.f;
+    if constexpr (LANES == 1) {
+      if (E <= 8) topk_regs<8>(row, E, k, bv, bi, mx1, den);
+      else topk_regs<16>(row, E, k, bv, bi, mx1, den);
+    } else {
+      if (E <= 32) topk_lanes<4, 8>(row, E, k, q, bv, bi, den);
+      else if (E <= 64) topk_lanes<4, 16>(row, E, k, q, bv, bi, den);
+      else if (E <= 128) topk_lanes<4, 32>(row, E, k, q, bv, bi, den);
+      else topk_lanes<4, 64>(row, E, k, q, bv, bi, den);
+    }
+    const float mx = bv[0];
     float sel[kMaxK];
     float selsum = 0.f;
 #pragma unroll
@@ -161,35 +249,37 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
       if (j < k) {
-        const float w = renorm ? sel[j] / selsum : sel[j] / den;
-        ids[(size_t)t * k + j] = bi[j];
-        topw[(size_t)t * k + j] = w;
-        slot_w[(size_t)t * slots + j] = w;
         my_ids[j] = bi[j];
+        if (j % LANES == q) {
+          const float w = renorm ? sel[j] / selsum : sel[j] / den;
+          ids[(size_t)t * k + j] = bi[j];
+          topw[(size_t)t * k + j] = w;
+          slot_w[(size_t)t * slots + j] = w;
+        }
       }
     }
 #pragma unroll
     for (int j = 0; j < kMaxSlots; ++j) {
       if (j >= k && j < slots) {
         my_ids[j] = E + (j - k);
-        slot_w[(size_t)t * slots + j] = 1.0f;
+        if (j % LANES == q) slot_w[(size_t)t * slots + j] = 1.0f;
       }
     }
 #pragma unroll
     for (int j = 0; j < kMaxSlots; ++j)
-      if (j < slots) atomicOr(&bits[my_ids[j]][tid >> 5], 1u << (tid & 31));
+      if (j < slots && j % LANES == q) atomicOr(&bits[my_ids[j]][tl >> 5], 1u << (tl & 31));
   }
   __syncthreads();
 
   // stable rank of each slot among earlier tokens of this block with the same expert
-  if (t < T) {
+  if (live) {
 #pragma unroll
     for (int j = 0; j < kMaxSlots; ++j) {
-      if (j < slots) {
+      if (j < slots && j % LANES == q) {
         const uint32_t* brow = bits[my_ids[j]];
         int c = 0;
-        for (int w = 0; w < (tid >> 5); ++w) c += __popc(brow[w]);
-        c += __popc(brow[tid >> 5] & ((1u << (tid & 31)) - 1u));
+        for (int w = 0; w < (tl >> 5); ++w) c += __popc(brow[w]);
+        c += __popc(brow[tl >> 5] & ((1u << (tl & 31)) - 1u));
         rank[j] = c;
       }
     }
@@ -199,41 +289,60 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
     for (int w = 0; w < kBitWords; ++w) count += __popc(bits[tid][w]);
   }
   if (gridDim.x == 1) {
-    // one wave scans the expert counts (ET <= 256: four experts per lane,
-    // then lane shuffles); scan_lds ends up holding each expert's offset
-    if (tid < ET) scan_lds[tid] = count;
-    __syncthreads();
-    if (tid < 64) {
-      int c[4], lsum = 0;
+    // one wave scans the expert counts with lane shuffles (up to 64 experts
+    // straight from the counting threads, up to 256 four per lane through
+    // LDS); scan_lds ends up holding each expert's offset
+    if (ET <= 64) {
+      if (tid < 64) {
+        const int v = tid < ET ? count : 0;
+        int incl = v;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = 4 * tid + q;
-        c[q] = e < ET ? scan_lds[e] : 0;
-        lsum += c[q];
-      }
-      int incl = lsum;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(incl, o);
-        if (tid >= o) incl += u;
-      }
-      int run = incl - lsum;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = 4 * tid + q;
-        if (e < ET) {
-          scan_lds[e] = run;
-          offsets[e] = run;
+        for (int o = 1; o < 64; o <<= 1) {
+          const int u = __shfl_up(incl, o);
+          if (tid >= o) incl += u;
         }
-        run += c[q];
+        if (tid < ET) {
+          scan_lds[tid] = incl - v;
+          offsets[tid] = incl - v;
+        }
+        if (tid == 63) offsets[ET] = incl;
       }
-      if (tid == 63) offsets[ET] = incl;
+      __syncthreads();
+    } else {
+      if (tid < ET) scan_lds[tid] = count;
+      __syncthreads();
+      if (tid < 64) {
+        int c[4], lsum = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int e = 4 * tid + u;
+          c[u] = e < ET ? scan_lds[e] : 0;
+          lsum += c[u];
+        }
+        int incl = lsum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int v = __shfl_up(incl, o);
+          if (tid >= o) incl += v;
+        }
+        int run = incl - lsum;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int e = 4 * tid + u;
+          if (e < ET) {
+            scan_lds[e] = run;
+            offsets[e] = run;
+          }
+          run += c[u];
+        }
+        if (tid == 63) offsets[ET] = incl;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (t < T) {
+    if (live) {
 #pragma unroll
       for (int j = 0; j < kMaxSlots; ++j) {
-        if (j < slots) {
+        if (j < slots && j % LANES == q) {
           const int s = t * slots + j;
           const int pos = scan_lds[my_ids[j]] + rank[j];
           sorted_pairs[pos] = s;
@@ -243,10 +352,10 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
     }
   } else {
     if (tid < ET) block_counts[(size_t)blockIdx.x * ET + tid] = count;
-    if (t < T) {
+    if (live) {
 #pragma unroll
       for (int j = 0; j < kMaxSlots; ++j)
-        if (j < slots) pair_pos[t * slots + j] = rank[j];
+        if (j < slots && j % LANES == q) pair_pos[t * slots + j] = rank[j];
     }
   }
 }
@@ -290,8 +399,13 @@ int32_t launch_route(const float* logits, int T, int E, int k, int S, int renorm
                      int32_t* pair_pos, int32_t* offsets, void* ws, hipStream_t st) {
   const int nblocks = (T + kRouteBlock - 1) / kRouteBlock;
   int32_t* counts = (int32_t*)ws;
-  hipLaunchKernelGGL(route_topk, dim3(nblocks), dim3(kRouteBlock), 0, st, logits, T, E, k, S,
-                     renorm, ids, w, slot_w, sorted_pairs, pair_pos, offsets, counts);
+  // one thread per token up to 16 experts, four above (shorter selection chains)
+  if (E <= 16)
+    hipLaunchKernelGGL(route_topk<1>, dim3(nblocks), dim3(kRouteBlock), 0, st, logits, T, E, k, S, renorm, ids,
+                       w, slot_w, sorted_pairs, pair_pos, offsets, counts);
+  else
+    hipLaunchKernelGGL(route_topk<4>, dim3(nblocks), dim3(4 * kRouteBlock), 0, st, logits, T, E, k, S, renorm,
+                       ids, w, slot_w, sorted_pairs, pair_pos, offsets, counts);
   int32_t rc = hip_status(hipGetLastError(), "route_topk launch");
   if (rc != MILO_OK || nblocks == 1) return rc;
   hipLaunchKernelGGL(route_scan, dim3(1), dim3(kRouteBlock), 0, st, nblocks, E + S, counts, offsets);
