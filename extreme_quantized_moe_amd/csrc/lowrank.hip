@@ -26,6 +26,8 @@
 
 namespace milo {
 
+constexpr int kPrepassMT = 4;   // m-tiles per block of the fp16 prefill pre-pass for large experts
+
 struct PrepassArgs {
   const uint16_t* x;
   const int32_t* sorted_pairs;
@@ -319,27 +321,34 @@ __global__ void __launch_bounds__(kDotThreads) prepass_dotq_kernel(PrepassArgs a
   dot_reduce_store<NJ>(acc, b.G, b.rows, b.tout, b.RW, part);
 }
 
-template <int NRT, int NWAVES, int UNR>
+template <int NRT, int NWAVES, int UNR, int MT>
 __global__ void __launch_bounds__(64 * NWAVES) prepass_kernel(PrepassArgs a) {
-  __shared__ float red[NWAVES][NRT][64][4];
+  __shared__ float red[NWAVES][MT][NRT][64][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   RowTile rt;
-  if (!find_tile16(a, &rt)) return;
+  if (!find_row_tile(a.offsets, a.num_experts, 0, 16 * MT, blockIdx.x, a.rp ? a.rank[0] : nullptr,
+                     a.rp ? a.rank[1] : nullptr, &rt))
+    return;
   const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
   if ((int)blockIdx.y == a.aux_y) {
-    prepass_aux(a, base, m0, M);
+    for (int g = m0; g < M && g < m0 + 16 * MT; g += 16) prepass_aux(a, base, g, M);
     return;
   }
   const int RW = a.n_w * a.rp;
   const int tiles_per_w = a.rp / 16;
   const int tr0 = blockIdx.y * NRT;            // first rank tile of this block
 
-  // A operand row of this lane
-  const int m = m0 + (lane & 15);
-  const bool row_ok = m < M;
-  int xr = 0;
-  if (row_ok) xr = a.gather_div > 0 ? a.sorted_pairs[base + m] / a.gather_div : base + m;
-  const uint16_t* xp = a.x + (size_t)xr * a.K + 8 * (lane >> 4);
+  // A operand rows of this lane, one per 16-row m-tile
+  const uint16_t* xp[MT];
+  bool row_ok[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = m0 + 16 * mt + (lane & 15);
+    row_ok[mt] = m < M;
+    int xr = 0;
+    if (row_ok[mt]) xr = a.gather_div > 0 ? a.sorted_pairs[base + m] / a.gather_div : base + m;
+    xp[mt] = a.x + (size_t)xr * a.K + 8 * (lane >> 4);
+  }
 
   // B operand rows (compensator ranks) of this lane, per rank tile
   const uint16_t* vp[NRT];
@@ -355,21 +364,25 @@ __global__ void __launch_bounds__(64 * NWAVES) prepass_kernel(PrepassArgs a) {
     vp[t] = a.V[f] + ((size_t)e * a.max_rank + (vok[t] ? j : 0)) * a.K + 8 * (lane >> 4);
   }
 
-  f32x4 acc[NRT];
+  f32x4 acc[MT][NRT];
 #pragma unroll
-  for (int t = 0; t < NRT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < NRT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // K steps s = wave + NWAVES i, in batches of UNR steps whose loads are all
   // issued before the first product (steps past the end are skipped)
   const int ksteps = a.K / 32;
   if (any) {
     for (int s0 = wave; s0 < ksteps; s0 += UNR * NWAVES) {
-      f16x8 xa[UNR], vb[UNR][NRT];
+      f16x8 xa[UNR][MT], vb[UNR][NRT];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int s = s0 + NWAVES * u;
         const bool in = s < ksteps;
-        xa[u] = (in && row_ok) ? *(const f16x8*)(xp + 32 * s) : f16x8{};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          xa[u][mt] = (in && row_ok[mt]) ? *(const f16x8*)(xp[mt] + 32 * s) : f16x8{};
 #pragma unroll
         for (int t = 0; t < NRT; ++t)
           vb[u][t] = (in && vok[t]) ? *(const f16x8*)(vp[t] + 32 * s) : f16x8{};
@@ -377,21 +390,25 @@ __global__ void __launch_bounds__(64 * NWAVES) prepass_kernel(PrepassArgs a) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u)
 #pragma unroll
-        for (int t = 0; t < NRT; ++t) acc[t] = mfma16x16x32(xa[u], vb[u][t], acc[t]);
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int t = 0; t < NRT; ++t) acc[mt][t] = mfma16x16x32(xa[u][mt], vb[u][t], acc[mt][t]);
     }
   }
 #pragma unroll
-  for (int t = 0; t < NRT; ++t)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][t][lane][r] = acc[t][r];
+    for (int t = 0; t < NRT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][mt][t][lane][r] = acc[mt][t][r];
   __syncthreads();
 
-  for (int o = threadIdx.x; o < NRT * 256; o += 64 * NWAVES) {
-    const int t = o >> 8, ln = (o >> 2) & 63, r = o & 3;
+  for (int o = threadIdx.x; o < MT * NRT * 256; o += 64 * NWAVES) {
+    const int mt = o / (NRT * 256), t = (o >> 8) % NRT, ln = (o >> 2) & 63, r = o & 3;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < NWAVES; ++w) v += red[w][t][ln][r];
-    const int row = 4 * (ln >> 4) + r;            // 0..15 within the tile
+    for (int w = 0; w < NWAVES; ++w) v += red[w][mt][t][ln][r];
+    const int row = 16 * mt + 4 * (ln >> 4) + r;  // within the tile
     const int col = (tr0 + t) * 16 + (ln & 15);   // 0..RW-1
     if (m0 + row < M) a.T[(size_t)(base + m0 + row) * RW + col] = float_to_half_bits(v);
   }
@@ -565,14 +582,26 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
     return hip_status(hipGetLastError(), "prepass_q_kernel launch");
   }
   {
-    dim3 grid(p.lr_tiles, rank_blocks + aux_blocks);
-    switch (per) {
-      case 2: hipLaunchKernelGGL((prepass_kernel<2, 4, 4>), grid, dim3(256), 0, st, a); break;
-      case 4: hipLaunchKernelGGL((prepass_kernel<4, 4, 4>), grid, dim3(256), 0, st, a); break;
-      case 8: hipLaunchKernelGGL((prepass_kernel<8, 4, 4>), grid, dim3(256), 0, st, a); break;
-      default:
-        set_error("internal: unsupported rank-tile count %d", per);
-        return MILO_ERR_RANK;
+    // row tiles of 16 MT rows (MT m-tiles per block, so each V row is read
+    // once per 16 MT pairs) x groups of at most four 16-rank tiles.  MT = 4
+    // where experts average 128 rows or more, else 1 (small experts would
+    // waste most of a 64-row tile, and the grid would be sparse)
+    const int tpb = per < 4 ? per : 4;
+    const bool big = d->num_pairs >= 128 * d->num_experts;
+    const int mt = big ? kPrepassMT : 1;
+    const int tiles = (d->num_pairs + 16 * mt - 1) / (16 * mt) + d->num_experts;
+    a.aux_y = aux_blocks ? nrt / tpb : -1;
+    dim3 grid(tiles, nrt / tpb + aux_blocks);
+    if (tpb != 2 && tpb != 4) {
+      set_error("internal: unsupported rank-tile count %d", per);
+      return MILO_ERR_RANK;
+    }
+    if (big) {
+      if (tpb == 2) hipLaunchKernelGGL((prepass_kernel<2, 4, 2, kPrepassMT>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((prepass_kernel<4, 4, 2, kPrepassMT>), grid, dim3(256), 0, st, a);
+    } else {
+      if (tpb == 2) hipLaunchKernelGGL((prepass_kernel<2, 4, 4, 1>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((prepass_kernel<4, 4, 4, 1>), grid, dim3(256), 0, st, a);
     }
   }
   return hip_status(hipGetLastError(), "prepass_kernel launch");
