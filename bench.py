@@ -354,17 +354,22 @@ def main():
     global TIMER
     TIMER = HipTimer()
     evs = [(TIMER.event(), TIMER.event()) for _ in range(args.steps)]
+    marks = [TIMER.event() for _ in range(args.steps + 1)]   # step boundaries
     start, stop = TIMER.event(), TIMER.event()
     torch.cuda.synchronize()
     t_host = time.perf_counter()
     TIMER.record(start, stream)
+    TIMER.record(marks[0], stream)
     for i in range(args.steps):
         run_step(i, evs[i])
+        TIMER.record(marks[i + 1], stream)
     TIMER.record(stop, stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
     ms_total = TIMER.ms(start, stop)
     ms_step = ms_total / args.steps
+    step_ms = sorted(TIMER.ms(marks[i], marks[i + 1]) for i in range(args.steps))
+    pct = lambda q: step_ms[min(len(step_ms) - 1, int(q * (len(step_ms) - 1) + 0.5))]
     k13_us = sum(TIMER.ms(a, b) for a, b in evs) / len(evs) * 1000.0
 
     # work accounting (after the timed region)
@@ -419,6 +424,7 @@ def main():
             "achieved_TBps_step": round(layer_bytes / (ms_step * 1e-3) / 1e12, 3),
             "achieved_TFLOPs_step": round(layer_flops / (ms_step * 1e-3) / 1e12, 2),
             "host_seconds_timed": round(t_host, 3),
+            "step_ms_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
             "path": args.path,
             "compensator_factors": args.lr,
         },

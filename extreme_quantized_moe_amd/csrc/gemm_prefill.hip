@@ -28,6 +28,8 @@ constexpr int kBM = 128;                 // rows per block
 constexpr int kMT = kBM / 16;            // m-tiles per wave
 constexpr int kXStride = kTileK + 8;     // LDS row stride in halves (272 B)
 constexpr int kXBuf = kBM * kXStride;    // halves per buffer
+constexpr int kExStride = 68;            // floats per row of the SwiGLU exchange
+static_assert(2 * kBM * kExStride * 4 <= 2 * kXBuf * 2, "exchange must fit the staging LDS");
 
 // Weight dequantization in packed fp16: from the extracted pair h = (off + q)
 // (exact), q = h - off is exact, and (q - z) s = fma(q, s, -z s) with -z s
@@ -190,7 +192,9 @@ gemm_prefill_kernel(GemmArgs a) {
   // ---- epilogue
   if (NW == 2) {
     // waves with f == 1 (W3) hand their tile to the partner wave (wave - 1)
-    float* ex = (float*)lds + (wave >> 1) * (kBM * 64);
+    // rows padded to kExStride floats: the four row groups of a wave's
+    // accumulators then fall on different LDS banks
+    float* ex = (float*)lds + (wave >> 1) * (kBM * kExStride);
     if (wave_on && f == 1) {
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt)
@@ -198,7 +202,7 @@ gemm_prefill_kernel(GemmArgs a) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            ex[(mt * 16 + 4 * (lane >> 4) + r) * 64 + 16 * i + (lane & 15)] = acc[mt][i][r];
+            ex[(mt * 16 + 4 * (lane >> 4) + r) * kExStride + 16 * i + (lane & 15)] = acc[mt][i][r];
     }
     __syncthreads();
     if (!wave_on || f == 1) return;
@@ -212,7 +216,7 @@ gemm_prefill_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int n = 16 * i + (lane & 15);
-          const float h3 = ex[mm * 64 + n];
+          const float h3 = ex[mm * kExStride + n];
           yrow[n] = float_to_half_bits(silu(acc[mt][i][r]) * h3);
         }
       }
