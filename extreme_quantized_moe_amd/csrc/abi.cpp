@@ -244,8 +244,8 @@ int32_t milo_quantize_hqq_int3(const float* W, int64_t rows, int64_t K, int32_t 
   if (iters < 0 || iters > 1000 || !(p_norm > 0.0 && p_norm <= 1.0) || !(beta > 0.0) || !(kappa >= 1.0))
     MILO_FAIL(MILO_ERR_ARG, "iters=%d p=%g beta=%g kappa=%g: need 0 <= iters <= 1000, 0 < p <= 1, beta > 0, "
               "kappa >= 1", iters, p_norm, beta, kappa);
-  if (!aligned(W, 4) || !aligned(scale, 2) || !aligned(zero, 2))
-    MILO_FAIL(MILO_ERR_ALIGN, "W must be 4-byte and scale/zero 2-byte aligned");
+  if (!aligned(W, 16) || !aligned(codes, 8) || !aligned(scale, 2) || !aligned(zero, 2))
+    MILO_FAIL(MILO_ERR_ALIGN, "W must be 16-byte, codes 8-byte and scale/zero 2-byte aligned");
   return launch_hqq(W, rows, K, iters, p_norm, beta, kappa, codes, scale, zero, (hipStream_t)stream);
 }
 

@@ -129,8 +129,13 @@ __global__ void __launch_bounds__(256) pack_kernel(const uint8_t* __restrict__ c
 
 // Sum over the 64 lanes of a wave; the xor butterfly adds the same pairs in
 // every lane, so all lanes hold the identical sum.
-// DPP move of a double (both halves) within rows of 16 lanes; CTRL is a
-// permutation that stays inside the row, so every lane has a source.
+// DPP move of a 32-bit value / a double (both halves) inside rows of 16
+// lanes; CTRL is a permutation that stays inside the row, so every lane has
+// a source.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
   const uint64_t b = (uint64_t)__double_as_longlong(v);
@@ -139,37 +144,40 @@ __device__ __forceinline__ double dpp_f64(double v) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-__device__ __forceinline__ double lane_f64(double v, int lane) {
-  const uint64_t b = (uint64_t)__double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-
-// Sum over the 64 lanes of a wave, the same value in every lane, in a fixed
-// order: pairs, quads, eights and sixteens inside each row by DPP
-// (swap neighbours, swap pairs, half-row mirror, row mirror -- each step adds
-// two equal partial sums in either order, so all lanes of a row agree), then
-// (row0 + row1) + (row2 + row3).
-__device__ __forceinline__ double wave_sum(double v) {
+// Sum over the 8 lanes of an aligned lane group, the same value in all of
+// them, in a fixed order: swap neighbours, swap pairs, half-row mirror (each
+// step adds two equal partial sums in either order).
+__device__ __forceinline__ double sum8(double v) {
   v += dpp_f64<0xB1>(v);    // quad_perm [1, 0, 3, 2]
   v += dpp_f64<0x4E>(v);    // quad_perm [2, 3, 0, 1]
   v += dpp_f64<0x141>(v);   // row_half_mirror
-  v += dpp_f64<0x140>(v);   // row_mirror
-  return (lane_f64(v, 0) + lane_f64(v, 16)) + (lane_f64(v, 32) + lane_f64(v, 48));
+  return v;
+}
+__device__ __forceinline__ float min8(float v) {
+  v = fminf(v, dpp_f32<0xB1>(v));
+  v = fminf(v, dpp_f32<0x4E>(v));
+  return fminf(v, dpp_f32<0x141>(v));
+}
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  return fmaxf(v, dpp_f32<0x141>(v));
 }
 
 // Code of a weight at zero point z given ws = w / s (the division is taken
 // once per weight: codes depend on w / s + z only).
 __device__ __forceinline__ double code_at(double ws, double z) { return fmin(fmax(rint(ws + z), 0.0), 7.0); }
 
-// HQQ-style zero-point optimization of each group of 64 (one wave per
-// (row, group), lane = column), float64: start from the RTN scale and zero
-// point; each iteration quantizes with the current zero point z, takes the
-// generalized soft threshold of the error, sum-of-lanes update
+// HQQ-style zero-point optimization of each group of 64, float64: start from
+// the RTN scale and zero point; each iteration quantizes with the current
+// zero point z, takes the generalized soft threshold of the error, updates
 // z = mean(q - (w - W_e) / s), beta *= kappa; the fp16 candidate f16(z) is
 // scored by the group's mean absolute error with codes chosen at it, and the
 // best candidate (the RTN zero point first) is kept.
+//
+// Eight lanes per group, eight consecutive weights per lane (a wave holds
+// eight groups; 32-byte loads, 8-byte code stores); group sums are the lane's
+// sum of its eight terms in order, then the 8-lane tree above.
 //
 // The threshold is zero unless |x|^(2-p) > 1 / beta, so for |x| at most half
 // of beta_last^(-1 / (2 - p)) (beta_last the largest beta used; beta never
@@ -180,55 +188,81 @@ __global__ void __launch_bounds__(256) hqq_kernel(const float* __restrict__ W, i
                                                   int iters, double p, double beta, double kappa,
                                                   uint8_t* __restrict__ codes, uint16_t* __restrict__ scale,
                                                   uint16_t* __restrict__ zero) {
-  const int lane = threadIdx.x & 63;
+  const int l8 = threadIdx.x & 7;
   const int64_t groups = K / kGroup;
   const int64_t total = rows * groups;
-  const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const int64_t g0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3;
+  const int64_t ng = ((int64_t)gridDim.x * blockDim.x) >> 3;
   const double skip = iters > 0 ? 0.5 * pow(beta * pow(kappa, (double)(iters - 1)), -1.0 / (2.0 - p)) : 0.0;
-  for (int64_t gi = wave0; gi < total; gi += nwaves) {
+  // the loop runs the same number of times in all 8 lanes of a group
+  for (int64_t gi = g0; gi < total; gi += ng) {
     const int64_t r = gi / groups, g = gi - r * groups;
-    const int64_t idx = r * K + g * kGroup + lane;
-    const float wf = W[idx];
-    float lo = wf, hi = wf;
+    const int64_t idx = r * K + g * kGroup + 8 * l8;
+    const float4 a0 = *(const float4*)(W + idx);
+    const float4 a1 = *(const float4*)(W + idx + 4);
+    const float wf[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    float lo = wf[0], hi = wf[0];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      lo = fminf(lo, __shfl_xor(lo, o));
-      hi = fmaxf(hi, __shfl_xor(hi, o));
+    for (int j = 1; j < 8; ++j) {
+      lo = fminf(lo, wf[j]);
+      hi = fmaxf(hi, wf[j]);
     }
+    lo = min8(lo);
+    hi = max8(hi);
     uint16_t sb = f64_to_f16_rne(((double)hi - (double)lo) / 7.0);
     if ((sb & 0x7FFFu) == 0) sb = 0x3C00u;
     const double s = f16_bits_to_f64(sb);
     const uint16_t z0b = f64_to_f16_rne(fmin(fmax(-(double)lo / s, -65504.0), 65504.0));
-    const double w = (double)wf;
-    const double ws = w / s;
+    double w[8], ws[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      w[j] = (double)wf[j];
+      ws[j] = w[j] / s;
+    }
     double z = f16_bits_to_f64(z0b);
     uint16_t best_b = z0b;
     double best_z = z;
-    double best_err = wave_sum(fabs(w - (code_at(ws, z) - z) * s));
+    double best_err = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) best_err += fabs(w[j] - (code_at(ws[j], z) - z) * s);
+    best_err = sum8(best_err);
     double b = beta;
     for (int it = 0; it < iters; ++it) {
-      const double q = code_at(ws, z);
-      const double x = w - (q - z) * s;
-      const double ax = fabs(x);
-      double u = ws;                       // (w - W_e) / s with W_e = 0
-      if (ax > skip) {
-        const double t = ax - pow(ax, p - 1.0) / b;
-        if (t > 0.0) u = (w - copysign(t, x)) / s;
+      double acc = 0.0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double q = code_at(ws[j], z);
+        const double x = w[j] - (q - z) * s;
+        const double ax = fabs(x);
+        double u = ws[j];                  // (w - W_e) / s with W_e = 0
+        if (ax > skip) {
+          const double t = ax - pow(ax, p - 1.0) / b;
+          if (t > 0.0) u = (w[j] - copysign(t, x)) / s;
+        }
+        acc += q - u;
       }
-      z = wave_sum(q - u) / (double)kGroup;
+      z = sum8(acc) / (double)kGroup;
       b *= kappa;
       const uint16_t zb = f64_to_f16_rne(fmin(fmax(z, -65504.0), 65504.0));
       const double zc = f16_bits_to_f64(zb);
-      const double err = wave_sum(fabs(w - (code_at(ws, zc) - zc) * s));
+      double err = 0.0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) err += fabs(w[j] - (code_at(ws[j], zc) - zc) * s);
+      err = sum8(err);
       if (err < best_err) {
         best_err = err;
         best_z = zc;
         best_b = zb;
       }
     }
-    codes[idx] = (uint8_t)code_at(ws, best_z);
-    if (lane == 0) {
+    uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c0 |= (uint32_t)code_at(ws[j], best_z) << (8 * j);
+      c1 |= (uint32_t)code_at(ws[j + 4], best_z) << (8 * j);
+    }
+    *(uint2*)(codes + idx) = make_uint2(c0, c1);
+    if (l8 == 0) {
       scale[r * groups + g] = sb;
       zero[r * groups + g] = best_b;
     }
@@ -357,8 +391,8 @@ int32_t launch_pack_lr(const uint8_t* v_codes, const uint16_t* v_scale, const ui
 
 int32_t launch_hqq(const float* W, int64_t rows, int64_t K, int iters, double p, double beta, double kappa,
                    uint8_t* codes, uint16_t* scale, uint16_t* zero, hipStream_t st) {
-  const int64_t waves = rows * (K / kGroup);
-  hipLaunchKernelGGL(hqq_kernel, dim3(grid_for(waves, 4)), dim3(256), 0, st, W, rows, K, iters, p, beta, kappa,
+  const int64_t groups = rows * (K / kGroup);      // 32 groups per 256-thread block
+  hipLaunchKernelGGL(hqq_kernel, dim3(grid_for(groups, 32)), dim3(256), 0, st, W, rows, K, iters, p, beta, kappa,
                      codes, scale, zero);
   return hip_status(hipGetLastError(), "hqq_kernel launch");
 }

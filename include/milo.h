@@ -108,7 +108,8 @@ int32_t milo_quantize_rtn_int3_grouped(const float* W, int64_t rows, int64_t K,
  *     candidate (RTN's zero point first) is stored, with its codes.
  * So no group's mean absolute error exceeds RTN's.  Published defaults:
  * p_norm 0.7, beta 10, kappa 1.01, 20 iterations; iters 0 reproduces RTN.
- * Arguments and outputs as milo_quantize_rtn_int3.
+ * Arguments and outputs as milo_quantize_rtn_int3, except alignment: W must
+ * be 16-byte and codes 8-byte aligned (MILO_ERR_ALIGN otherwise).
  */
 int32_t milo_quantize_hqq_int3(const float* W, int64_t rows, int64_t K,
                                int32_t iters, double p_norm, double beta,

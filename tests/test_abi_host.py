@@ -78,6 +78,18 @@ def test_lr_word_counts_match_the_spec(L, N, K, max_rank):
     assert lib.milo_lr_u_sz_words(N) == oracle.lr_u_sz_words(N)
 
 
+def test_hqq_rejects(L):
+    lib = L.lib()
+    f = C.c_void_p(0x100000)
+    q = lambda W=f, rows=4, K=128, it=20, p=0.7, b=10.0, k=1.01, codes=f: lib.milo_quantize_hqq_int3(
+        W, rows, K, it, p, b, k, codes, f, f, None)
+    assert q(W=None) == 1
+    assert q(K=96) == 2 and q(rows=0) == 2
+    assert q(it=-1) == 6 and q(p=0.0) == 6 and q(p=1.5) == 6 and q(b=0.0) == 6 and q(k=0.5) == 6
+    assert q(W=C.c_void_p(0x100004)) == 3          # W must be 16-byte aligned
+    assert q(codes=C.c_void_p(0x100004)) == 3      # codes 8-byte aligned
+
+
 def test_pack_lr_rejects(L):
     lib = L.lib()
     f = C.c_void_p(0x1000)
