@@ -172,6 +172,22 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
   p->lr_tiles = (P + 15) / 16 + d->num_experts;
   const int nrt = d->n_w * p->rp / 16;
   p->lr_tiles_per_block = rows_bound <= kDecodeMaxRows ? 1 : (nrt > 0 ? nrt : 1);
+  p->lr_mt = 1;
+  p->lr_ks = 1;
+  if (p->rp > 0 && p->lr_tiles_per_block > 1 && d->w[0].lr_format == MILO_LR_FP16) {
+    // fp16 prefill-form pre-pass: 64-row tiles where experts average 128 rows
+    // or more; split K while the row tiles x rank groups (counted without
+    // partial tiles) number fewer than kPrepassBlocks, keeping at least one
+    // batch of loads (4 waves x UNR steps of 32) per chunk
+    p->lr_mt = P >= 128 * d->num_experts ? kPrepassMT : 1;
+    const int unr = p->lr_mt > 1 ? 2 : 4;
+    const int tpb = p->lr_tiles_per_block < 4 ? p->lr_tiles_per_block : 4;
+    const int est = ((P + 16 * p->lr_mt - 1) / (16 * p->lr_mt)) * (nrt / tpb);
+    int ks = (kPrepassBlocks + est - 1) / est;
+    const int ks_max = (d->K / 32) / (4 * unr);
+    if (ks > ks_max) ks = ks_max;
+    p->lr_ks = ks < 1 ? 1 : ks;
+  }
 
   size_t off = 0;
   p->off_t = off;
@@ -183,6 +199,8 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
   p->off_dec_part = off;
   if (p->dec_ksplit > 1)
     off += round_up((size_t)p->dec_ksplit * d->num_experts * p->n_tiles * d->n_w * p->dec_mt * 16 * 64 * 4, 256);
+  p->off_tpart = off;
+  if (p->lr_ks > 1) off += round_up((size_t)p->lr_ks * P * d->n_w * p->rp * 4, 256);
   p->total = off;
   return MILO_OK;
 }

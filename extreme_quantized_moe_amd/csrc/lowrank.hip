@@ -26,8 +26,6 @@
 
 namespace milo {
 
-constexpr int kPrepassMT = 4;   // m-tiles per block of the fp16 prefill pre-pass for large experts
-
 struct PrepassArgs {
   const uint16_t* x;
   const int32_t* sorted_pairs;
@@ -39,6 +37,9 @@ struct PrepassArgs {
   int64_t vq_per_expert, vsz_per_expert;
   const int32_t* rank[2];
   uint16_t* T;        // fp16 [P][n_w * rp]
+  float* tpart;       // fp32 [ks][P][n_w * rp]: K-chunk partials of T (prefill form, ks > 1), or null
+  int ks_steps;       // 32-wide K steps per chunk (prefill form)
+  int num_pairs;
   uint16_t* xg;       // fp16 [P][K]: row of each pair (small-M experts), or null
   float* pw;          // fp32 [P]: route weight of each pair, or null
   int K, gather_div, num_experts, n_w, rp, max_rank;
@@ -53,10 +54,11 @@ __device__ __forceinline__ bool find_tile16(const PrepassArgs& a, RowTile* t) {
                        a.rp ? a.rank[1] : nullptr, t);
 }
 
-// Gathered rows (pair order) and pair weights of one 16-row tile.
-__device__ void prepass_aux(const PrepassArgs& a, int base, int m0, int M) {
+// Gathered rows (pair order) and pair weights of one 16-row tile; part
+// `part` of `parts` of the rows' 16-byte chunks (the weights with part 0).
+__device__ void prepass_aux(const PrepassArgs& a, int base, int m0, int M, int part = 0, int parts = 1) {
   const int rows = (M - m0) < 16 ? (M - m0) : 16;
-  if (a.pw && threadIdx.x < rows) {
+  if (a.pw && part == 0 && threadIdx.x < rows) {
     const int i = base + m0 + threadIdx.x;
     a.pw[i] = a.slot_w[a.sorted_pairs[i]];
   }
@@ -64,14 +66,15 @@ __device__ void prepass_aux(const PrepassArgs& a, int base, int m0, int M) {
   // copy the tile's rows in pair order, eight 16-byte chunks in flight per thread
   const int chunks = a.K / 8;                     // 16-byte chunks per row
   const int n = rows * chunks;
-  for (int o0 = threadIdx.x; o0 < n; o0 += 8 * blockDim.x) {
+  const int o_end = (int)((int64_t)n * (part + 1) / parts);
+  for (int o0 = (int)((int64_t)n * part / parts) + threadIdx.x; o0 < o_end; o0 += 8 * blockDim.x) {
     u32x4 v[8];
     size_t dst[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int o = o0 + u * blockDim.x;
       dst[u] = 0;
-      if (o < n) {
+      if (o < o_end) {
         const int r = o / chunks, c = o - r * chunks;
         const int i = base + m0 + r;
         const int xr = a.sorted_pairs[i] / a.gather_div;
@@ -81,7 +84,7 @@ __device__ void prepass_aux(const PrepassArgs& a, int base, int m0, int M) {
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (o0 + u * blockDim.x < n) *(u32x4*)(a.xg + dst[u]) = v[u];
+      if (o0 + u * blockDim.x < o_end) *(u32x4*)(a.xg + dst[u]) = v[u];
   }
 }
 
@@ -331,12 +334,16 @@ __global__ void __launch_bounds__(64 * NWAVES) prepass_kernel(PrepassArgs a) {
     return;
   const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
   if ((int)blockIdx.y == a.aux_y) {
-    for (int g = m0; g < M && g < m0 + 16 * MT; g += 16) prepass_aux(a, base, g, M);
+    for (int g = m0; g < M && g < m0 + 16 * MT; g += 16) prepass_aux(a, base, g, M, blockIdx.z, gridDim.z);
     return;
   }
   const int RW = a.n_w * a.rp;
   const int tiles_per_w = a.rp / 16;
   const int tr0 = blockIdx.y * NRT;            // first rank tile of this block
+  // K chunk of this block: 32-wide steps [s_lo, s_hi)
+  const int ksteps = a.K / 32;
+  const int s_lo = blockIdx.z * a.ks_steps;
+  const int s_hi = s_lo + a.ks_steps < ksteps ? s_lo + a.ks_steps : ksteps;
 
   // A operand rows of this lane, one per 16-row m-tile
   const uint16_t* xp[MT];
@@ -370,16 +377,15 @@ __global__ void __launch_bounds__(64 * NWAVES) prepass_kernel(PrepassArgs a) {
 #pragma unroll
     for (int t = 0; t < NRT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K steps s = wave + NWAVES i, in batches of UNR steps whose loads are all
-  // issued before the first product (steps past the end are skipped)
-  const int ksteps = a.K / 32;
+  // K steps s = s_lo + wave + NWAVES i, in batches of UNR steps whose loads
+  // are all issued before the first product (steps past the chunk are skipped)
   if (any) {
-    for (int s0 = wave; s0 < ksteps; s0 += UNR * NWAVES) {
+    for (int s0 = s_lo + wave; s0 < s_hi; s0 += UNR * NWAVES) {
       f16x8 xa[UNR][MT], vb[UNR][NRT];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int s = s0 + NWAVES * u;
-        const bool in = s < ksteps;
+        const bool in = s < s_hi;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           xa[u][mt] = (in && row_ok[mt]) ? *(const f16x8*)(xp[mt] + 32 * s) : f16x8{};
@@ -410,8 +416,38 @@ __global__ void __launch_bounds__(64 * NWAVES) prepass_kernel(PrepassArgs a) {
     for (int w = 0; w < NWAVES; ++w) v += red[w][mt][t][ln][r];
     const int row = 16 * mt + 4 * (ln >> 4) + r;  // within the tile
     const int col = (tr0 + t) * 16 + (ln & 15);   // 0..RW-1
-    if (m0 + row < M) a.T[(size_t)(base + m0 + row) * RW + col] = float_to_half_bits(v);
+    if (m0 + row >= M) continue;
+    const size_t o_t = (size_t)(base + m0 + row) * RW + col;
+    if (a.tpart) a.tpart[(size_t)blockIdx.z * a.num_pairs * RW + o_t] = v;
+    else a.T[o_t] = float_to_half_bits(v);
   }
+}
+
+// T = sum of the K-chunk partials, added in chunk order (fp32), rounded once
+// to fp16.  Four elements per thread; n (= P x RW) is a multiple of 32.
+__global__ void __launch_bounds__(256) prepass_reduce_kernel(const float* __restrict__ part, int ks, int n,
+                                                             uint16_t* __restrict__ T) {
+  const int i = 4 * (blockIdx.x * 256 + threadIdx.x);
+  if (i >= n) return;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  // eight chunks' loads in flight, added in chunk order
+  for (int k0 = 0; k0 < ks; k0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = k0 + u < ks ? *(const f32x4*)(part + (size_t)(k0 + u) * n + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      s[0] += v[u][0];
+      s[1] += v[u][1];
+      s[2] += v[u][2];
+      s[3] += v[u][3];
+    }
+  }
+  uint2 h;
+  h.x = (uint32_t)float_to_half_bits(s[0]) | ((uint32_t)float_to_half_bits(s[1]) << 16);
+  h.y = (uint32_t)float_to_half_bits(s[2]) | ((uint32_t)float_to_half_bits(s[3]) << 16);
+  *(uint2*)(T + i) = h;
 }
 
 // int3 factors, prefill form: block = one 16-row tile of pairs x NRT rank
@@ -558,6 +594,9 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
   a.max_rank = d->max_rank;
   a.aux_y = aux_blocks ? rank_blocks : -1;
   a.dec_max_rows = p.dec_max_rows;
+  a.tpart = nullptr;
+  a.ks_steps = d->K / 32;
+  a.num_pairs = d->num_pairs;
   if (per == 1) {                                   // decode
     constexpr int kNJ3 = 4;
     const int nj = lrq ? kNJ3 : 1;
@@ -586,12 +625,17 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
     // once per 16 MT pairs) x groups of at most four 16-rank tiles.  MT = 4
     // where experts average 128 rows or more, else 1 (small experts would
     // waste most of a 64-row tile, and the grid would be sparse)
+    // K is split into p.lr_ks chunks (grid.z) when the rows alone give a
+    // sparse grid; the chunks' fp32 partials are then added by a reduce pass
     const int tpb = per < 4 ? per : 4;
-    const bool big = d->num_pairs >= 128 * d->num_experts;
-    const int mt = big ? kPrepassMT : 1;
+    const bool big = p.lr_mt > 1;
+    const int mt = p.lr_mt;
     const int tiles = (d->num_pairs + 16 * mt - 1) / (16 * mt) + d->num_experts;
+    const int ksteps = d->K / 32;
     a.aux_y = aux_blocks ? nrt / tpb : -1;
-    dim3 grid(tiles, nrt / tpb + aux_blocks);
+    a.ks_steps = (ksteps + p.lr_ks - 1) / p.lr_ks;
+    if (p.lr_ks > 1) a.tpart = (float*)(ws + p.off_tpart);
+    dim3 grid(tiles, nrt / tpb + aux_blocks, p.lr_ks);
     if (tpb != 2 && tpb != 4) {
       set_error("internal: unsupported rank-tile count %d", per);
       return MILO_ERR_RANK;
@@ -602,6 +646,14 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
     } else {
       if (tpb == 2) hipLaunchKernelGGL((prepass_kernel<2, 4, 4, 1>), grid, dim3(256), 0, st, a);
       else hipLaunchKernelGGL((prepass_kernel<4, 4, 4, 1>), grid, dim3(256), 0, st, a);
+    }
+    if (p.lr_ks > 1) {
+      const int32_t rc = hip_status(hipGetLastError(), "prepass_kernel launch");
+      if (rc != MILO_OK) return rc;
+      const int n = d->num_pairs * nrt * 16;
+      hipLaunchKernelGGL(prepass_reduce_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, st, a.tpart, p.lr_ks, n,
+                         a.T);
+      return hip_status(hipGetLastError(), "prepass_reduce_kernel launch");
     }
   }
   return hip_status(hipGetLastError(), "prepass_kernel launch");

@@ -24,6 +24,8 @@ constexpr int kTileSzWords = 128;  // 64 rows x 2 groups
 constexpr int kGroup = 64;
 constexpr int kMaxRank = 64;
 constexpr int kDecodeMaxRows = 32;  // largest expert row count of the small-M path
+constexpr int kPrepassMT = 4;       // m-tiles per block of the fp16 prefill pre-pass for large experts
+constexpr int kPrepassBlocks = 512; // the fp16 prefill pre-pass splits K until its grid has about this many blocks
 
 // Per-pair constant offsets of the "off + q" float16 encoding produced by the
 // code extraction (see dequant_triplet): pair pi of a triplet holds codes at
@@ -227,6 +229,8 @@ struct GemmPlan {
   int rp;            // compensator rank padded to 32 (0 = no compensator)
   int lr_tiles_per_block;  // rank tiles (16 ranks) per pre-pass block
   int lr_tiles;      // grid.x of the low-rank pre-pass (16-row tiles)
+  int lr_mt;         // fp16 prefill-form pre-pass: 16-row m-tiles per block
+  int lr_ks;         // fp16 prefill-form pre-pass: K chunks (fp32 partials + reduce when > 1)
   int dec_mt;        // 16-row m-tiles of the small-M kernel (0 = not launched)
   int dec_max_rows;  // experts with at most this many rows use the small-M kernel
   int dec_ksplit;    // split-K factor of the small-M kernel
@@ -234,7 +238,7 @@ struct GemmPlan {
   int pre_launch;    // launch the tile kernel
   int pre_tiles;     // grid.x bound of the tile kernel
   // workspace carve-up (byte offsets)
-  size_t off_t, off_xg, off_pw, off_dec_part, total;
+  size_t off_t, off_xg, off_pw, off_dec_part, off_tpart, total;
 };
 int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p);
 int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st);
