@@ -11,13 +11,15 @@
 // owns one 64-wide output tile of one weight family (SWIGLU: waves (W1, W3) x
 // two n-tiles; otherwise four n-tiles of the one family), so every packed
 // weight tile is read and dequantized by exactly one wave.  Activation rows
-// are staged through LDS (128 rows x 128 K, double buffered, rows padded by
-// 16 bytes against bank conflicts) and shared by the four waves; the next
-// K block's activations and weights are loaded into registers while the
-// current one is computed.  Weights are dequantized in registers (int3 pair
+// go straight from global memory into LDS (global_load_lds_dwordx4: 128
+// rows x 128 K, double buffered, 16-byte chunks XOR-swizzled per row against
+// bank conflicts) and are shared by the four waves; the next K block's
+// activations (into LDS) and weights (into registers) load while the current
+// one is computed.  Weights are dequantized in registers (int3 pair
 // extraction, then packed fp16: subtract the offset, one fused multiply-add
 // by the scale with -z s) and multiplied on v_mfma_f32_16x16x32_f16 with fp32
-// accumulation.
+// accumulation; the dequantization of K step s + 1 is interleaved with the
+// products of step s.
 // Epilogue: low-rank term as two more matrix-core K-steps per 32 ranks, then
 // SWIGLU through LDS, or fp16 store, or route-weighted fp32 scatter.
 #include "gemm_common.hpp"
@@ -26,10 +28,10 @@ namespace milo {
 
 constexpr int kBM = 128;                 // rows per block
 constexpr int kMT = kBM / 16;            // m-tiles per wave
-constexpr int kXStride = kTileK + 8;     // LDS row stride in halves (272 B)
+constexpr int kXStride = kTileK;         // LDS row stride in halves (256 B; chunks swizzled)
 constexpr int kXBuf = kBM * kXStride;    // halves per buffer
 constexpr int kExStride = 68;            // floats per row of the SwiGLU exchange
-static_assert(2 * kBM * kExStride * 4 <= 2 * kXBuf * 2, "exchange must fit the staging LDS");
+constexpr size_t kPreLds = 2 * kBM * kExStride * 4 > 2 * kXBuf * 2 ? 2 * kBM * kExStride * 4 : 2 * kXBuf * 2;
 
 // Weight dequantization in packed fp16: from the extracted pair h = (off + q)
 // (exact), q = h - off is exact, and (q - z) s = fma(q, s, -z s) with -z s
@@ -77,27 +79,33 @@ gemm_prefill_kernel(GemmArgs a) {
   const int nt = (NW == 2) ? (2 * blockIdx.x + (wave >> 1)) : (4 * blockIdx.x + wave);
   const bool wave_on = nt < a.n_tiles;
 
-  // ---- activation staging: thread loads 8 chunks of 16 B per K block, rows
-  // (tid / 16) + 16 j, column chunk tid % 16.  Rows past the expert's count
-  // read its first row instead: they only feed output rows that are not stored.
+  // ---- activation staging, global memory -> LDS without registers: per K
+  // block a wave issues 8 loads of 1 KB, load j filling rows 16 j + 4 wave ..
+  // + 3 (lane l: row + l / 16, 16-byte slot l % 16).  Slot p of row r holds
+  // column chunk p ^ (r % 16), so a fragment read (16 rows, one chunk) hits
+  // 16 different slots.  Rows past the expert's count read its first row
+  // instead: they only feed output rows that are not stored.
+  (void)tid;
+  const int srow = 4 * wave + (lane >> 4);
   int xrow[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int m = m0 + (tid >> 4) + 16 * j;
+    const int m = m0 + srow + 16 * j;
     const int i = base + (m < M ? m : m0);
     xrow[j] = a.gather_div > 0 ? a.sorted_pairs[i] / a.gather_div : i;
   }
-  const uint16_t* xcol = a.x + 8 * (tid & 15);
-  const int xdst = (tid >> 4) * kXStride + 8 * (tid & 15);
-  u32x4 xreg[8];
-  auto load_x = [&](int kb) {
+  const uint16_t* xcol = a.x + 8 * ((lane & 15) ^ (srow & 15));
+  auto stage_x = [&](int kb, int buf) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xreg[j] = *(const u32x4*)(xcol + (size_t)xrow[j] * a.K + (size_t)kb * kTileK);
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(xcol + (size_t)xrow[j] * a.K + (size_t)kb * kTileK),
+          (__attribute__((address_space(3))) void*)(lds + buf * kXBuf + (16 * j + 4 * wave) * kXStride), 16, 0, 0);
   };
-  auto store_x = [&](int buf) {
+  // fragment of K step s: row lane % 16 of each m-tile, chunk 4 s + lane / 16
+  int xoff[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *(u32x4*)(lds + buf * kXBuf + xdst + 16 * j * kXStride) = xreg[j];
-  };
+  for (int s4 = 0; s4 < 4; ++s4) xoff[s4] = (lane & 15) * kXStride + 8 * ((4 * s4 + (lane >> 4)) ^ (lane & 15));
 
   // ---- weights of this wave
   const uint32_t* tbase = a.packed[f] + e * a.words_per_expert + (size_t)(wave_on ? nt : 0) * a.kblocks * kTileWords;
@@ -119,41 +127,53 @@ gemm_prefill_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_x(0);
+  stage_x(0, 0);
   if (wave_on) load_w(0);
-  store_x(0);
-  __syncthreads();
+  __syncthreads();   // waits for the staging loads (vmcnt) first
 
+  // B operands of K step s of the current block, from the lane's triplets
+  auto dequant = [&](f16x8 (&wf)[4], int s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t h[16];
+      extract_triplet(wq[0][i], wq[1][i], wq[2][i], h, kc);
+      const int idx = 2 * i + (s >> 1);
+      const GroupConstPk gc = group_const_pk(idx < 4 ? wz[0][idx] : wz[1][idx - 4]);
+      wf[i] = dequant_step_pk(h, s, gc);
+    }
+  };
+
+  // Each K block is one straight-line region (the prefetch indices are
+  // clamped instead of branched on; the last block re-loads its own data),
+  // so the scheduler can overlap a step's dequantization with the previous
+  // step's products.
   const int KB = a.kblocks;
-  for (int kb = 0; kb < KB; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < KB) load_x(kb + 1);
-    const uint16_t* xb = lds + buf * kXBuf + (lane & 15) * kXStride + 8 * (lane >> 4);
-    // K step by K step: dequantize the step's B operands of the four 16-row
-    // sub-tiles, then the m-tiles' products (keeps one step of operands live)
+  if (wave_on) {
+    for (int kb = 0; kb < KB; ++kb) {
+      const int buf = kb & 1;
+      const int kn = kb + 1 < KB ? kb + 1 : kb;
+      stage_x(kn, buf ^ 1);
+      const uint16_t* xb = lds + buf * kXBuf;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (wave_on) {
+      for (int s = 0; s < 4; ++s) {
         f16x8 wf[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t h[16];
-          extract_triplet(wq[0][i], wq[1][i], wq[2][i], h, kc);
-          const int idx = 2 * i + (s >> 1);
-          const GroupConstPk gc = group_const_pk(idx < 4 ? wz[0][idx] : wz[1][idx - 4]);
-          wf[i] = dequant_step_pk(h, s, gc);
-        }
-        if (s == 3 && kb + 1 < KB) load_w(kb + 1);   // the codes of this block are consumed
+        dequant(wf, s);
+        if (s == 3) load_w(kn);   // the codes of this block are consumed
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
-          const f16x8 xa = *(const f16x8*)(xb + mt * 16 * kXStride + 32 * s);
+          const f16x8 xa = *(const f16x8*)(xb + xoff[s] + mt * 16 * kXStride);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[mt][i] = mfma16x16x32(xa, wf[i], acc[mt][i]);
         }
       }
+      __syncthreads();   // waits for the staging loads (vmcnt) first
     }
-    if (kb + 1 < KB) store_x(buf ^ 1);
-    __syncthreads();
+  } else {
+    // no output tile: only the share of the activation staging
+    for (int kb = 0; kb < KB; ++kb) {
+      stage_x(kb + 1 < KB ? kb + 1 : kb, (kb & 1) ^ 1);
+      __syncthreads();
+    }
   }
 
   // ---- low-rank term: (x V^T) U^T as extra K steps (int3 U: the lane's
@@ -248,7 +268,7 @@ gemm_prefill_kernel(GemmArgs a) {
 int32_t launch_gemm_prefill(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st) {
   if (!p.pre_launch) return MILO_OK;
   GemmArgs a = make_gemm_args(d, p, ws);
-  const size_t lds_bytes = 2 * kXBuf * sizeof(uint16_t);   // >= 2 x 128 x 64 fp32 for SWIGLU
+  const size_t lds_bytes = kPreLds;
   if (d->n_w == 2) {
     dim3 grid((p.n_tiles + 1) / 2, p.pre_tiles);
     if (a.lrq) hipLaunchKernelGGL((gemm_prefill_kernel<2, true>), grid, dim3(256), lds_bytes, st, a);
