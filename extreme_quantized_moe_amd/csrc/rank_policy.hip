@@ -37,6 +37,49 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
   return s;
 }
 
+// Sums over elements [e0, e1) of one matrix for this thread: PASS 0 sum of
+// w - mu; PASS 1 sums of (w - mu)^2 and (w - mu)^4.  16-byte non-temporal
+// loads (each weight is read once per pass), four in flight; e0 and the
+// chunk are multiples of 4.  A thread adds its elements in ascending order.
+template <int PASS>
+__device__ __forceinline__ void moments_sums(const float* __restrict__ wm, int64_t e0, int64_t e1, double mu,
+                                             double& s1, double& s2) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  double a1 = 0.0, a2 = 0.0;
+  auto add = [&](double x) {
+    const double d = x - mu;
+    if (PASS) {
+      const double d2 = d * d;
+      a1 += d2;
+      a2 += d2 * d2;
+    } else {
+      a1 += d;
+    }
+  };
+  const int64_t step = 4 * (int64_t)kMomThreads;
+  int64_t i = e0 + 4 * (int64_t)threadIdx.x;
+  for (; i + 3 * step + 3 < e1; i += 4 * step) {
+    f32x4_t q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q[u] = __builtin_nontemporal_load((const f32x4_t*)(wm + i + u * step));
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) add((double)q[u][k]);
+  }
+  for (; i < e1; i += step) {
+    if (i + 3 < e1) {
+      const f32x4_t q = __builtin_nontemporal_load((const f32x4_t*)(wm + i));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) add((double)q[k]);
+    } else {
+      for (int64_t k = i; k < e1; ++k) add((double)wm[k]);
+    }
+  }
+  s1 = a1;
+  s2 = a2;
+}
+
 // pass 0: sum of w;  pass 1: sum of (w - mean)^2 and (w - mean)^4.
 // Block (b, m) covers elements [b chunk, (b + 1) chunk) of matrix m.
 __global__ void __launch_bounds__(kMomThreads) moments_kernel(const float* __restrict__ W, int64_t elems,
@@ -48,33 +91,9 @@ __global__ void __launch_bounds__(kMomThreads) moments_kernel(const float* __res
   const float* wm = W + (size_t)m * elems;
   const int64_t e0 = (int64_t)b * chunk;
   const int64_t e1 = e0 + chunk < elems ? e0 + chunk : elems;
-  const double mu = pass ? mean[m] : 0.0;
   double s1 = 0.0, s2 = 0.0;
-  // 16-byte loads where the chunk is aligned (chunk and elems multiples of 4)
-  for (int64_t i = e0 + 4 * (int64_t)threadIdx.x; i < e1; i += 4 * (int64_t)kMomThreads) {
-    float v[4];
-    int nv = 4;
-    if (i + 3 < e1) {
-      const float4 q = *(const float4*)(wm + i);
-      v[0] = q.x, v[1] = q.y, v[2] = q.z, v[3] = q.w;
-    } else {
-      nv = (int)(e1 - i);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = k < nv ? wm[i + k] : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (k >= nv) continue;
-      const double d = (double)v[k] - mu;
-      if (pass) {
-        const double d2 = d * d;
-        s1 += d2;
-        s2 += d2 * d2;
-      } else {
-        s1 += d;
-      }
-    }
-  }
+  if (pass) moments_sums<1>(wm, e0, e1, mean[m], s1, s2);
+  else moments_sums<0>(wm, e0, e1, 0.0, s1, s2);
   const double t1 = block_sum(s1, red);
   const double t2 = pass ? block_sum(s2, red) : 0.0;
   if (threadIdx.x == 0) {
