@@ -109,10 +109,23 @@ __global__ void __launch_bounds__(64) moments_finish_kernel(const double* __rest
                                                             double* __restrict__ mean,
                                                             double* __restrict__ kurt) {
   for (int m = blockIdx.x * blockDim.x + threadIdx.x; m < count; m += gridDim.x * blockDim.x) {
+    // partials added in block order; eight blocks' loads in flight
     double a = 0.0, c = 0.0;
-    for (int b = 0; b < nb; ++b) {
-      a += part[((size_t)m * nb + b) * 2];
-      c += part[((size_t)m * nb + b) * 2 + 1];
+    const double* pm = part + (size_t)m * nb * 2;
+    for (int b0 = 0; b0 < nb; b0 += 8) {
+      double pa[8], pc[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        pa[u] = b0 + u < nb ? pm[(b0 + u) * 2] : 0.0;
+        pc[u] = b0 + u < nb ? pm[(b0 + u) * 2 + 1] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (b0 + u < nb) {
+          a += pa[u];
+          c += pc[u];
+        }
+      }
     }
     if (pass == 0) {
       mean[m] = a / (double)elems;
