@@ -110,15 +110,15 @@ gemm_prefill_kernel(GemmArgs a) {
   // ---- weights of this wave
   const uint32_t* tbase = a.packed[f] + e * a.words_per_expert + (size_t)(wave_on ? nt : 0) * a.kblocks * kTileWords;
   const uint32_t* sbase = a.sz[f] + e * a.sz_per_expert + (size_t)(wave_on ? nt : 0) * a.kblocks * kTileSzWords;
-  u32x4 wq[3], wz[2];
-  auto load_w = [&](int kb) {
+  u32x4 wq[3], wz[2], nq[3], nz[2];
+  auto load_w = [&](int kb, u32x4 (&q)[3], u32x4 (&z)[2]) {
     const uint32_t* tp = tbase + (size_t)kb * kTileWords;
     const uint32_t* sp = sbase + (size_t)kb * kTileSzWords + 8 * (lane & 15);
-    wq[0] = *(const u32x4*)(tp + 4 * lane);
-    wq[1] = *(const u32x4*)(tp + 256 + 4 * lane);
-    wq[2] = *(const u32x4*)(tp + 512 + 4 * lane);
-    wz[0] = *(const u32x4*)(sp);
-    wz[1] = *(const u32x4*)(sp + 4);
+    q[0] = *(const u32x4*)(tp + 4 * lane);
+    q[1] = *(const u32x4*)(tp + 256 + 4 * lane);
+    q[2] = *(const u32x4*)(tp + 512 + 4 * lane);
+    z[0] = *(const u32x4*)(sp);
+    z[1] = *(const u32x4*)(sp + 4);
   };
 
   f32x4 acc[kMT][4];
@@ -128,7 +128,7 @@ gemm_prefill_kernel(GemmArgs a) {
     for (int i = 0; i < 4; ++i) acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   stage_x(0, 0);
-  if (wave_on) load_w(0);
+  if (wave_on) load_w(0, wq, wz);
   __syncthreads();   // waits for the staging loads (vmcnt) first
 
   // B operands of K step s of the current block, from the lane's triplets
@@ -153,18 +153,31 @@ gemm_prefill_kernel(GemmArgs a) {
       const int buf = kb & 1;
       const int kn = kb + 1 < KB ? kb + 1 : kb;
       stage_x(kn, buf ^ 1);
+      // one weight family: the next block's weights load ahead of this
+      // block's work (a second register set); two families keep one set
+      // (no registers to spare) and load after the last step's dequantization
+      if constexpr (NW == 1) {
+        load_w(kn, nq, nz);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const uint16_t* xb = lds + buf * kXBuf;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         f16x8 wf[4];
         dequant(wf, s);
-        if (s == 3) load_w(kn);   // the codes of this block are consumed
+        if (NW == 2 && s == 3) load_w(kn, wq, wz);   // the codes of this block are consumed
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
           const f16x8 xa = *(const f16x8*)(xb + xoff[s] + mt * 16 * kXStride);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[mt][i] = mfma16x16x32(xa, wf[i], acc[mt][i]);
         }
+      }
+      if constexpr (NW == 1) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) wq[j] = nq[j];
+        wz[0] = nz[0];
+        wz[1] = nz[1];
       }
       __syncthreads();   // waits for the staging loads (vmcnt) first
     }
