@@ -175,17 +175,33 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
   p->lr_mt = 1;
   p->lr_ks = 1;
   if (p->rp > 0 && p->lr_tiles_per_block > 1 && d->w[0].lr_format == MILO_LR_FP16) {
-    // fp16 prefill-form pre-pass: 64-row tiles where experts average 128 rows
-    // or more; split K while the row tiles x rank groups (counted without
-    // partial tiles) number fewer than kPrepassBlocks, keeping at least one
-    // batch of loads (4 waves x UNR steps of 32) per chunk
-    p->lr_mt = P >= 128 * d->num_experts ? kPrepassMT : 1;
-    const int unr = p->lr_mt > 1 ? 2 : 4;
-    const int tpb = p->lr_tiles_per_block < 4 ? p->lr_tiles_per_block : 4;
-    const int est = ((P + 16 * p->lr_mt - 1) / (16 * p->lr_mt)) * (nrt / tpb);
-    int ks = (kPrepassBlocks + est - 1) / est;
-    const int ks_max = (d->K / 32) / (4 * unr);
-    if (ks > ks_max) ks = ks_max;
+    // fp16 prefill-form pre-pass.  Experts averaging 128 rows or more: the
+    // 128-row tile kernel (all ranks per block), K split until the row tiles
+    // (counted without partial tiles) fill about one block per CU, at least
+    // four K blocks per chunk.  Otherwise 16-row tiles x groups of four rank
+    // tiles, K split while they number fewer than kPrepassBlocks, keeping at
+    // least one batch of loads (4 waves x 4 steps of 32) per chunk.
+    int ks;
+    if (P >= 128 * d->num_experts) {
+      p->lr_mt = kPrepassTileRows / 16;
+      const int est = (P + kPrepassTileRows - 1) / kPrepassTileRows;
+      ks = (256 + est - 1) / est;
+      const int ks_max = (d->K / 128) / 4;
+      if (ks > ks_max) ks = ks_max;
+      if (ks < 1) ks = 1;
+      const int per = (d->K / 128 + ks - 1) / ks;   // K blocks per chunk
+      ks = (d->K / 128 + per - 1) / per;             // every chunk non-empty
+    } else {
+      p->lr_mt = 1;
+      const int tpb = p->lr_tiles_per_block < 4 ? p->lr_tiles_per_block : 4;
+      const int est = ((P + 15) / 16) * (nrt / tpb);
+      ks = (kPrepassBlocks + est - 1) / est;
+      const int ks_max = (d->K / 32) / 16;
+      if (ks > ks_max) ks = ks_max;
+      if (ks < 1) ks = 1;
+      const int per = (d->K / 32 + ks - 1) / ks;     // K steps per chunk
+      ks = (d->K / 32 + per - 1) / per;              // every chunk non-empty
+    }
     p->lr_ks = ks < 1 ? 1 : ks;
   }
 

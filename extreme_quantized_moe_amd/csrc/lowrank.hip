@@ -423,6 +423,132 @@ __global__ void __launch_bounds__(64 * NWAVES) prepass_kernel(PrepassArgs a) {
   }
 }
 
+// fp16 V, experts with many rows: block = 128 rows of one expert x every rank
+// tile (both families).  The activation tile (128 rows x 128 K per K block)
+// goes global -> LDS with global_load_lds_dwordx4 (16-byte chunks
+// XOR-swizzled per row, double buffered) and is shared by the four waves;
+// wave w owns rank tiles w + 4 u (u < RT) and reads their V fragments straight
+// from global memory, one K block ahead.  So the activation rows are read once
+// per 128 pairs for all ranks, and each V row once per 128 pairs; no wave
+// partials to add (each output has one owner).  grid.z splits K as in
+// prepass_kernel (fp32 partials, then the reduce pass).
+constexpr int kPtRows = kPrepassTileRows;
+constexpr int kPtXBuf = kPtRows * 128;   // halves per staging buffer
+constexpr size_t kPtLds = 2 * kPtXBuf * 2;
+
+template <int RT>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prepass_tile_kernel(PrepassArgs a) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  RowTile rt;
+  if (!find_row_tile(a.offsets, a.num_experts, 0, kPtRows, blockIdx.x, a.rp ? a.rank[0] : nullptr,
+                     a.rp ? a.rank[1] : nullptr, &rt))
+    return;
+  const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
+  if ((int)blockIdx.y == a.aux_y) {
+    for (int g = m0; g < M && g < m0 + kPtRows; g += 16) prepass_aux(a, base, g, M, blockIdx.z, gridDim.z);
+    return;
+  }
+  const int RW = a.n_w * a.rp;
+  const int nrt = RW / 16;
+  const int tiles_per_w = a.rp / 16;
+  const int KB = a.K / 128;
+  const int kb_lo = blockIdx.z * (a.ks_steps / 4);
+  const int kb_hi = kb_lo + a.ks_steps / 4 < KB ? kb_lo + a.ks_steps / 4 : KB;
+
+  // activation staging (as in the tile GEMM): load j of a wave fills rows
+  // 16 j + 4 wave .. + 3; slot p of row r holds column chunk p ^ (r % 16)
+  const int srow = 4 * wave + (lane >> 4);
+  int xrow[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int m = m0 + srow + 16 * j;
+    const int i = base + (m < M ? m : m0);
+    xrow[j] = a.gather_div > 0 ? a.sorted_pairs[i] / a.gather_div : i;
+  }
+  const uint16_t* xcol = a.x + 8 * ((lane & 15) ^ (srow & 15));
+  auto stage_x = [&](int kb, int buf) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(xcol + (size_t)xrow[j] * a.K + (size_t)kb * 128),
+          (__attribute__((address_space(3))) void*)(lds + buf * kPtXBuf + (16 * j + 4 * wave) * 128), 16, 0, 0);
+  };
+  int xoff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) xoff[s] = (lane & 15) * 128 + 8 * ((4 * s + (lane >> 4)) ^ (lane & 15));
+
+  // rank tiles of this wave; V rows at or beyond the expert's rank are zero
+  const uint16_t* vp[RT];
+  bool vok[RT];
+#pragma unroll
+  for (int u = 0; u < RT; ++u) {
+    const int t = wave + 4 * u;
+    const int f = t < nrt ? t / tiles_per_w : 0;
+    const int j = t < nrt ? (t % tiles_per_w) * 16 + (lane & 15) : 0;
+    vok[u] = t < nrt && j < rt.rank(f);
+    vp[u] = a.V[f] + ((size_t)e * a.max_rank + (vok[u] ? j : 0)) * a.K + 8 * (lane >> 4);
+  }
+  f16x8 vb[RT][4], vn[RT][4];
+  auto load_v = [&](int kb, f16x8 (&v)[RT][4]) {
+#pragma unroll
+    for (int u = 0; u < RT; ++u)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 w = *(const f16x8*)(vp[u] + (size_t)kb * 128 + 32 * s);
+        v[u][s] = vok[u] ? w : f16x8{};
+      }
+  };
+
+  f32x4 acc[8][RT];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int u = 0; u < RT; ++u) acc[mt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int kb0 = kb_lo < KB ? kb_lo : KB - 1;   // (chunks are never empty; loads stay in range regardless)
+  stage_x(kb0, 0);
+  load_v(kb0, vb);
+  __syncthreads();   // waits for the staging loads (vmcnt) first
+  for (int kb = kb_lo; kb < kb_hi; ++kb) {
+    const int buf = (kb - kb_lo) & 1;
+    const int kn = kb + 1 < kb_hi ? kb + 1 : kb;   // the last block re-loads its own data
+    stage_x(kn, buf ^ 1);
+    load_v(kn, vn);
+    const uint16_t* xb = lds + buf * kPtXBuf;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const f16x8 xa = *(const f16x8*)(xb + xoff[s] + mt * 16 * 128);
+#pragma unroll
+        for (int u = 0; u < RT; ++u) acc[mt][u] = mfma16x16x32(xa, vb[u][s], acc[mt][u]);
+      }
+#pragma unroll
+    for (int u = 0; u < RT; ++u)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) vb[u][s] = vn[u][s];
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int u = 0; u < RT; ++u) {
+    const int t = wave + 4 * u;
+    if (t >= nrt) continue;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = mt * 16 + 4 * (lane >> 4) + r;
+        if (m0 + row >= M) continue;
+        const size_t o_t = (size_t)(base + m0 + row) * RW + t * 16 + (lane & 15);
+        if (a.tpart) a.tpart[(size_t)blockIdx.z * a.num_pairs * RW + o_t] = acc[mt][u][r];
+        else a.T[o_t] = float_to_half_bits(acc[mt][u][r]);
+      }
+  }
+}
+
 // T = sum of the K-chunk partials, added in chunk order (fp32), rounded once
 // to fp16.  Four elements per thread; n (= P x RW) is a multiple of 32.
 __global__ void __launch_bounds__(256) prepass_reduce_kernel(const float* __restrict__ part, int ks, int n,
@@ -621,29 +747,29 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
     return hip_status(hipGetLastError(), "prepass_q_kernel launch");
   }
   {
-    // row tiles of 16 MT rows (MT m-tiles per block, so each V row is read
-    // once per 16 MT pairs) x groups of at most four 16-rank tiles.  MT = 4
-    // where experts average 128 rows or more, else 1 (small experts would
-    // waste most of a 64-row tile, and the grid would be sparse)
-    // K is split into p.lr_ks chunks (grid.z) when the rows alone give a
-    // sparse grid; the chunks' fp32 partials are then added by a reduce pass
-    const int tpb = per < 4 ? per : 4;
-    const bool big = p.lr_mt > 1;
-    const int mt = p.lr_mt;
-    const int tiles = (d->num_pairs + 16 * mt - 1) / (16 * mt) + d->num_experts;
-    const int ksteps = d->K / 32;
-    a.aux_y = aux_blocks ? nrt / tpb : -1;
-    a.ks_steps = (ksteps + p.lr_ks - 1) / p.lr_ks;
+    // experts averaging 128 rows or more (plan lr_mt = 8): 128-row tiles with
+    // every rank tile per block; otherwise 16-row tiles x groups of at most
+    // four 16-rank tiles.  K is split into p.lr_ks chunks (grid.z) when the
+    // rows alone give a sparse grid; the chunks' fp32 partials are then added
+    // by a reduce pass.
     if (p.lr_ks > 1) a.tpart = (float*)(ws + p.off_tpart);
-    dim3 grid(tiles, nrt / tpb + aux_blocks, p.lr_ks);
-    if (tpb != 2 && tpb != 4) {
-      set_error("internal: unsupported rank-tile count %d", per);
-      return MILO_ERR_RANK;
-    }
-    if (big) {
-      if (tpb == 2) hipLaunchKernelGGL((prepass_kernel<2, 4, 2, kPrepassMT>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((prepass_kernel<4, 4, 2, kPrepassMT>), grid, dim3(256), 0, st, a);
+    if (p.lr_mt == kPtRows / 16) {
+      const int tiles = (d->num_pairs + kPtRows - 1) / kPtRows + d->num_experts;
+      a.ks_steps = 4 * ((d->K / 128 + p.lr_ks - 1) / p.lr_ks);
+      a.aux_y = aux_blocks ? 1 : -1;
+      dim3 grid(tiles, 1 + aux_blocks, p.lr_ks);
+      if (nrt > 4) hipLaunchKernelGGL(prepass_tile_kernel<2>, grid, dim3(256), kPtLds, st, a);
+      else hipLaunchKernelGGL(prepass_tile_kernel<1>, grid, dim3(256), kPtLds, st, a);
     } else {
+      const int tpb = per < 4 ? per : 4;
+      const int tiles = (d->num_pairs + 15) / 16 + d->num_experts;
+      a.aux_y = aux_blocks ? nrt / tpb : -1;
+      a.ks_steps = (d->K / 32 + p.lr_ks - 1) / p.lr_ks;
+      dim3 grid(tiles, nrt / tpb + aux_blocks, p.lr_ks);
+      if (tpb != 2 && tpb != 4) {
+        set_error("internal: unsupported rank-tile count %d", per);
+        return MILO_ERR_RANK;
+      }
       if (tpb == 2) hipLaunchKernelGGL((prepass_kernel<2, 4, 4, 1>), grid, dim3(256), 0, st, a);
       else hipLaunchKernelGGL((prepass_kernel<4, 4, 4, 1>), grid, dim3(256), 0, st, a);
     }

@@ -24,7 +24,7 @@ constexpr int kTileSzWords = 128;  // 64 rows x 2 groups
 constexpr int kGroup = 64;
 constexpr int kMaxRank = 64;
 constexpr int kDecodeMaxRows = 32;  // largest expert row count of the small-M path
-constexpr int kPrepassMT = 4;       // m-tiles per block of the fp16 prefill pre-pass for large experts
+constexpr int kPrepassTileRows = 128;  // rows per block of the fp16 prefill pre-pass for large experts
 constexpr int kPrepassBlocks = 512; // the fp16 prefill pre-pass splits K until its grid has about this many blocks
 
 // Per-pair constant offsets of the "off + q" float16 encoding produced by the
@@ -229,7 +229,7 @@ struct GemmPlan {
   int rp;            // compensator rank padded to 32 (0 = no compensator)
   int lr_tiles_per_block;  // rank tiles (16 ranks) per pre-pass block
   int lr_tiles;      // grid.x of the low-rank pre-pass (16-row tiles)
-  int lr_mt;         // fp16 prefill-form pre-pass: 16-row m-tiles per block
+  int lr_mt;         // fp16 prefill-form pre-pass: 16-row m-tiles per block (8: the 128-row tile kernel)
   int lr_ks;         // fp16 prefill-form pre-pass: K chunks (fp32 partials + reduce when > 1)
   int dec_mt;        // 16-row m-tiles of the small-M kernel (0 = not launched)
   int dec_max_rows;  // experts with at most this many rows use the small-M kernel
