@@ -276,8 +276,8 @@ TIMER = None
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
-              "multi-GPU path: the MoE layer is measured on one MI355X.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): there is no "
+              "multi-GPU path; the MoE layer is measured on one MI355X.", file=sys.stderr)
         sys.exit(2)
     import torch
     import extreme_quantized_moe_amd as m
