@@ -10,17 +10,20 @@
 // matrix cores) and stored as float16 for the GEMM kernels, which add
 // T . U^T as two more matrix-core K-steps.
 //
-// Grid: x = 16-row tiles over all experts (expert by expert); y = compensator
-// ranks or groups of them (decode) or groups of NRT rank tiles of 16 ranks
-// (prefill), plus one "aux" index for the gather / pair weights.
+// Grid: x = row tiles over all experts (expert by expert); y = compensator
+// ranks or groups of them (decode) or groups of rank tiles of 16 ranks
+// (prefill), plus one "aux" index for the gather / pair weights; z = K chunks
+// (prefill forms, fp16 V) when the rows alone give a sparse grid.
 // At decode (at most 32 rows per expert) a block computes one rank (fp16 V)
 // or four ranks (int3 V) of T for its rows as plain dot products over
 // coalesced chunks of the V rows and the activation rows; per-thread partial
-// sums are added in a fixed tree order.  At prefill a block is 4 waves on
-// every rank tile of its rows on the matrix cores (the activation rows are
-// read once); wave partial sums are added in LDS in wave order.  int3 factors
-// ([talk] MiLo Algorithm, last step: U and V stored as int3) are dequantized
-// in registers: folded into the dot products at decode, to fp16 matrix-core
+// sums are added in a fixed tree order.  At prefill the products run on the
+// matrix cores: 128-row tiles with every rank tile per block where experts
+// average 128 rows or more, else 16-row tiles x groups of rank tiles with
+// wave partial sums added in LDS in wave order; K-chunk partials (fp32) are
+// added in chunk order by a reduce pass.  int3 factors ([talk] MiLo
+// Algorithm, last step: U and V stored as int3) are dequantized in
+// registers: folded into the dot products at decode, to fp16 matrix-core
 // operands at prefill.
 #include "gemm_common.hpp"
 
