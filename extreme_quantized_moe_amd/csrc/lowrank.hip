@@ -46,7 +46,8 @@ struct PrepassArgs {
   uint16_t* xg;       // fp16 [P][K]: row of each pair (small-M experts), or null
   float* pw;          // fp32 [P]: route weight of each pair, or null
   int K, gather_div, num_experts, n_w, rp, max_rank;
-  int aux_y;          // blockIdx.y of the aux blocks (-1: none)
+  int aux_y;          // first blockIdx.y of the aux blocks (-1: none)
+  int aux_parts;      // aux blocks per row tile along y (each copies a share of the rows)
   int dec_max_rows;   // experts with more rows are not gathered
 };
 
@@ -91,6 +92,11 @@ __device__ void prepass_aux(const PrepassArgs& a, int base, int m0, int M, int p
   }
 }
 
+// Aux block test and share for the grid.y layout [rank blocks | aux_parts].
+__device__ __forceinline__ bool is_aux(const PrepassArgs& a) {
+  return a.aux_y >= 0 && (int)blockIdx.y >= a.aux_y;
+}
+
 constexpr int kDotThreads = 512;
 
 // Decode form, fp16 V: block (16-row tile, rank j over all families), THREADS
@@ -109,8 +115,8 @@ __global__ void __launch_bounds__(THREADS) prepass_dot_kernel(PrepassArgs a) {
   RowTile rt;
   if (!find_tile16(a, &rt)) return;
   const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
-  if ((int)blockIdx.y == a.aux_y) {
-    prepass_aux(a, base, m0, M);
+  if (is_aux(a)) {
+    prepass_aux(a, base, m0, M, blockIdx.y - a.aux_y, a.aux_parts);
     return;
   }
   const int RW = a.n_w * a.rp;
@@ -213,8 +219,8 @@ __device__ __forceinline__ bool dot_block(const PrepassArgs& a, DotBlock& b) {
   b.m0 = rt.m0;
   b.M = rt.rows;
   b.base = rt.base;
-  if ((int)blockIdx.y == a.aux_y) {
-    prepass_aux(a, b.base, b.m0, b.M);
+  if (is_aux(a)) {
+    prepass_aux(a, b.base, b.m0, b.M, blockIdx.y - a.aux_y, a.aux_parts);
     return false;
   }
   b.RW = a.n_w * a.rp;
@@ -596,8 +602,8 @@ __global__ void __launch_bounds__(64 * NWAVES) prepass_q_kernel(PrepassArgs a) {
   RowTile rt;
   if (!find_tile16(a, &rt)) return;
   const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
-  if ((int)blockIdx.y == a.aux_y) {
-    prepass_aux(a, base, m0, M);
+  if (is_aux(a)) {
+    prepass_aux(a, base, m0, M, blockIdx.y - a.aux_y, a.aux_parts);
     return;
   }
   const int RW = a.n_w * a.rp;
@@ -722,6 +728,7 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
   a.rp = p.rp;
   a.max_rank = d->max_rank;
   a.aux_y = aux_blocks ? rank_blocks : -1;
+  a.aux_parts = 1;
   a.dec_max_rows = p.dec_max_rows;
   a.tpart = nullptr;
   a.ks_steps = d->K / 32;
@@ -730,8 +737,11 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
     constexpr int kNJ3 = 4;
     const int nj = lrq ? kNJ3 : 1;
     const int rank_groups = p.rp ? d->n_w * p.rp / nj : 0;
+    // the gathered-row copy (up to 16 rows of K) is spread over eight blocks
+    // per tile, so it does not outlast the rank blocks
     a.aux_y = aux_blocks ? rank_groups : -1;
-    dim3 grid(p.lr_tiles, rank_groups + aux_blocks);
+    a.aux_parts = need_xg ? 8 : 1;
+    dim3 grid(p.lr_tiles, rank_groups + aux_blocks * a.aux_parts);
     if (lrq) hipLaunchKernelGGL(prepass_dotq_kernel<kNJ3>, grid, dim3(kDotThreads), 0, st, a);
     else if (d->K <= 4096) hipLaunchKernelGGL(prepass_dot_kernel<256>, grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL(prepass_dot_kernel<512>, grid, dim3(512), 0, st, a);
