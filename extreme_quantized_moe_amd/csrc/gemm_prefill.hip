@@ -68,7 +68,7 @@ template <int NW, bool LRQ>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_prefill_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const CodeConsts kc = make_code_consts();
   RowTile rt;
   if (!find_row_tile(a.offsets, a.num_experts, a.pre_min_rows, kBM, blockIdx.y, a.rp ? a.rank[0] : nullptr,
@@ -85,7 +85,6 @@ gemm_prefill_kernel(GemmArgs a) {
   // column chunk p ^ (r % 16), so a fragment read (16 rows, one chunk) hits
   // 16 different slots.  Rows past the expert's count read its first row
   // instead: they only feed output rows that are not stored.
-  (void)tid;
   const int srow = 4 * wave + (lane >> 4);
   int xrow[8];
 #pragma unroll

@@ -62,7 +62,7 @@ __device__ __forceinline__ bool find_tile16(const PrepassArgs& a, RowTile* t) {
 // `part` of `parts` of the rows' 16-byte chunks (the weights with part 0).
 __device__ void prepass_aux(const PrepassArgs& a, int base, int m0, int M, int part = 0, int parts = 1) {
   const int rows = (M - m0) < 16 ? (M - m0) : 16;
-  if (a.pw && part == 0 && threadIdx.x < rows) {
+  if (a.pw && part == 0 && (int)threadIdx.x < rows) {
     const int i = base + m0 + threadIdx.x;
     a.pw[i] = a.slot_w[a.sorted_pairs[i]];
   }
@@ -88,7 +88,7 @@ __device__ void prepass_aux(const PrepassArgs& a, int base, int m0, int M, int p
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (o0 + u * blockDim.x < o_end) *(u32x4*)(a.xg + dst[u]) = v[u];
+      if (o0 + u * (int)blockDim.x < o_end) *(u32x4*)(a.xg + dst[u]) = v[u];
   }
 }
 
