@@ -144,7 +144,8 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
     p->pre_launch = 1;
   }
   p->dec_max_rows = 16 * p->dec_mt;
-  p->pre_tiles = (P + 127) / 128 + d->num_experts;
+  p->pre_bm = P >= 256 * d->num_experts ? 128 : 64;
+  p->pre_tiles = (P + p->pre_bm - 1) / p->pre_bm + d->num_experts;
 
   if (p->dec_mt) {
     // persistent grid: two blocks per CU.  Split K only when it shortens the

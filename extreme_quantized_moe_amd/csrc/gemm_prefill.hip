@@ -26,12 +26,12 @@
 
 namespace milo {
 
-constexpr int kBM = 128;                 // rows per block
-constexpr int kMT = kBM / 16;            // m-tiles per wave
 constexpr int kXStride = kTileK;         // LDS row stride in halves (256 B; chunks swizzled)
-constexpr int kXBuf = kBM * kXStride;    // halves per buffer
 constexpr int kExStride = 68;            // floats per row of the SwiGLU exchange
-constexpr size_t kPreLds = 2 * kBM * kExStride * 4 > 2 * kXBuf * 2 ? 2 * kBM * kExStride * 4 : 2 * kXBuf * 2;
+// LDS of a BM-row block: two staging buffers, or the SwiGLU exchange
+constexpr size_t prefill_lds(int bm) {
+  return 2 * bm * kExStride * 4 > 2 * bm * kXStride * 2 ? (size_t)2 * bm * kExStride * 4 : (size_t)2 * bm * kXStride * 2;
+}
 
 // Weight dequantization in packed fp16: from the extracted pair h = (off + q)
 // (exact), q = h - off is exact, and (q - z) s = fma(q, s, -z s) with -z s
@@ -64,14 +64,16 @@ __device__ __forceinline__ f16x8 dequant_step_pk(const uint32_t h[16], int step,
   return __builtin_bit_cast(f16x8, u);
 }
 
-template <int NW, bool LRQ>
+template <int NW, bool LRQ, int BM>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_prefill_kernel(GemmArgs a) {
+  constexpr int kMT = BM / 16;            // m-tiles per wave
+  constexpr int kXBuf = BM * kXStride;     // halves per staging buffer
   extern __shared__ __align__(16) uint16_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const CodeConsts kc = make_code_consts();
   RowTile rt;
-  if (!find_row_tile(a.offsets, a.num_experts, a.pre_min_rows, kBM, blockIdx.y, a.rp ? a.rank[0] : nullptr,
+  if (!find_row_tile(a.offsets, a.num_experts, a.pre_min_rows, BM, blockIdx.y, a.rp ? a.rank[0] : nullptr,
                      a.rp ? a.rank[1] : nullptr, &rt))
     return;
   const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
@@ -80,15 +82,15 @@ gemm_prefill_kernel(GemmArgs a) {
   const bool wave_on = nt < a.n_tiles;
 
   // ---- activation staging, global memory -> LDS without registers: per K
-  // block a wave issues 8 loads of 1 KB, load j filling rows 16 j + 4 wave ..
+  // block a wave issues BM / 16 loads of 1 KB, load j filling rows 16 j + 4 wave ..
   // + 3 (lane l: row + l / 16, 16-byte slot l % 16).  Slot p of row r holds
   // column chunk p ^ (r % 16), so a fragment read (16 rows, one chunk) hits
   // 16 different slots.  Rows past the expert's count read its first row
   // instead: they only feed output rows that are not stored.
   const int srow = 4 * wave + (lane >> 4);
-  int xrow[8];
+  int xrow[BM / 16];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < BM / 16; ++j) {
     const int m = m0 + srow + 16 * j;
     const int i = base + (m < M ? m : m0);
     xrow[j] = a.gather_div > 0 ? a.sorted_pairs[i] / a.gather_div : i;
@@ -96,7 +98,7 @@ gemm_prefill_kernel(GemmArgs a) {
   const uint16_t* xcol = a.x + 8 * ((lane & 15) ^ (srow & 15));
   auto stage_x = [&](int kb, int buf) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < BM / 16; ++j)
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(xcol + (size_t)xrow[j] * a.K + (size_t)kb * kTileK),
           (__attribute__((address_space(3))) void*)(lds + buf * kXBuf + (16 * j + 4 * wave) * kXStride), 16, 0, 0);
@@ -226,7 +228,7 @@ gemm_prefill_kernel(GemmArgs a) {
     // waves with f == 1 (W3) hand their tile to the partner wave (wave - 1)
     // rows padded to kExStride floats: the four row groups of a wave's
     // accumulators then fall on different LDS banks
-    float* ex = (float*)lds + (wave >> 1) * (kBM * kExStride);
+    float* ex = (float*)lds + (wave >> 1) * (BM * kExStride);
     if (wave_on && f == 1) {
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt)
@@ -280,15 +282,27 @@ gemm_prefill_kernel(GemmArgs a) {
 int32_t launch_gemm_prefill(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st) {
   if (!p.pre_launch) return MILO_OK;
   GemmArgs a = make_gemm_args(d, p, ws);
-  const size_t lds_bytes = kPreLds;
-  if (d->n_w == 2) {
-    dim3 grid((p.n_tiles + 1) / 2, p.pre_tiles);
-    if (a.lrq) hipLaunchKernelGGL((gemm_prefill_kernel<2, true>), grid, dim3(256), lds_bytes, st, a);
-    else hipLaunchKernelGGL((gemm_prefill_kernel<2, false>), grid, dim3(256), lds_bytes, st, a);
+  // 128-row tiles where experts average 256 rows or more, else 64-row tiles
+  // (less padding and twice the blocks for mid-sized experts)
+  const dim3 grid(d->n_w == 2 ? (p.n_tiles + 1) / 2 : (p.n_tiles + 3) / 4, p.pre_tiles);
+  if (p.pre_bm == 128) {
+    const size_t lds = prefill_lds(128);
+    if (d->n_w == 2) {
+      if (a.lrq) hipLaunchKernelGGL((gemm_prefill_kernel<2, true, 128>), grid, dim3(256), lds, st, a);
+      else hipLaunchKernelGGL((gemm_prefill_kernel<2, false, 128>), grid, dim3(256), lds, st, a);
+    } else {
+      if (a.lrq) hipLaunchKernelGGL((gemm_prefill_kernel<1, true, 128>), grid, dim3(256), lds, st, a);
+      else hipLaunchKernelGGL((gemm_prefill_kernel<1, false, 128>), grid, dim3(256), lds, st, a);
+    }
   } else {
-    dim3 grid((p.n_tiles + 3) / 4, p.pre_tiles);
-    if (a.lrq) hipLaunchKernelGGL((gemm_prefill_kernel<1, true>), grid, dim3(256), lds_bytes, st, a);
-    else hipLaunchKernelGGL((gemm_prefill_kernel<1, false>), grid, dim3(256), lds_bytes, st, a);
+    const size_t lds = prefill_lds(64);
+    if (d->n_w == 2) {
+      if (a.lrq) hipLaunchKernelGGL((gemm_prefill_kernel<2, true, 64>), grid, dim3(256), lds, st, a);
+      else hipLaunchKernelGGL((gemm_prefill_kernel<2, false, 64>), grid, dim3(256), lds, st, a);
+    } else {
+      if (a.lrq) hipLaunchKernelGGL((gemm_prefill_kernel<1, true, 64>), grid, dim3(256), lds, st, a);
+      else hipLaunchKernelGGL((gemm_prefill_kernel<1, false, 64>), grid, dim3(256), lds, st, a);
+    }
   }
   return hip_status(hipGetLastError(), "gemm_prefill_kernel launch");
 }

@@ -236,7 +236,8 @@ struct GemmPlan {
   int dec_ksplit;    // split-K factor of the small-M kernel
   int dec_blocks;    // persistent grid of the small-M kernel
   int pre_launch;    // launch the tile kernel
-  int pre_tiles;     // grid.x bound of the tile kernel
+  int pre_tiles;     // grid.y bound of the tile kernel (row tiles)
+  int pre_bm;        // rows per block of the tile kernel (64 or 128)
   // workspace carve-up (byte offsets)
   size_t off_t, off_xg, off_pw, off_dec_part, off_tpart, total;
 };

@@ -175,13 +175,14 @@ def test_prefill_ragged_tiles(T):
     assert_close(got, want, f"prefill T={T}")
 
 
-@pytest.mark.parametrize("T,K,epi", [(300, 1024, "swiglu"), (300, 512, "route"), (200, 2048, "route"),
-                                      (260, 512, "swiglu")])
+@pytest.mark.parametrize("T,K,epi", [(400, 1024, "swiglu"), (300, 512, "route"), (200, 2048, "route"),
+                                      (400, 512, "swiglu")])
 def test_prefill_large_experts(T, K, epi):
     """At least 128 pairs per expert on average: the low-rank pre-pass runs on
     128-row tiles with every rank tile per block (ragged last tiles, a rank-0
     expert, ranks that are not multiples of 16), with K split over blocks at
-    K >= 1024 and unsplit at K = 512."""
+    K >= 1024 and unsplit at K = 512; the tile GEMM takes 128-row blocks at
+    T = 400 (at least 256 pairs per expert) and 64-row blocks below."""
     m = _m()
     epilogue = {"swiglu": m.EPI_SWIGLU, "route": m.EPI_ROUTE_SCALE}[epi]
     got, want = _moe_case(E=3, S=0, N=128, K=K, ranks=[40, 0, 64], T=T, k=2,
