@@ -181,7 +181,8 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
     // (counted without partial tiles) fill about one block per CU, at least
     // four K blocks per chunk.  Otherwise 16-row tiles x groups of four rank
     // tiles, K split while they number fewer than kPrepassBlocks, keeping at
-    // least one batch of loads (4 waves x 4 steps of 32) per chunk.
+    // least one batch of loads (4 waves x 4 steps of 32) per chunk, and only
+    // below 64 blocks.
     int ks;
     if (P >= 128 * d->num_experts) {
       p->lr_mt = kPrepassTileRows / 16;
@@ -196,7 +197,10 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
       p->lr_mt = 1;
       const int tpb = p->lr_tiles_per_block < 4 ? p->lr_tiles_per_block : 4;
       const int est = ((P + 15) / 16) * (nrt / tpb);
-      ks = (kPrepassBlocks + est - 1) / est;
+      // a split costs a reduce launch: it pays only where the unsplit grid
+      // leaves most of the GPU idle (measured: 8 to 16 blocks gain three- to
+      // fivefold, 128 to 256 blocks lose)
+      ks = est < 64 ? (kPrepassBlocks + est - 1) / est : 1;
       const int ks_max = (d->K / 32) / 16;
       if (ks > ks_max) ks = ks_max;
       if (ks < 1) ks = 1;
