@@ -24,6 +24,7 @@ constexpr int kTileSzWords = 128;  // 64 rows x 2 groups
 constexpr int kGroup = 64;
 constexpr int kMaxRank = 64;
 constexpr int kDecodeMaxRows = 32;  // largest expert row count of the small-M path
+constexpr int64_t kSmallMatrixElems = (int64_t)1 << 22;  // N x K at most: mid-sized experts take the tile kernel
 constexpr int kPrepassTileRows = 128;  // rows per block of the fp16 prefill pre-pass for large experts
 constexpr int kPrepassBlocks = 512; // the fp16 prefill pre-pass splits K until its grid has about this many blocks
 
