@@ -391,7 +391,19 @@ def main():
         w0 = works[0]
     tokens_per_s = cfg.T / (ms_step / 1000.0)
     prefill = cfg.T * cfg.k / cfg.E > 64
-    kname = "gemm_prefill_kernel<2> (gate/up + SwiGLU)" if prefill else "gemm_decode_kernel<MT,2> (gate/up + SwiGLU)"
+    # the kernels the library's automatic path launches for the gate/up call:
+    # small-M only up to 32 rows per expert; small matrices (N K <= 2^22) with
+    # experts averaging 16+ rows: the 64-row tile kernel only; else both
+    pairs = cfg.T * (cfg.k + cfg.S)
+    ET = cfg.E + cfg.S
+    if prefill:
+        kname = "gemm_prefill_kernel<2,...,128> (gate/up + SwiGLU)"
+    elif cfg.T <= 32 or args.path == "decode":
+        kname = "gemm_decode_kernel<MT,2> (gate/up + SwiGLU)"
+    elif args.path == "prefill" or (cfg.F * cfg.H <= (1 << 22) and pairs >= 16 * ET):
+        kname = "gate/up call: gemm_prefill_kernel<2,...> (tile kernel for every expert)"
+    else:
+        kname = "gate/up call: gemm_decode_kernel<MT,2> + gemm_prefill_kernel<2,...> (both paths)"
     if prefill:
         achieved = k_flops / (k13_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,

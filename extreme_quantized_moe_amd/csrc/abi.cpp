@@ -139,6 +139,12 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
     p->pre_launch = 1;
   } else if (rows_bound <= kDecodeMaxRows) {
     p->dec_mt = mt_for(rows_bound);
+  } else if ((int64_t)d->N * d->K <= kSmallMatrixElems && P >= 16 * d->num_experts) {
+    // small matrices, experts averaging 16 rows or more: the tile kernel for
+    // every expert (measured: 1408 x 2048 experts, 31 rows on average,
+    // 0.205 ms per layer with both paths -> 0.198 ms)
+    p->dec_mt = 0;
+    p->pre_launch = 1;
   } else {
     // both paths: the small-M kernel takes experts of up to 32 rows (two
     // m-tiles), or for small matrices only those of up to 16 rows, the tile
