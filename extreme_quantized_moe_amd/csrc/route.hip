@@ -196,7 +196,11 @@ __device__ int block_exclusive_scan(int v, int* lds, int* total) {
   return incl - v;
 }
 
-template <int LANES>
+// NV: experts per token row this instantiation handles (LANES = 1: 8 or 16
+// in registers; LANES = 4: 32, 64, 128 or 256, a quarter per thread); one
+// width per kernel keeps each kernel's code small (a single block runs it
+// cold from the instruction cache).
+template <int LANES, int NV>
 __global__ void __launch_bounds__(LANES * kRouteBlock)
 route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int renorm,
            int32_t* __restrict__ ids, float* __restrict__ topw, float* __restrict__ slot_w,
@@ -229,15 +233,8 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
     int bi[kMaxK];
     float den;
     float mx1 = 0.f;
-    if constexpr (LANES == 1) {
-      if (E <= 8) topk_regs<8>(row, E, k, bv, bi, mx1, den);
-      else topk_regs<16>(row, E, k, bv, bi, mx1, den);
-    } else {
-      if (E <= 32) topk_lanes<4, 8>(row, E, k, q, bv, bi, den);
-      else if (E <= 64) topk_lanes<4, 16>(row, E, k, q, bv, bi, den);
-      else if (E <= 128) topk_lanes<4, 32>(row, E, k, q, bv, bi, den);
-      else topk_lanes<4, 64>(row, E, k, q, bv, bi, den);
-    }
+    if constexpr (LANES == 1) topk_regs<NV>(row, E, k, bv, bi, mx1, den);
+    else topk_lanes<4, NV / 4>(row, E, k, q, bv, bi, den);
     const float mx = bv[0];
     float sel[kMaxK];
     float selsum = 0.f;
@@ -400,12 +397,16 @@ int32_t launch_route(const float* logits, int T, int E, int k, int S, int renorm
   const int nblocks = (T + kRouteBlock - 1) / kRouteBlock;
   int32_t* counts = (int32_t*)ws;
   // one thread per token up to 16 experts, four above (shorter selection chains)
-  if (E <= 16)
-    hipLaunchKernelGGL(route_topk<1>, dim3(nblocks), dim3(kRouteBlock), 0, st, logits, T, E, k, S, renorm, ids,
-                       w, slot_w, sorted_pairs, pair_pos, offsets, counts);
-  else
-    hipLaunchKernelGGL(route_topk<4>, dim3(nblocks), dim3(4 * kRouteBlock), 0, st, logits, T, E, k, S, renorm,
-                       ids, w, slot_w, sorted_pairs, pair_pos, offsets, counts);
+#define MILO_ROUTE_LAUNCH(L, NV)                                                                             \
+  hipLaunchKernelGGL((route_topk<L, NV>), dim3(nblocks), dim3(L * kRouteBlock), 0, st, logits, T, E, k, S, \
+                     renorm, ids, w, slot_w, sorted_pairs, pair_pos, offsets, counts)
+  if (E <= 8) MILO_ROUTE_LAUNCH(1, 8);
+  else if (E <= 16) MILO_ROUTE_LAUNCH(1, 16);
+  else if (E <= 32) MILO_ROUTE_LAUNCH(4, 32);
+  else if (E <= 64) MILO_ROUTE_LAUNCH(4, 64);
+  else if (E <= 128) MILO_ROUTE_LAUNCH(4, 128);
+  else MILO_ROUTE_LAUNCH(4, 256);
+#undef MILO_ROUTE_LAUNCH
   int32_t rc = hip_status(hipGetLastError(), "route_topk launch");
   if (rc != MILO_OK || nblocks == 1) return rc;
   hipLaunchKernelGGL(route_scan, dim3(1), dim3(kRouteBlock), 0, st, nblocks, E + S, counts, offsets);
