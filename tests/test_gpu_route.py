@@ -46,6 +46,16 @@ def test_route_ties(T):
     _check(logits, 3, 1, True)
 
 
+@pytest.mark.parametrize("T,E,k,S", [(256, 64, 6, 2), (100, 32, 4, 0)])
+def test_route_ties_four_lanes(T, E, k, S):
+    """More than 16 experts: four threads per token, each with its own top-k
+    over a quarter of the row, merged by (larger value, then lower id).
+    Integer logits make ties within and across the quarters common."""
+    g = torch.Generator().manual_seed(T + E)
+    logits = torch.randint(-2, 3, (T, E), generator=g).float()
+    _check(logits, k, S, False)
+
+
 def test_route_all_to_one_expert():
     logits = torch.full((300, 8), -5.0)
     logits[:, 3] = 5.0
