@@ -162,6 +162,11 @@ gemm_prefill_kernel(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       const uint16_t* xb = lds + buf * kXBuf;
+      // raised wave priority while a block's products issue, back to normal
+      // at the barrier: the two waves sharing a SIMD drift out of phase, one
+      // issuing products while the other waits at its barrier or on loads
+      // (measured: gate/up 93.5 -> 84.6 us on 64-row tiles, -1.6 % on 128)
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         f16x8 wf[4];
@@ -180,6 +185,7 @@ gemm_prefill_kernel(GemmArgs a) {
         wz[0] = nz[0];
         wz[1] = nz[1];
       }
+      __builtin_amdgcn_s_setprio(0);
       __syncthreads();   // waits for the staging loads (vmcnt) first
     }
   } else {
