@@ -190,6 +190,19 @@ def test_prefill_large_experts(T, K, epi):
     assert_close(got, want, f"large experts T={T} K={K} {epi}")
 
 
+@pytest.mark.parametrize("epi,lr", [("swiglu", "fp16"), ("route", "fp16"), ("swiglu", "int3")])
+def test_auto_small_matrices_sparse_batch(epi, lr):
+    """Automatic path, small matrices, experts averaging under 16 rows with
+    one heavy expert (every token): the small-M kernel takes the experts of
+    up to 16 rows in one launch, the tile kernel the heavy one."""
+    m = _m()
+    epilogue = {"swiglu": m.EPI_SWIGLU, "route": m.EPI_ROUTE_SCALE}[epi]
+    ranks = [8, 16, 32, 64, 0, 40, 24, 16, 8, 32, 48, 64, 16, 0, 32, 8]
+    got, want = _moe_case(E=16, S=0, N=128, K=256, ranks=ranks, T=40, k=2, epilogue=epilogue,
+                          path=PATHS["auto"], seed=77, skew=3, lr_format=lr)
+    assert_close(got, want, f"auto sparse {epi} {lr}")
+
+
 @pytest.mark.parametrize("path", ["decode", "prefill"])
 def test_zero_weights_isolate_lowrank(path):
     m = _m()
