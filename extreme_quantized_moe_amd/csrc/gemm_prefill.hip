@@ -5,21 +5,22 @@
 // with fused dequantization; asynchronous global loads overlap memory with
 // compute.  MiLo Algorithm: W_out = W_quant + U V.
 //
-// Grid: x = n-tile groups (fastest), y = 128-row tiles, so the blocks that
-// run together share activation rows (L2 hits) while the weights stream.
-// Block = 128 rows of one expert (pairs in sorted order) x 4 waves.  Each wave
+// Grid: x = n-tile groups (fastest), y = row tiles of BM rows (128 where
+// experts average 256 rows or more, else 64), so the blocks that run together
+// share activation rows (L2 hits) while the weights stream.
+// Block = BM rows of one expert (pairs in sorted order) x 4 waves.  Each wave
 // owns one 64-wide output tile of one weight family (SWIGLU: waves (W1, W3) x
 // two n-tiles; otherwise four n-tiles of the one family), so every packed
 // weight tile is read and dequantized by exactly one wave.  Activation rows
-// go straight from global memory into LDS (global_load_lds_dwordx4: 128
-// rows x 128 K, double buffered, 16-byte chunks XOR-swizzled per row against
-// bank conflicts) and are shared by the four waves; the next K block's
+// go straight from global memory into LDS (global_load_lds_dwordx4: BM rows
+// x 128 K, double buffered, 16-byte chunks XOR-swizzled per row against bank
+// conflicts) and are shared by the four waves; the next K block's
 // activations (into LDS) and weights (into registers) load while the current
 // one is computed.  Weights are dequantized in registers (int3 pair
 // extraction, then packed fp16: subtract the offset, one fused multiply-add
 // by the scale with -z s) and multiplied on v_mfma_f32_16x16x32_f16 with fp32
-// accumulation; the dequantization of K step s + 1 is interleaved with the
-// products of step s.
+// accumulation; each K block is one branch-free region the scheduler
+// interleaves, issued at raised wave priority.
 // Epilogue: low-rank term as two more matrix-core K-steps per 32 ranks, then
 // SWIGLU through LDS, or fp16 store, or route-weighted fp32 scatter.
 #include "gemm_common.hpp"
