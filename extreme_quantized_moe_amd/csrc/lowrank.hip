@@ -734,15 +734,19 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
   a.ks_steps = d->K / 32;
   a.num_pairs = d->num_pairs;
   if (per == 1) {                                   // decode
-    constexpr int kNJ3 = 4;
-    const int nj = lrq ? kNJ3 : 1;
+    // int3 V: two ranks per block, one for long rows (more blocks in flight:
+    // C2 gate/up 10.7 -> 8.7 us with two instead of four, down 16.8 -> 12.1 us
+    // with one)
+    const int nj = lrq ? (d->K > 4096 ? 1 : 2) : 1;
     const int rank_groups = p.rp ? d->n_w * p.rp / nj : 0;
     // the gathered-row copy (up to 16 rows of K) is spread over eight blocks
     // per tile, so it does not outlast the rank blocks
     a.aux_y = aux_blocks ? rank_groups : -1;
     a.aux_parts = need_xg ? 8 : 1;
     dim3 grid(p.lr_tiles, rank_groups + aux_blocks * a.aux_parts);
-    if (lrq) hipLaunchKernelGGL(prepass_dotq_kernel<kNJ3>, grid, dim3(kDotThreads), 0, st, a);
+    if (lrq && nj == 1) hipLaunchKernelGGL(prepass_dotq_kernel<1>, grid, dim3(kDotThreads), 0, st, a);
+    else if (lrq && nj == 2) hipLaunchKernelGGL(prepass_dotq_kernel<2>, grid, dim3(kDotThreads), 0, st, a);
+    else if (lrq) hipLaunchKernelGGL(prepass_dotq_kernel<4>, grid, dim3(kDotThreads), 0, st, a);
     else if (d->K <= 4096) hipLaunchKernelGGL(prepass_dot_kernel<256>, grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL(prepass_dot_kernel<512>, grid, dim3(512), 0, st, a);
     return hip_status(hipGetLastError(), "prepass_dot_kernel launch");
