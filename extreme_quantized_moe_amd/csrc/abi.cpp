@@ -119,6 +119,26 @@ static int32_t validate_gemm(const milo_gemm_desc* d) {
   return MILO_OK;
 }
 
+// Compute units of the current device (cached per device; 256, the MI355X
+// count, if the runtime cannot tell, e.g. on a host without a GPU where only
+// workspace sizes are queried).
+static int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  cached[dev] = cus;
+  return cus;
+}
+
 int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
   memset(p, 0, sizeof *p);
   p->n_tiles = d->N / kTileRows;
@@ -158,11 +178,12 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
   p->pre_tiles = (P + p->pre_bm - 1) / p->pre_bm + d->num_experts;
 
   if (p->dec_mt) {
-    // persistent grid: two blocks per CU.  Split K only when it shortens the
+    // persistent grid: two blocks per compute unit (the kernel's register
+    // budget allows two).  Split K only when it shortens the
     // busiest block's work (in items) to under 3/4 of the unsplit round: a
     // split costs a reduce launch, and e.g. 448 items take one round whether
     // split or not.  Keep at least four K blocks per split (one per wave).
-    const int slots = 512;
+    const int slots = 2 * device_cu_count();
     const int active = d->num_experts < P ? d->num_experts : P;
     const int items = active * p->n_tiles;
     int ks_max = p->kblocks / 4;

@@ -25,6 +25,7 @@ struct GemmArgs {
   int N, K, kblocks, n_tiles, gather_div, num_experts, n_w, rp, max_rank;
   int epilogue, ksplit, dec_max_rows, pre_min_rows;
   int m_lo, m_hi;          // row-count range of the experts a decode launch handles
+  int poison_over;         // decode launch: NaN-fill the rows of experts above m_hi
 };
 
 struct GemmPlan;

@@ -69,7 +69,28 @@ struct DecShared {
   int act[kMaxE];
   int rank[2][kMaxE];
   int nact;
+  int over;   // some expert has more rows than this launch handles
 };
+
+// Output rows of experts with more rows than the small-M path takes, when no
+// other launch of the call covers them (the caller's row bound was wrong):
+// they are set to NaN instead of being left unwritten.  Grid-strided over
+// the rows x N outputs of each such expert.
+template <int EPI>
+__device__ void poison_over_rows(const GemmArgs& a, const DecShared& sh) {
+  const int stride = gridDim.x * blockDim.x;
+  for (int e = 0; e < a.num_experts; ++e) {
+    const int base = sh.off[e], M = sh.off[e + 1] - base;
+    if (M <= a.m_hi) continue;
+    const int64_t n = (int64_t)M * a.N;
+    for (int64_t o = blockIdx.x * blockDim.x + threadIdx.x; o < n; o += stride) {
+      const int row = (int)(o / a.N), col = (int)(o - (int64_t)row * a.N);
+      const int i = base + row;
+      if (EPI == MILO_EPI_ROUTE_SCALE) ((float*)a.y)[(size_t)a.sorted_pairs[i] * a.N + col] = __builtin_nanf("");
+      else ((uint16_t*)a.y)[(size_t)i * a.N + col] = 0x7E00u;   // fp16 quiet NaN
+    }
+  }
+}
 
 // fp16 constant fragments: all ones, and the per-slot offset of step `step`
 __device__ __forceinline__ f16x8 ones_frag() {
@@ -237,14 +258,17 @@ gemm_decode_kernel(GemmArgs a) {
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int n = 0;
+    int n = 0, over = 0;
     for (int e = 0; e < a.num_experts; ++e) {
       const int M = sh.off[e + 1] - sh.off[e];
       if (M >= a.m_lo && M <= a.m_hi) sh.act[n++] = e;
+      over |= M > a.m_hi;
     }
     sh.nact = n;
+    sh.over = over;
   }
   __syncthreads();
+  if (a.poison_over && sh.over) poison_over_rows<EPI>(a, sh);
   const int total = __builtin_amdgcn_readfirstlane(sh.nact) * a.n_tiles * a.ksplit;
   if ((int)blockIdx.x >= total) return;
 
@@ -447,6 +471,7 @@ int32_t launch_gemm_decode(const milo_gemm_desc* d, const GemmPlan& p, char* ws,
   a.pw = (const float*)(ws + p.off_pw);
   a.m_lo = 1;
   a.m_hi = p.dec_max_rows;
+  a.poison_over = p.pre_launch ? 0 : 1;   // no tile launch takes the larger experts
   switch (p.dec_mt) {
     case 1: launch_mt<1>(a, d->epilogue, p.dec_blocks, d->num_experts, st); break;
     case 2: launch_mt<2>(a, d->epilogue, p.dec_blocks, d->num_experts, st); break;

@@ -334,9 +334,10 @@ _gemm_ws = {}
 
 
 def _workspace(dev, nbytes):
-    """A scratch workspace per device, grown on demand.  Calls on one stream
-    run in order, so they can share it."""
-    key = dev.index
+    """A scratch workspace per (device, stream), grown on demand.  Calls on
+    one stream run in order, so they can share it; calls on different streams
+    may overlap in time and get different workspaces."""
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
     ws = _gemm_ws.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)

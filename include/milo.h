@@ -405,7 +405,12 @@ typedef struct milo_gemm_desc {
                                    [offsets[e], offsets[e+1])                  */
   int32_t num_pairs;            /* P = offsets[num_experts]                    */
   int32_t max_rows_per_expert;  /* host upper bound on offsets[e+1]-offsets[e]
-                                   (e.g. T for top-k routing); 0 = num_pairs  */
+                                   (e.g. T for top-k routing); 0 = num_pairs.
+                                   The plan is chosen from it without reading
+                                   the device offsets; if an expert exceeds it
+                                   and the plan has no kernel for that many
+                                   rows, that expert's output rows are set to
+                                   NaN (never left unwritten)                 */
   const float* slot_w;          /* ROUTE_SCALE only: float32 [y_rows]          */
   int32_t y_rows;               /* ROUTE_SCALE only: rows of y                 */
   int32_t epilogue;             /* MILO_EPI_*                                  */

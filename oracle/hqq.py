@@ -58,6 +58,21 @@ def hqq_zero_step(w, s, z, beta, p):
     return np.mean(q - (w - we) / s, axis=-1, keepdims=True)
 
 
+def hqq_zero_trajectory(w, s, z0, iters, p=0.7, beta=10.0, kappa=1.01):
+    """The unrounded zero points z_1 .. z_iters of the half-quadratic
+    iteration started at z0 (w: [..., group], s and z0: [..., 1]); the
+    threshold parameter is beta at the first update and grows by the factor
+    kappa after each one.  Returns a list of arrays shaped like z0."""
+    z = np.asarray(z0, dtype=np.float64)
+    out = []
+    b = float(beta)
+    for _ in range(iters):
+        z = hqq_zero_step(w, s, z, b, p)
+        b *= kappa
+        out.append(z)
+    return out
+
+
 def quantize_hqq_int3(W, group=64, iters=20, p=0.7, beta=10.0, kappa=1.01):
     """W [R][K] -> (codes uint8 [R][K], scale fp16 [R][K/group], zero fp16
     [R][K/group]); scale is the RTN scale."""
@@ -66,13 +81,10 @@ def quantize_hqq_int3(W, group=64, iters=20, p=0.7, beta=10.0, kappa=1.01):
     _, s16, z16 = quantize_rtn_int3(W, group)
     w = W.astype(np.float64).reshape(R, K // group, group)
     s = s16.astype(np.float64)[..., None]
-    z = z16.astype(np.float64)[..., None]
-    best = z.copy()
+    z0 = z16.astype(np.float64)[..., None]
+    best = z0.copy()
     best_err = group_mae(w, s, best)
-    b = float(beta)
-    for _ in range(iters):
-        z = hqq_zero_step(w, s, z, b, p)
-        b *= kappa
+    for z in hqq_zero_trajectory(w, s, z0, iters, p, beta, kappa):
         zc = f16_sat(z).astype(np.float64)
         err = group_mae(w, s, zc)
         better = err < best_err

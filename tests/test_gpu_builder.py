@@ -4,7 +4,11 @@ the oracle's randomized algorithm with the same test matrix and the exact
 SVD), on a flat quantization-noise spectrum (energies and singular values),
 and the quantize <-> compensate refinement (first iteration bit-exact codes,
 later iterations within a statistical bar, fixed point on grid weights,
-rank 0 = plain RTN)."""
+rank 0 = plain RTN).  Integer outputs of later rounds are checked for
+validity, not by share: a round quantizes W - L with L the previous round's
+factors (formed in fp32 on the GPU), so the check re-quantizes W - U V with
+the GPU's own previous-round factors in float64 and allows differences only
+at rounding ties (tests/int_checks.py)."""
 import numpy as np
 import pytest
 import torch
@@ -12,6 +16,7 @@ import torch
 import oracle
 from oracle import builder as OB
 from tests.gpu_helpers import to_np
+from tests.int_checks import assert_hqq_valid, assert_rtn_valid
 
 pytestmark = pytest.mark.gpu
 
@@ -106,20 +111,37 @@ def test_build_first_iteration(N, K, r, p):
     assert e_gpu < np.linalg.norm(R)
 
 
+def _prev_round_residual(m, W, r, iters, om, q, quantizer="rtn"):
+    """W - U V in float64 with the GPU's factors after iters rounds (the
+    builder is deterministic, so these are the factors round iters + 1 of a
+    longer run starts from)."""
+    out = m.build_compensator(W.cuda(), r, iters, om[:iters].cuda(), power_iters=q, quantizer=quantizer)
+    torch.cuda.synchronize()
+    U, V = to_np(out[3]).astype(np.float64), to_np(out[4]).astype(np.float64)
+    return W.numpy().astype(np.float64) - U @ V
+
+
+# W - U V differs between fp32 (GPU) and float64 by a few 1e-9 at weights of
+# 0.02 with scales near 0.017: w / s moves by under 1e-6 and the group extremes
+# by under 1e-6 relative
+_REL, _EPS = 1e-6, 1e-5
+
+
 def test_build_refinement_iterations():
-    """iters = 3: the GPU and the oracle follow the same steps with the same
-    test matrices; quantization decisions of later iterations are taken on
-    W - L with L from fp32 vs fp64 arithmetic, so a few codes near a rounding
-    tie may differ: compare the share of equal codes and the final error."""
+    """iters = 3: the final round's codes, scales and zero points are the RTN
+    quantization of W - U2 V2 (the GPU's round-2 factors) except at rounding
+    ties; the compensated error follows the oracle's float64 refinement with
+    the same test matrices."""
     m = _m()
     N, K, r, p = 512, 512, 16, 8
     W = _weights(N, K, 11)
     om = torch.stack([_omega(r + p, K, 20 + t) for t in range(3)])
     codes, scale, zero, U, V, s = m.build_compensator(W.cuda(), r, 3, om.cuda(), power_iters=2)
     torch.cuda.synchronize()
+    Wp = _prev_round_residual(m, W, r, 2, om, 2)
+    nsz, nc = assert_rtn_valid(Wp, to_np(codes), to_np(scale), to_np(zero), _REL, _EPS, "round 3 of 3")
+    print(f"refinement: {nsz} scale/zero groups and {nc} codes excused as rounding ties")
     ref = OB.build_ref(W.numpy(), r, 3, om.numpy(), 2)
-    same = np.mean(to_np(codes) == ref["codes"])
-    assert same >= 0.999, same
     Wd = oracle.dequant_int3(to_np(codes), to_np(scale), to_np(zero))
     L = to_np(U).astype(np.float64) @ to_np(V).astype(np.float64)
     err = np.linalg.norm(W.numpy().astype(np.float64) - Wd - L)
@@ -152,23 +174,29 @@ def test_build_rank_zero_is_rtn():
 
 
 def test_build_with_hqq_quantizer():
-    """quantizer "hqq", 2 iterations: the first iteration's codes follow the
-    HQQ-style quantizer (against the oracle's float64 run, by share: zero
-    candidates whose errors tie to the last bits may differ), and the final
-    codes and compensated error follow the oracle's refinement."""
+    """quantizer "hqq", 2 iterations: the first round is the HQQ-style
+    quantizer on W (validated against the oracle as in the quantizer's own
+    test: zero points equal except at error ties); the second is the same
+    quantizer on W - U1 V1 (the GPU's round-1 factors, formed in fp32), so
+    the tie and rounding-sensitivity allowances widen to the size of that
+    fp32 rounding; codes are the codes at the stored zero point everywhere;
+    the compensated error follows the oracle's refinement."""
     m = _m()
     N, K, r, p = 512, 512, 16, 8
     W = _weights(N, K, 50)
     om = torch.stack([_omega(r + p, K, 60 + t) for t in range(2)])
-    c1 = m.build_compensator(W.cuda(), r, 1, om[:1].cuda(), power_iters=2, quantizer="hqq")[0]
+    first = m.build_compensator(W.cuda(), r, 1, om[:1].cuda(), power_iters=2, quantizer="hqq")
     out = m.build_compensator(W.cuda(), r, 2, om.cuda(), power_iters=2, quantizer="hqq")
     torch.cuda.synchronize()
-    from oracle import hqq as HQ
-    q, _, _ = HQ.quantize_hqq_int3(W.numpy())
-    assert np.mean(to_np(c1) == q) >= 0.9999
-    ref = OB.build_ref(W.numpy(), r, 2, om.numpy(), 2, quantizer="hqq")
+    c1, s1, z1 = (to_np(t) for t in first[:3])
+    assert_hqq_valid(W.numpy().astype(np.float64), c1, s1, z1, "hqq build round 1")
     codes, scale, zero, U, V, s = (to_np(t) for t in out)
-    assert np.mean(codes == ref["codes"]) >= 0.999
+    U1, V1 = to_np(first[3]).astype(np.float64), to_np(first[4]).astype(np.float64)
+    Wp = W.numpy().astype(np.float64) - U1 @ V1
+    nd = assert_hqq_valid(Wp, codes, scale, zero, "hqq build round 2", tie_rel=_REL, traj_rel=_REL,
+                          code_eps=_EPS)
+    print(f"hqq build round 2: {nd} zero points differ from the float64 run")
+    ref = OB.build_ref(W.numpy(), r, 2, om.numpy(), 2, quantizer="hqq")
     Wd = oracle.dequant_int3(codes, scale, zero)
     err = np.linalg.norm(W.numpy().astype(np.float64) - Wd - U.astype(np.float64) @ V.astype(np.float64))
     assert abs(err - ref["errors"][-1]) <= 1e-3 * ref["errors"][-1]

@@ -98,6 +98,32 @@ def _check_out(cfg, layer, lay, toks, ncols, seed, lr_format="fp16"):
     assert_close(got, ref["out"], f"{cfg.name} out (tokens {list(toks)}, {len(cols)} columns, {lr_format} factors)")
 
 
+def _check_tokens_full(cfg, layer, lay, toks, what):
+    """Every column of G for every pair of the tokens toks, and every column
+    of their layer output (the oracle recomputes those tokens' expert FFNs in
+    full).  Returns the (rel_fro, max_abs) of both checks."""
+    toks = np.asarray(sorted(set(int(t) for t in toks)))
+    X = lay.X.cpu().numpy()[toks].astype(np.float64)
+    logits = lay.logits.cpu().numpy()[toks]
+
+    def get_expert(e):
+        d = _expert_host(cfg, layer, e, lay.ranks[e], ("W1", "W3", "W2"))
+        return oracle.quantize_expert(d)
+
+    ref = oracle.moe_layer_ref(X, logits, get_expert, cfg.k, cfg.S, cfg.renormalize)
+    pair_pos = lay.route["pair_pos"].cpu().numpy()
+    G = lay.G.cpu().numpy()
+    s_loc = sorted(ref["g_pair"])
+    got_g = np.stack([G[pair_pos[toks[s // cfg.slots] * cfg.slots + s % cfg.slots]] for s in s_loc])
+    want_g = np.stack([ref["g_pair"][s] for s in s_loc])
+    g_err = assert_close(got_g, want_g, f"{what}: G ({len(s_loc)} pairs, all {cfg.F} columns)")
+    got_o = lay.out.cpu().numpy().astype(np.float64)[toks]
+    o_err = assert_close(got_o, ref["out"], f"{what}: out ({len(toks)} tokens, all {cfg.H} columns)")
+    print(f"{what}: G rel_fro {g_err[0]:.2e} max_abs {g_err[1]:.2e}; out rel_fro {o_err[0]:.2e} "
+          f"max_abs {o_err[1]:.2e} (bounds 1e-3, 2e-2)")
+    return g_err, o_err
+
+
 def test_c2_full_decode_layer():
     cfg = SC.get_config("C2")
     lay = _run_layer(cfg, 0)
@@ -121,14 +147,35 @@ def test_c3_full_prefill_layer_sampled():
     _check_out(cfg, 0, lay, [0, 1234, 2900, cfg.T - 1], 256, seed=6)
 
 
-@pytest.mark.parametrize("T", [1, 64])
+@pytest.mark.timeout(900)
+def test_c3_full_prefill_tile_edges():
+    """C3 at full size: for every 128-row tile of every expert (the tile
+    kernel's row blocks at prefill), the pairs on its first and last row --
+    all columns of their G rows, and all output columns of their tokens
+    (which brings in every other pair of those tokens as well)."""
+    cfg = SC.get_config("C3")
+    lay = _run_layer(cfg, 0)
+    route = oracle.route_ref(lay.logits.cpu().numpy(), cfg.k, cfg.S, cfg.renormalize)
+    sp, off = route["sorted_pairs"], route["offsets"]
+    np.testing.assert_array_equal(lay.route["offsets"].cpu().numpy(), off)
+    toks = []
+    for e in range(cfg.E + cfg.S):
+        M = int(off[e + 1] - off[e])
+        for m0 in range(0, M, 128):
+            for m in (m0, min(m0 + 127, M - 1)):
+                toks.append(int(sp[off[e] + m]) // cfg.slots)
+    _check_tokens_full(cfg, 0, lay, toks, "C3 tile edges")
+
+
+@pytest.mark.parametrize("T", [1, 8, 32, 64])
 def test_c5_layer_at_batch(T):
-    """One layer of the 32-layer stack at batch 1 (one token, two experts) and
-    64 (two-m-tile decode items)."""
+    """One layer of the 32-layer stack at each batch size the benchmark sweeps:
+    1 (one token, two experts), 8, 32 (two-m-tile decode items at K = 14336)
+    and 64 (both kernels)."""
     cfg = SC.get_config("C5").with_(T=T)
     lay = _run_layer(cfg, 7)
     _check_g(cfg, 7, lay, 32, seed=7)
-    _check_out(cfg, 7, lay, [0] if T == 1 else [5, 17, 40, T - 1], 256, seed=8)
+    _check_out(cfg, 7, lay, [0] if T == 1 else sorted({1, 5, T // 2, T - 1}), 256, seed=8)
 
 
 def test_c2_full_decode_layer_int3_factors():

@@ -48,7 +48,7 @@ def _route(T, E, k, S, seed, skew=None):
 
 
 def _moe_case(E, S, N, K, ranks, T, k, epilogue, path, seed, skew=None, zero_w=False, zero_lr=False,
-              lr_format="fp16", logits=None, max_rows=None, workspace=None):
+              lr_format="fp16", logits=None, max_rows=None, workspace=None, fill=None):
     m = _m()
     ET = E + S
     if logits is None:
@@ -72,7 +72,10 @@ def _moe_case(E, S, N, K, ranks, T, k, epilogue, path, seed, skew=None, zero_w=F
                                lr_format=lr_format)
         fams.append(fam)
         refs.append(ref)
-    if epilogue == m.EPI_ROUTE_SCALE:
+    ydt = torch.float32 if epilogue == m.EPI_ROUTE_SCALE else torch.float16
+    if fill is not None:
+        y = torch.full((P, N), fill, dtype=ydt, device="cuda")
+    elif epilogue == m.EPI_ROUTE_SCALE:
         y = torch.full((P, N), float("nan"), dtype=torch.float32, device="cuda")
     else:
         y = torch.empty((P, N), dtype=torch.float16, device="cuda")
@@ -314,3 +317,25 @@ def test_fp16_factors_beyond_rank_are_never_read(path):
         fam.V[e, r:, :] = float("nan")
     dirty = run()
     assert torch.equal(clean, dirty)
+
+
+@pytest.mark.parametrize("epi", ["swiglu", "route"])
+def test_row_bound_too_small_poisons_rows(epi):
+    """A caller bound below the real rows per expert: the automatic plan is
+    the small-M kernel alone (it takes up to 16 rows per expert here), so the
+    rows of heavier experts have no kernel -- they must come back as NaN, not
+    as whatever the output held, while every other row is correct."""
+    m = _m()
+    E, N, K, T, k = 4, 128, 256, 40, 2
+    e_epi = m.EPI_SWIGLU if epi == "swiglu" else m.EPI_ROUTE_SCALE
+    got, want = _moe_case(E, 0, N, K, [16] * E, T, k, e_epi, PATHS["auto"], 91, skew=0, max_rows=8, fill=0.0)
+    ref_r = oracle.route_ref(_route(T, E, k, 0, 91, 0).numpy(), k, 0, True)
+    off, sp = ref_r["offsets"], ref_r["sorted_pairs"]
+    rows = np.diff(off)
+    assert rows.max() > 16 and rows.min() <= 16, rows
+    for e in range(E):
+        idx = sp[off[e]:off[e + 1]] if e_epi == m.EPI_ROUTE_SCALE else np.arange(off[e], off[e + 1])
+        if rows[e] > 16:
+            assert np.all(np.isnan(got[idx])), f"expert {e} ({rows[e]} rows): rows not poisoned"
+        elif rows[e]:
+            assert_close(got[idx], want[idx], f"expert {e} ({rows[e]} rows) next to a poisoned expert")

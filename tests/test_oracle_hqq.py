@@ -87,3 +87,46 @@ def test_threshold_active_on_unit_scale_weights():
     z = z16.astype(np.float64)[..., None]
     x = w - (np.clip(np.rint(w / s + z), 0, 7) - z) * s
     assert np.count_nonzero(HQ.shrink_lp(x, 10.0, 0.7)) > 0
+
+
+def _golden_group():
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hqq_cases.json")))
+    w = np.zeros(64)
+    w[1] = 7.0
+    w[2:] = np.arange(62) % 7 + 0.25
+    return g, w
+
+
+def test_hqq_trajectory_hand_worked():
+    """Two half-quadratic updates of one unit-scale group with p = 1/2, by
+    hand (tests/golden/hqq_cases.json): the first update uses beta, the
+    second beta * kappa -- a dropped or inverted schedule gives another z2."""
+    g, w = _golden_group()
+    q, s16, z16 = oracle.quantize_rtn_int3(w[None, :].astype(np.float32))
+    assert float(s16[0, 0]) == g["group"]["rtn_scale"] and float(z16[0, 0]) == g["group"]["rtn_zero"]
+    beta = g["beta_num"] / g["beta_den"]
+    ws = w.reshape(1, 1, 64)
+    s = np.ones((1, 1, 1))
+    z0 = np.zeros((1, 1, 1))
+    z2s = []
+    for case in g["cases"]:
+        traj = HQ.hqq_zero_trajectory(ws, s, z0, 2, g["p"], beta, case["kappa"])
+        assert traj[0][0, 0, 0] == pytest.approx(g["iteration_1"]["z"], abs=1e-12)
+        assert traj[1][0, 0, 0] == pytest.approx(case["z2"], abs=1e-12)
+        z2s.append(case["z2"])
+    assert len(set(z2s)) == len(z2s)
+
+
+def test_hqq_quantizer_follows_trajectory():
+    """quantize_hqq_int3 keeps the best candidate among the RTN zero point and
+    f16(z_t) of the trajectory: for the hand-worked group the stored zero is
+    one of those and its error is the least of them."""
+    g, w = _golden_group()
+    beta = g["beta_num"] / g["beta_den"]
+    c, s, z = HQ.quantize_hqq_int3(w[None, :].astype(np.float32), iters=2, p=0.5, beta=beta, kappa=2.0)
+    cands = [0.0, float(np.float16(-0.09)), float(np.float16(g["cases"][0]["z2"]))]
+    errs = [HQ.group_mae(w.reshape(1, 1, 64), np.ones((1, 1, 1)), np.full((1, 1, 1), zc))[0, 0] for zc in cands]
+    assert float(z[0, 0]) in cands
+    assert HQ.group_mae(w.reshape(1, 1, 64), np.ones((1, 1, 1)), np.full((1, 1, 1), float(z[0, 0])))[0, 0] == min(errs)
