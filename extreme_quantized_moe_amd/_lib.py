@@ -11,6 +11,7 @@ STATUS_NAMES = {0: "MILO_OK", 1: "MILO_ERR_NULL", 2: "MILO_ERR_SHAPE", 3: "MILO_
 EPI_NONE, EPI_SWIGLU, EPI_ROUTE_SCALE = 0, 1, 2
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 GEMM_PREPASS_DONE = 1
+STATIC_WORKSPACE_BYTES = 64 << 20
 LR_FP16, LR_INT3 = 0, 1
 QUANT_RTN, QUANT_HQQ = 0, 1
 
@@ -86,6 +87,7 @@ def lib():
         "milo_moe_gemm_workspace_bytes": (sz, [C.POINTER(MiloGemmDesc)]),
         "milo_moe_w3a16_lowrank_gemm": (i32, [C.POINTER(MiloGemmDesc), vp, sz, vp]),
         "milo_moe_lowrank_prepass": (i32, [C.POINTER(MiloGemmDesc), vp, sz, vp]),
+        "milo_moe_w3a16_lowrank_gemm_static": (i32, [C.POINTER(MiloGemmDesc), vp]),
         "milo_moe_combine": (i32, [vp, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():

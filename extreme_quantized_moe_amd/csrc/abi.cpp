@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gemm_common.hpp"
 
 namespace milo {
@@ -540,6 +542,65 @@ int32_t milo_moe_w3a16_lowrank_gemm(const milo_gemm_desc* d, void* workspace, si
   rc = launch_gemm_decode(d, p, ws, st);
   if (rc != MILO_OK) return rc;
   return launch_gemm_prefill(d, p, ws, st);
+}
+
+}  // extern "C"
+
+namespace milo {
+
+// Library-owned scratch of milo_moe_w3a16_lowrank_gemm_static.  Host code
+// never uses the array's name as an address: each device's copy is looked
+// up once (hipGetSymbolAddress, with that device current) and the pointer
+// kept per device.
+static __device__ __align__(256) unsigned char scratch[MILO_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices] = {nullptr};
+static std::mutex g_scratch_mu;
+
+static int32_t static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) MILO_FAIL(MILO_ERR_HIP, "device %d outside 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) MILO_FAIL(MILO_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL on device %d", dev);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MILO_OK;
+}
+
+}  // namespace milo
+
+extern "C" {
+
+int32_t milo_moe_w3a16_lowrank_gemm_static(const milo_gemm_desc* d, void* stream) {
+  g_err[0] = 0;
+  int32_t rc = validate_gemm(d);
+  if (rc != MILO_OK) return rc;
+  if (d->flags) MILO_FAIL(MILO_ERR_ARG, "flags=0x%x: the static-workspace call runs the whole GEMM (flags must be 0)",
+                          d->flags);
+  GemmPlan p;
+  rc = plan_gemm(d, &p);
+  if (rc != MILO_OK || d->num_pairs == 0) return rc;
+  if (p.total > MILO_STATIC_WORKSPACE_BYTES)
+    MILO_FAIL(MILO_ERR_WORKSPACE, "this GEMM needs %zu bytes of workspace, more than the library's static %zu; "
+              "use milo_moe_w3a16_lowrank_gemm with a caller workspace", p.total,
+              (size_t)MILO_STATIC_WORKSPACE_BYTES);
+  void* ws = nullptr;
+  rc = static_scratch(&ws);
+  if (rc != MILO_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  rc = launch_lowrank(d, p, (char*)ws, st);
+  if (rc != MILO_OK) return rc;
+  rc = launch_gemm_decode(d, p, (char*)ws, st);
+  if (rc != MILO_OK) return rc;
+  return launch_gemm_prefill(d, p, (char*)ws, st);
 }
 
 int32_t milo_moe_combine(const float* y, int32_t T, int32_t slots, int32_t H, uint16_t* out,

@@ -466,6 +466,25 @@ int32_t milo_moe_lowrank_prepass(const milo_gemm_desc* desc, void* workspace,
                                  size_t ws_bytes, void* stream);
 
 /*
+ * milo_moe_w3a16_lowrank_gemm without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the scratch lives in a static
+ * device array of MILO_STATIC_WORKSPACE_BYTES inside the library, one copy
+ * per GPU, held until the process ends.  The call allocates nothing (no
+ * hipMalloc, no allocating library routine); the caller still owns every
+ * input and output.  Same descriptor, validation and results as the
+ * workspace call with desc->flags == 0 (other flags: MILO_ERR_ARG).  A
+ * descriptor whose workspace (milo_moe_gemm_workspace_bytes) exceeds the
+ * static size returns MILO_ERR_WORKSPACE and enqueues nothing.  Every call on
+ * one GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads without ordering) race and
+ * must not be issued.  The scratch needs no initialisation (every byte a call
+ * reads was written earlier in the same call).
+ */
+#define MILO_STATIC_WORKSPACE_BYTES (64u << 20)
+int32_t milo_moe_w3a16_lowrank_gemm_static(const milo_gemm_desc* desc, void* stream);
+
+/*
  * Weighted combine: out[t][h] = sum over j = 0..slots-1, in that order, of
  * y[t*slots + j][h] (fp32 adds), rounded to fp16 (nearest even).  y already
  * holds the route-weighted slot outputs (MILO_EPI_ROUTE_SCALE).
