@@ -53,150 +53,100 @@ __device__ __forceinline__ GroupConstPk group_const_pk(uint32_t szword) {
   return g;
 }
 
-__device__ __forceinline__ f16x8 dequant_step_pk(const uint32_t h[16], int step, const GroupConstPk& g) {
+// B operand of K step `step` from the step's four extracted pairs h4.
+__device__ __forceinline__ f16x8 dequant_pairs_pk(const uint32_t h4[4], int step, const GroupConstPk& g) {
   const f16x2 off64 = {(_Float16)64.f, (_Float16)64.f}, off8 = {(_Float16)8.f, (_Float16)8.f};
   u32x4 u;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int pi = 4 * step + v;
-    const f16x2 q = __builtin_bit_cast(f16x2, h[pi]) - (pair_offset(pi) == 64 ? off64 : off8);
+    const f16x2 q = __builtin_bit_cast(f16x2, h4[v]) - (pair_offset(pi) == 64 ? off64 : off8);
     u[v] = __builtin_bit_cast(uint32_t, q * g.s + g.nzs);
   }
   return __builtin_bit_cast(f16x8, u);
 }
 
-template <int NW, bool LRQ, int BM>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-gemm_prefill_kernel(GemmArgs a) {
-  constexpr int kMT = BM / 16;            // m-tiles per wave
-  constexpr int kXBuf = BM * kXStride;     // halves per staging buffer
-  extern __shared__ __align__(16) uint16_t lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const CodeConsts kc = make_code_consts();
-  RowTile rt;
-  if (!find_row_tile(a.offsets, a.num_experts, a.pre_min_rows, BM, blockIdx.y, a.rp ? a.rank[0] : nullptr,
-                     a.rp ? a.rank[1] : nullptr, &rt))
-    return;
-  const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
-  const int f = (NW == 2) ? (wave & 1) : 0;
-  const int nt = (NW == 2) ? (2 * blockIdx.x + (wave >> 1)) : (4 * blockIdx.x + wave);
-  const bool wave_on = nt < a.n_tiles;
-
-  // ---- activation staging, global memory -> LDS without registers: per K
-  // block a wave issues BM / 16 loads of 1 KB, load j filling rows 16 j + 4 wave ..
-  // + 3 (lane l: row + l / 16, 16-byte slot l % 16).  Slot p of row r holds
-  // column chunk p ^ (r % 16), so a fragment read (16 rows, one chunk) hits
-  // 16 different slots.  Rows past the expert's count read its first row
-  // instead: they only feed output rows that are not stored.
-  const int srow = 4 * wave + (lane >> 4);
-  int xrow[BM / 16];
+// Products of one K block of a wave: the codes of each of the lane's four
+// triplets (q: three planes, one word per row group) are extracted once; K
+// step s dequantizes its four B operands (one per 16-wide output group, with
+// the scale/zero words z) and multiplies them with the A fragments of the
+// NMT m-tiles, read from the LDS staging buffer xb at xoff[s].
+template <int NMT>
+__device__ __forceinline__ void tile_products(const u32x4 (&q)[3], const u32x4 (&z)[2], const uint16_t* xb,
+                                              const int (&xoff)[4], f32x4 (&acc)[NMT][4], const CodeConsts& kc) {
+  uint32_t h[4][16];
 #pragma unroll
-  for (int j = 0; j < BM / 16; ++j) {
-    const int m = m0 + srow + 16 * j;
-    const int i = base + (m < M ? m : m0);
-    xrow[j] = a.gather_div > 0 ? a.sorted_pairs[i] / a.gather_div : i;
-  }
-  const uint16_t* xcol = a.x + 8 * ((lane & 15) ^ (srow & 15));
-  auto stage_x = [&](int kb, int buf) {
+  for (int i = 0; i < 4; ++i) extract_triplet(q[0][i], q[1][i], q[2][i], h[i], kc);
 #pragma unroll
-    for (int j = 0; j < BM / 16; ++j)
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(xcol + (size_t)xrow[j] * a.K + (size_t)kb * kTileK),
-          (__attribute__((address_space(3))) void*)(lds + buf * kXBuf + (16 * j + 4 * wave) * kXStride), 16, 0, 0);
-  };
-  // fragment of K step s: row lane % 16 of each m-tile, chunk 4 s + lane / 16
-  int xoff[4];
-#pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) xoff[s4] = (lane & 15) * kXStride + 8 * ((4 * s4 + (lane >> 4)) ^ (lane & 15));
-
-  // ---- weights of this wave
-  const uint32_t* tbase = a.packed[f] + e * a.words_per_expert + (size_t)(wave_on ? nt : 0) * a.kblocks * kTileWords;
-  const uint32_t* sbase = a.sz[f] + e * a.sz_per_expert + (size_t)(wave_on ? nt : 0) * a.kblocks * kTileSzWords;
-  u32x4 wq[3], wz[2], nq[3], nz[2];
-  auto load_w = [&](int kb, u32x4 (&q)[3], u32x4 (&z)[2]) {
-    const uint32_t* tp = tbase + (size_t)kb * kTileWords;
-    const uint32_t* sp = sbase + (size_t)kb * kTileSzWords + 8 * (lane & 15);
-    q[0] = *(const u32x4*)(tp + 4 * lane);
-    q[1] = *(const u32x4*)(tp + 256 + 4 * lane);
-    q[2] = *(const u32x4*)(tp + 512 + 4 * lane);
-    z[0] = *(const u32x4*)(sp);
-    z[1] = *(const u32x4*)(sp + 4);
-  };
-
-  f32x4 acc[kMT][4];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  stage_x(0, 0);
-  if (wave_on) load_w(0, wq, wz);
-  __syncthreads();   // waits for the staging loads (vmcnt) first
-
-  // B operands of K step s of the current block, from the lane's triplets
-  auto dequant = [&](f16x8 (&wf)[4], int s) {
+  for (int s = 0; s < 4; ++s) {
+    f16x8 wf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t h[16];
-      extract_triplet(wq[0][i], wq[1][i], wq[2][i], h, kc);
       const int idx = 2 * i + (s >> 1);
-      const GroupConstPk gc = group_const_pk(idx < 4 ? wz[0][idx] : wz[1][idx - 4]);
-      wf[i] = dequant_step_pk(h, s, gc);
+      uint32_t h4[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) h4[v] = h[i][4 * s + v];
+      wf[i] = dequant_pairs_pk(h4, s, group_const_pk(idx < 4 ? z[0][idx] : z[1][idx - 4]));
     }
-  };
-
-  // Each K block is one straight-line region (the prefetch indices are
-  // clamped instead of branched on; the last block re-loads its own data),
-  // so the scheduler can overlap a step's dequantization with the previous
-  // step's products.
-  const int KB = a.kblocks;
-  if (wave_on) {
-    for (int kb = 0; kb < KB; ++kb) {
-      const int buf = kb & 1;
-      const int kn = kb + 1 < KB ? kb + 1 : kb;
-      stage_x(kn, buf ^ 1);
-      // one weight family: the next block's weights load ahead of this
-      // block's work (a second register set); two families keep one set
-      // (no registers to spare) and load after the last step's dequantization
-      if constexpr (NW == 1) {
-        load_w(kn, nq, nz);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const uint16_t* xb = lds + buf * kXBuf;
-      // raised wave priority while a block's products issue, back to normal
-      // at the barrier: the two waves sharing a SIMD drift out of phase, one
-      // issuing products while the other waits at its barrier or on loads
-      // (measured: gate/up 93.5 -> 84.6 us on 64-row tiles, -1.6 % on 128)
-      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        f16x8 wf[4];
-        dequant(wf, s);
-        if (NW == 2 && s == 3) load_w(kn, wq, wz);   // the codes of this block are consumed
+    for (int mt = 0; mt < NMT; ++mt) {
+      const f16x8 xa = *(const f16x8*)(xb + xoff[s] + mt * 16 * kXStride);
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-          const f16x8 xa = *(const f16x8*)(xb + xoff[s] + mt * 16 * kXStride);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][i] = mfma16x16x32(xa, wf[i], acc[mt][i]);
-        }
-      }
-      if constexpr (NW == 1) {
-#pragma unroll
-        for (int j = 0; j < 3; ++j) wq[j] = nq[j];
-        wz[0] = nz[0];
-        wz[1] = nz[1];
-      }
-      __builtin_amdgcn_s_setprio(0);
-      __syncthreads();   // waits for the staging loads (vmcnt) first
-    }
-  } else {
-    // no output tile: only the share of the activation staging
-    for (int kb = 0; kb < KB; ++kb) {
-      stage_x(kb + 1 < KB ? kb + 1 : kb, (kb & 1) ^ 1);
-      __syncthreads();
+      for (int i = 0; i < 4; ++i) acc[mt][i] = mfma16x16x32(xa, wf[i], acc[mt][i]);
     }
   }
+}
 
+// Source addresses of the activation chunks a lane stages: rows
+// srow + 16 j (j < NMT) of the tile, gathered through sorted_pairs; rows past
+// the expert's count take its first row.  All index loads are issued before
+// any is used (no dependent round trip per row).
+template <int NMT>
+__device__ __forceinline__ void stage_rows(const GemmArgs& a, int m0, int M, int base, int srow, int lane,
+                                           const uint16_t* (&xsrc)[NMT]) {
+  const bool gather = a.gather_div > 0;
+  const int32_t* idx_src = gather ? a.sorted_pairs : a.offsets;   // a valid array either way
+  int i[NMT], v[NMT];
+#pragma unroll
+  for (int j = 0; j < NMT; ++j) {
+    const int m = m0 + srow + 16 * j;
+    i[j] = base + (m < M ? m : m0);
+    v[j] = idx_src[gather ? i[j] : 0];
+  }
+#pragma unroll
+  for (int j = 0; j < NMT; ++j) {
+    const int xr = gather ? v[j] / a.gather_div : i[j];
+    xsrc[j] = a.x + (size_t)xr * a.K + 8 * ((lane & 15) ^ (srow & 15));
+  }
+}
+
+// Loads of one K block of a wave: its 64 x 128 code tile (three planes), the
+// eight scale/zero words of its lane's rows, and its NMT 16-byte chunks of
+// the block's activation rows.  Register stages of a ring: everything is a
+// plain global load, so the compiler's load counters wait exactly for the
+// stage being consumed while the younger stages stay in flight.
+template <int NMT>
+struct TileStage {
+  u32x4 q[3];
+  u32x4 z[2];
+  u32x4 x[NMT];
+};
+
+// Stages in flight: deeper where a K block carries little matrix-core work
+// (few rows), as deep as the registers allow at 128 rows.
+template <int NMT>
+struct TileDepth {
+  static constexpr int D = NMT <= 1 ? 4 : (NMT <= 4 ? 3 : 2);
+};
+
+// After the K loop: the low-rank term and the epilogue of a wave's output
+// tile (NMT m-tiles x 64 columns of family f, n-tile nt).
+template <int NW, bool LRQ, int NMT>
+__device__ __forceinline__ void tile_finish(const GemmArgs& a, const RowTile& rt, uint16_t* lds,
+                                            const CodeConsts& kc, f32x4 (&acc)[NMT][4], int f, int nt,
+                                            bool wave_on) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
   // ---- low-rank term: (x V^T) U^T as extra K steps (int3 U: the lane's
   // triplet of each 32-rank U tile is its B operand for the four row groups)
   if (wave_on && a.rp > 0) {
@@ -221,9 +171,10 @@ gemm_prefill_kernel(GemmArgs a) {
         }
       }
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
+      for (int mt = 0; mt < NMT; ++mt) {
         const int m = m0 + mt * 16 + (lane & 15);
-        const f16x8 ta = m < M ? *(const f16x8*)(a.T + (size_t)(base + m) * RW + f * a.rp + j0) : f16x8{};
+        const f16x8 tv = *(const f16x8*)(a.T + (size_t)(base + (m < M ? m : m0)) * RW + f * a.rp + j0);
+        const f16x8 ta = m < M ? tv : f16x8{};
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[mt][i] = mfma16x16x32(ta, ub[i], acc[mt][i]);
       }
@@ -235,10 +186,10 @@ gemm_prefill_kernel(GemmArgs a) {
     // waves with f == 1 (W3) hand their tile to the partner wave (wave - 1)
     // rows padded to kExStride floats: the four row groups of a wave's
     // accumulators then fall on different LDS banks
-    float* ex = (float*)lds + (wave >> 1) * (BM * kExStride);
+    float* ex = (float*)lds + (wave >> 1) * (NMT * 16 * kExStride);
     if (wave_on && f == 1) {
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
+      for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -248,7 +199,7 @@ gemm_prefill_kernel(GemmArgs a) {
     __syncthreads();
     if (!wave_on || f == 1) return;
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
+    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int mm = mt * 16 + 4 * (lane >> 4) + r;
@@ -265,7 +216,7 @@ gemm_prefill_kernel(GemmArgs a) {
   }
   if (!wave_on) return;
 #pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
+  for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int mm = mt * 16 + 4 * (lane >> 4) + r;
@@ -285,6 +236,214 @@ gemm_prefill_kernel(GemmArgs a) {
     }
 }
 
+// One block's tile: NMT active 16-row m-tiles (the tile's rows, rounded up).
+template <int NW, bool LRQ, int NMT>
+__device__ __forceinline__ void tile_body(const GemmArgs& a, const RowTile& rt, uint16_t* lds,
+                                          const CodeConsts& kc) {
+  constexpr int D = TileDepth<NMT>::D;
+  constexpr int kXBuf = NMT * 16 * kXStride;   // halves per staging buffer
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
+  const int f = (NW == 2) ? (wave & 1) : 0;
+  const int nt = (NW == 2) ? (2 * blockIdx.x + (wave >> 1)) : (4 * blockIdx.x + wave);
+  const bool wave_on = nt < a.n_tiles;
+
+  // ---- activation staging: lane l of wave w stages, for j < NMT, row
+  // 16 j + 4 w + l / 16 of the tile, 16-byte column chunk (l mod 16) XOR
+  // (row mod 16), into LDS slot l mod 16 of that row; a fragment read (16
+  // rows, one chunk) then hits 16 different slots.  Rows past the expert's
+  // count read its first row instead: they only feed outputs that are not
+  // stored.
+  const int srow = 4 * wave + (lane >> 4);
+  const uint16_t* xsrc[NMT];
+  stage_rows<NMT>(a, m0, M, base, srow, lane, xsrc);
+  const int xdst = srow * kXStride + 8 * (lane & 15);
+  // fragment of K step s: row lane % 16 of each m-tile, chunk 4 s + lane / 16
+  int xoff[4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) xoff[s4] = (lane & 15) * kXStride + 8 * ((4 * s4 + (lane >> 4)) ^ (lane & 15));
+
+  // ---- weights of this wave (a wave without an output tile loads tile 0)
+  const int ntc = wave_on ? nt : 0;
+  const uint32_t* tbase = a.packed[f] + e * a.words_per_expert + (size_t)ntc * a.kblocks * kTileWords + 4 * lane;
+  const uint32_t* sbase =
+      a.sz[f] + e * a.sz_per_expert + (size_t)ntc * a.kblocks * kTileSzWords + 8 * (lane & 15);
+  const int KB = a.kblocks;
+  auto issue = [&](TileStage<NMT>& S, int kb) {
+    const uint32_t* tp = tbase + (size_t)kb * kTileWords;
+    S.q[0] = *(const u32x4*)(tp);
+    S.q[1] = *(const u32x4*)(tp + 256);
+    S.q[2] = *(const u32x4*)(tp + 512);
+    const uint32_t* sp = sbase + (size_t)kb * kTileSzWords;
+    S.z[0] = *(const u32x4*)(sp);
+    S.z[1] = *(const u32x4*)(sp + 4);
+#pragma unroll
+    for (int j = 0; j < NMT; ++j) S.x[j] = *(const u32x4*)(xsrc[j] + (size_t)kb * kTileK);
+  };
+  auto put_x = [&](const TileStage<NMT>& S, int buf) {
+#pragma unroll
+    for (int j = 0; j < NMT; ++j) *(u32x4*)(lds + buf * kXBuf + xdst + 16 * j * kXStride) = S.x[j];
+  };
+
+  f32x4 acc[NMT][4];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // products of one K block: the codes of each of the lane's four triplets
+  // are extracted once; K step s dequantizes its four B operands (one per
+  // 16-wide output group) and multiplies them with the m-tiles' A fragments
+  auto compute = [&](const TileStage<NMT>& S, int buf) {
+    tile_products<NMT>(S.q, S.z, lds + buf * kXBuf, xoff, acc, kc);
+  };
+
+  // ---- K loop over a ring of D register stages.  Stage j (K block j) sits
+  // in slot j mod D: it is issued at the end of block j - D (the slot's
+  // previous contents consumed), its activation chunks go to LDS buffer
+  // j mod 2 at the end of block j - 1, and block j is computed from them
+  // after the barrier.  The loop is unrolled by D so slots are registers.
+  // Blocks past the end re-load the last block (never computed): every
+  // iteration issues the same loads.
+  TileStage<NMT> ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(ring[d], d < KB ? d : KB - 1);
+  put_x(ring[0], 0);
+  __syncthreads();
+  for (int kb0 = 0; kb0 < KB; kb0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int kb = kb0 + u;
+      if (kb < KB) {
+        // raised wave priority while a block's products issue, back to
+        // normal at the barrier: the two waves sharing a SIMD drift out of
+        // phase, one issuing products while the other waits
+        __builtin_amdgcn_s_setprio(2);
+        if (wave_on) compute(ring[u], kb & 1);
+        __builtin_amdgcn_s_setprio(0);
+        issue(ring[u], kb + D < KB ? kb + D : KB - 1);
+        put_x(ring[(u + 1) % D], (kb + 1) & 1);
+        __syncthreads();
+      }
+    }
+  }
+
+  tile_finish<NW, LRQ, NMT>(a, rt, lds, kc, acc, f, nt, wave_on);
+}
+
+// 128-row tiles (eight m-tiles): the accumulators take half the registers,
+// so nothing is staged in registers.  Activations and weights both go from
+// global memory straight into LDS (global_load_lds: x double buffered, one
+// 3.5 KB weight slot per wave: three code planes of 1 KB and the 512-byte
+// scale/zero tile), all issued at the start of the previous K block.  Every
+// load of the loop is such an LDS transfer, so the compiler inserts no load
+// waits of its own; the loop waits explicitly: the wave's own transfers
+// (vmcnt 0) before the barrier that ends a block, and its slot read-back
+// (lgkmcnt 0) before the slot is refilled.
+constexpr int kWSlotHalves = 3584 / 2;    // 3 KB codes + 512 B scale/zero per wave
+constexpr size_t prefill_lds_128 = (size_t)2 * 128 * kXStride * 2 + 4 * 3584;
+
+__device__ __forceinline__ void dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+}
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; a field at its maximum does not wait)
+constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
+
+template <int NW, bool LRQ, int NMT>
+__device__ __forceinline__ void tile_body_lds(const GemmArgs& a, const RowTile& rt, uint16_t* lds,
+                                              const CodeConsts& kc) {
+  constexpr int kXBuf = NMT * 16 * kXStride;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
+  const int f = (NW == 2) ? (wave & 1) : 0;
+  const int nt = (NW == 2) ? (2 * blockIdx.x + (wave >> 1)) : (4 * blockIdx.x + wave);
+  const bool wave_on = nt < a.n_tiles;
+
+  // activation staging as in tile_body, but by LDS transfers: load j of a
+  // wave fills rows 16 j + 4 wave .. + 3 (lane l: row + l / 16, slot l % 16)
+  const int srow = 4 * wave + (lane >> 4);
+  const uint16_t* xsrc[NMT];
+  stage_rows<NMT>(a, m0, M, base, srow, lane, xsrc);
+  int xoff[4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) xoff[s4] = (lane & 15) * kXStride + 8 * ((4 * s4 + (lane >> 4)) ^ (lane & 15));
+
+  const int ntc = wave_on ? nt : 0;
+  const uint32_t* tbase = a.packed[f] + e * a.words_per_expert + (size_t)ntc * a.kblocks * kTileWords + 4 * lane;
+  const uint32_t* sbase = a.sz[f] + e * a.sz_per_expert + (size_t)ntc * a.kblocks * kTileSzWords + lane;
+  uint16_t* wslot = lds + 2 * kXBuf + wave * kWSlotHalves;
+  const int KB = a.kblocks;
+  auto issue = [&](int kb, int buf) {
+#pragma unroll
+    for (int j = 0; j < NMT; ++j)
+      dma16(xsrc[j] + (size_t)kb * kTileK, lds + buf * kXBuf + (16 * j + 4 * wave) * kXStride);
+    const uint32_t* tp = tbase + (size_t)kb * kTileWords;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) dma16(tp + 256 * p, wslot + 512 * p);
+    const uint32_t* sp = sbase + (size_t)kb * kTileSzWords;
+    dma4(sp, wslot + 1536);
+    dma4(sp + 64, wslot + 1536 + 128);
+  };
+
+  f32x4 acc[NMT][4];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  for (int kb = 0; kb < KB; ++kb) {
+    const int buf = kb & 1;
+    // the wave's weights of block kb: slot -> registers (lane l: its 16 bytes
+    // of each plane; the scale/zero words of its rows, 32 bytes at 32 (l mod 16))
+    u32x4 q[3], z[2];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) q[p] = *(const u32x4*)(wslot + 512 * p + 8 * lane);
+    z[0] = *(const u32x4*)(wslot + 1536 + 16 * (lane & 15));
+    z[1] = *(const u32x4*)(wslot + 1536 + 16 * (lane & 15) + 8);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kb + 1 < KB ? kb + 1 : kb, buf ^ 1);   // the last block re-loads its own data
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(2);
+    if (wave_on) tile_products<NMT>(q, z, lds + buf * kXBuf, xoff, acc, kc);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  }
+  tile_finish<NW, LRQ, NMT>(a, rt, lds, kc, acc, f, nt, wave_on);
+}
+
+template <int NW, bool LRQ, int BM>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_prefill_kernel(GemmArgs a) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  const CodeConsts kc = make_code_consts();
+  RowTile rt;
+  if (!find_row_tile(a.offsets, a.num_experts, a.pre_min_rows, BM, blockIdx.y, a.rp ? a.rank[0] : nullptr,
+                     a.rp ? a.rank[1] : nullptr, &rt))
+    return;
+  if constexpr (BM == 64) {
+    // only the tile's own rows: fewer products and staged rows for the
+    // small experts (a 3-row expert costs one m-tile, not four)
+    const int rows = rt.rows - rt.m0;
+    if (rows <= 16) tile_body<NW, LRQ, 1>(a, rt, lds, kc);
+    else if (rows <= 32) tile_body<NW, LRQ, 2>(a, rt, lds, kc);
+    else tile_body<NW, LRQ, 4>(a, rt, lds, kc);
+  } else {
+    tile_body_lds<NW, LRQ, BM / 16>(a, rt, lds, kc);
+  }
+}
+
 
 int32_t launch_gemm_prefill(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st) {
   if (!p.pre_launch) return MILO_OK;
@@ -293,7 +452,7 @@ int32_t launch_gemm_prefill(const milo_gemm_desc* d, const GemmPlan& p, char* ws
   // (less padding and twice the blocks for mid-sized experts)
   const dim3 grid(d->n_w == 2 ? (p.n_tiles + 1) / 2 : (p.n_tiles + 3) / 4, p.pre_tiles);
   if (p.pre_bm == 128) {
-    const size_t lds = prefill_lds(128);
+    const size_t lds = prefill_lds(128) > prefill_lds_128 ? prefill_lds(128) : prefill_lds_128;
     if (d->n_w == 2) {
       if (a.lrq) hipLaunchKernelGGL((gemm_prefill_kernel<2, true, 128>), grid, dim3(256), lds, st, a);
       else hipLaunchKernelGGL((gemm_prefill_kernel<2, false, 128>), grid, dim3(256), lds, st, a);

@@ -98,6 +98,33 @@ __device__ __forceinline__ void extract_triplet(uint32_t w0, uint32_t w1, uint32
   out[15] = and_or(w2 << 6, k.b6, s);
 }
 
+// The four code pairs of MFMA K-step `step` (pairs 4 step .. 4 step + 3) of
+// one layout-v1 triplet, extracted on their own (the same values as
+// extract_triplet's out[4 step .. 4 step + 3]); for callers that cannot keep
+// all sixteen extracted pairs of a triplet live at once.
+__device__ __forceinline__ void extract_step(uint32_t w0, uint32_t w1, uint32_t w2, int step, uint32_t out[4],
+                                             const CodeConsts& k) {
+  const uint32_t w[3] = {w0, w1, w2};
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int pi = 4 * step + v;
+    if (pi == 15) {
+      uint32_t s = and_or(w0 << 4, k.b4, k.m64);
+      s = and_or(w1 << 5, k.b5, s);
+      out[v] = and_or(w2 << 6, k.b6, s);
+      continue;
+    }
+    const uint32_t a = w[pi / 5];
+    switch (pi % 5) {
+      case 0: out[v] = and_or(a << 3, k.lo, k.m64); break;
+      case 1: out[v] = and_or(a, k.lo, k.m64); break;
+      case 2: out[v] = and_or(a, k.hi, k.m8); break;
+      case 3: out[v] = and_or(a >> 6, k.lo, k.m64); break;
+      default: out[v] = and_or(a >> 6, k.hi, k.m8); break;
+    }
+  }
+}
+
 // (off + q) -> (q - z) * s as float16, computed as fma(h, s, -(off + z) s) in
 // float32 and rounded once.
 __device__ __forceinline__ uint32_t dequant_pair(uint32_t h, float s, float c) {
