@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+REL_FRO_TOL, MAX_ABS_TOL = 1e-3, 2e-2   # fp16 outputs vs the float64 oracle
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores
 METRIC = "MoE-layer tokens/s + achieved HBM TB/s (decode) / MFMA % (prefill)"
 
@@ -51,6 +52,10 @@ def parse():
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="C2 only: skip the prefill (C3) sub-record measured in the same run")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-check-tokens", type=int, default=2)
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--lr", default="fp16", choices=["fp16", "int3"],
                     help="storage of the compensator factors U, V")
@@ -94,6 +99,7 @@ class Layer:
         import torch
         L = m._lib
         self.m, self.cfg = m, cfg
+        self.layer_idx = layer_idx
         self.lr_format = lr_format
         self.ranks = synth.gen_ranks(cfg, layer_idx)
         ET = cfg.E + cfg.S
@@ -166,6 +172,13 @@ class Layer:
 
     # algorithmic bytes / flops from the routed row counts (host copies)
     def work(self, offsets):
+        """Kernel- and step-level work of one layer step.  Step bytes count
+        what the layer must move: the touched experts' packed codes,
+        scale/zero and compensator factors, the activations read and the
+        output written; the intermediates (G, per-slot Y, low-rank products,
+        gathered rows) are reported separately.  The gate/up kernel's own
+        bytes (the roofline line) are its weights, factors U, gathered rows,
+        low-rank products and its output G."""
         cfg = self.cfg
         H, F = cfg.H, cfg.F
         rows = [int(offsets[e + 1] - offsets[e]) for e in range(cfg.E + cfg.S)]
@@ -177,28 +190,37 @@ class Layer:
         # (U: one group per output row; V: groups of 64 along the input)
         u_bytes = (lambda n, r: n * r * 3 // 8 + (4 * n if r else 0)) if q3 else (lambda n, r: n * r * 2)
         v_bytes = (lambda r, k: r * k * 3 // 8 + r * (k // 64) * 4) if q3 else (lambda r, k: r * k * 2)
+        w_bytes = lambda n, k: 3 * n * k // 8 + n * k // 16      # packed int3 + scale/zero
+        wt = lr = 0
+        inter = 0
         for e, M in enumerate(rows):
             if M == 0:
                 continue
             touched += 1
             r = self.ranks[e]
-            # gate/up kernel: W1, W3 packed + scale/zero + U (N x r) per matrix,
-            # gathered X rows, T rows, G written
-            b13 += 2 * (3 * F * H // 8 + F * H // 16 + u_bytes(F, r)) + M * H * 2 + M * 2 * r * 2 + M * F * 2
-            b2 += (3 * H * F // 8 + H * F // 16 + u_bytes(H, r)) + M * F * 2 + M * r * 2 + M * H * 4
+            wt += 2 * w_bytes(F, H) + w_bytes(H, F)
+            lr += 2 * (u_bytes(F, r) + v_bytes(r, H)) + u_bytes(H, r) + v_bytes(r, F)
+            # gate/up kernel: W1, W3 + U1, U3, gathered X rows, T rows, G written
+            b13 += 2 * (w_bytes(F, H) + u_bytes(F, r)) + M * H * 2 + M * 2 * r * 2 + M * F * 2
+            b2 += w_bytes(H, F) + u_bytes(H, r) + M * F * 2 + M * r * 2 + M * H * 4
             f13 += 2 * M * 2 * F * H + 2 * M * 2 * r * (H + F)
             f2 += 2 * M * H * F + 2 * M * r * (H + F)
-        # pre-pass reads of V (V1, V3: r x H; V2: r x F) for touched experts
-        vbytes = sum(2 * v_bytes(r, H) + v_bytes(r, F) for e, r in enumerate(self.ranks) if rows[e])
-        layer_bytes = b13 + b2 + vbytes + cfg.T * H * 2 * 2 + cfg.T * cfg.E * 4
+            # intermediates: G written and read, Y written and read, T13 / T2
+            # written and read, gathered activation rows
+            inter += 2 * M * F * 2 + 2 * M * H * 4 + 2 * (M * 2 * r * 2 + M * r * 2) + M * H * 2
+        io = cfg.T * H * 2 * 2                                  # X read + out written
         return {"rows": rows, "touched": touched, "bytes13": b13, "bytes2": b2, "flops13": f13,
-                "flops2": f2, "layer_bytes": layer_bytes, "layer_flops": f13 + f2}
+                "flops2": f2, "layer_bytes": wt + lr + io, "layer_flops": f13 + f2,
+                "weight_bytes": wt, "compensator_bytes": lr, "io_bytes": io, "intermediate_bytes": inter}
 
 
-def cpu_baseline(cfg, layer, offsets, budget_s):
+def cpu_baseline(cfg, layer, budget_s):
     """The CPU oracle (float64 NumPy, as it stands) on a bounded sample of the
     same layer: routing of all tokens plus the expert FFNs of as many touched
-    experts as fit the time budget, scaled to the whole layer."""
+    experts as fit the time budget, scaled to the whole layer.  Its results
+    are kept: the per-slot outputs Y of the sampled experts and the outputs
+    of the tokens whose every slot was sampled are compared with the GPU's
+    (layer.Y / layer.out from the last timed step on this weight set)."""
     import numpy as np
     import oracle
     import synth
@@ -209,17 +231,21 @@ def cpu_baseline(cfg, layer, offsets, budget_s):
     rt = oracle.route_ref(logits, cfg.k, cfg.S, cfg.renormalize)
     t_route = time.perf_counter() - t0
     sp, off = rt["sorted_pairs"], rt["offsets"]
+    slot_w = rt["slot_w"].reshape(-1)
     touched = [e for e in range(cfg.E + cfg.S) if off[e + 1] > off[e]]
     done, t_exp, pairs_done = [], 0.0, 0
+    y_ref = {}
     for e in touched:
-        exp = synth.gen_expert(cfg, 0, e, layer.ranks[e], device="cuda")
+        exp = synth.gen_expert(cfg, layer.layer_idx, e, layer.ranks[e], device="cuda")
         qe = oracle.quantize_expert({k: v.cpu() for k, v in exp.items()},
                                     lr_format=layer.lr_format)              # offline, untimed
         seg = sp[off[e]:off[e + 1]]
         rows = X[seg // cfg.slots]
         t1 = time.perf_counter()
-        oracle.expert_ffn_ref(rows, qe)
+        _, y = oracle.expert_ffn_ref(rows, qe)
         t_exp += time.perf_counter() - t1
+        for i, s in enumerate(seg):
+            y_ref[int(s)] = y[i] * slot_w[s]
         done.append(e)
         pairs_done += seg.size
         del qe
@@ -228,13 +254,67 @@ def cpu_baseline(cfg, layer, offsets, budget_s):
     scale = cfg.P / max(pairs_done, 1)
     layer_s = t_route + t_exp * scale
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    # the check of the timed output
+    slots = sorted(y_ref)
+    Yg = layer.Y.cpu().numpy().astype(np.float64)
+    check = {"what": f"per-slot route-weighted expert outputs Y of {len(slots)} of {cfg.P} slots"}
+    rf_y = oracle.rel_fro(Yg[slots], np.stack([y_ref[s] for s in slots]))
+    ma_y = oracle.max_abs(Yg[slots], np.stack([y_ref[s] for s in slots]))
+    full = [t for t in range(cfg.T) if all((t * cfg.slots + j) in y_ref for j in range(cfg.slots))]
+    check.update({"Y_rel_fro": rf_y, "Y_max_abs": ma_y, "tokens_checked": len(full)})
+    if full:
+        out_ref = np.stack([sum(y_ref[t * cfg.slots + j] for j in range(cfg.slots)) for t in full])
+        og = layer.out.cpu().numpy().astype(np.float64)[full]
+        check["out_rel_fro"] = oracle.rel_fro(og, out_ref)
+        check["out_max_abs"] = oracle.max_abs(og, out_ref)
+    check["pass"] = bool(max(rf_y, check.get("out_rel_fro", 0.0)) <= REL_FRO_TOL and
+                         max(ma_y, check.get("out_max_abs", 0.0)) <= MAX_ABS_TOL)
     return {
         "value": cfg.T / layer_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
         "sample": f"oracle.route_ref on all {cfg.T} tokens + oracle.expert_ffn_ref (float64 dequant + "
                   f"matmul) for {len(done)} of {len(touched)} touched experts ({pairs_done} of {cfg.P} "
                   f"pairs) in {t_route + t_exp:.1f} s, scaled x{scale:.2f} by pairs to the whole layer",
         "layer_seconds": layer_s,
-    }
+        "cpu_model": cpu_model(),
+        "host_cpus_available": len(os.sched_getaffinity(0)),
+    }, check
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def device_info(timer):
+    """GPU name, compute units and clocks: the runtime's figures, and the
+    shader clock the driver reports after the timed region (best effort)."""
+    import subprocess
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    info = {"gpu": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count}
+    v = C.c_int()
+    h = timer.h
+    h.hipDeviceGetAttribute.argtypes = [C.POINTER(C.c_int), C.c_int, C.c_int]
+    HIP_ATTR_CLOCK_RATE = 5            # kHz, peak
+    if h.hipDeviceGetAttribute(C.byref(v), HIP_ATTR_CLOCK_RATE, 0) == 0:
+        info["peak_clock_mhz"] = v.value // 1000
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+        for card in d.values():
+            for k, val in card.items():
+                if "sclk" in k.lower():
+                    info["sclk_after_run"] = val
+                    break
+            break
+    except Exception:
+        pass
+    return info
 
 
 class HipTimer:
@@ -324,96 +404,14 @@ def main():
     if args.batch:
         cfg = cfg.with_(T=args.batch)
     path = {"auto": 0, "decode": 1, "prefill": 2}[args.path]
-    stack = cfg.layers > 1
-    nsets = cfg.layers if stack else args.copies
-    log(f"building {nsets} weight set(s) of {args.config} (T={cfg.T}) on the GPU")
-    X = synth.gen_tokens(cfg, 0, device="cuda")
-    t0 = time.time()
-    layers = []
-    for i in range(nsets):
-        logits = synth.gen_logits(cfg, i if stack else 0, device="cuda")
-        layers.append(Layer(m, cfg, i if stack else 0, X, logits, path, args.lr) if (stack or i == 0)
-                      else Layer(m, cfg, 100 + i, X, logits, path, args.lr))
-    ws = torch.zeros(max(lay.ws_need for lay in layers), dtype=torch.uint8, device="cuda")
-    for lay in layers:
-        lay.ws = ws
-    torch.cuda.synchronize()
-    log(f"weights ready in {time.time() - t0:.1f} s")
-    stream = torch.cuda.current_stream().cuda_stream
-
-    def run_step(i, ev=None):
-        if stack:
-            for li, lay in enumerate(layers):
-                lay.step(stream, ev if li == 0 else None)
-        else:
-            layers[i % nsets].step(stream, ev)
-
-    for i in range(args.warmup):
-        run_step(i)
-    torch.cuda.synchronize()
     global TIMER
     TIMER = HipTimer()
-    evs = [(TIMER.event(), TIMER.event()) for _ in range(args.steps)]
-    marks = [TIMER.event() for _ in range(args.steps + 1)]   # step boundaries
-    start, stop = TIMER.event(), TIMER.event()
-    torch.cuda.synchronize()
-    t_host = time.perf_counter()
-    TIMER.record(start, stream)
-    TIMER.record(marks[0], stream)
-    for i in range(args.steps):
-        run_step(i, evs[i])
-        TIMER.record(marks[i + 1], stream)
-    TIMER.record(stop, stream)
-    torch.cuda.synchronize()
-    t_host = time.perf_counter() - t_host
-    ms_total = TIMER.ms(start, stop)
-    ms_step = ms_total / args.steps
-    step_ms = sorted(TIMER.ms(marks[i], marks[i + 1]) for i in range(args.steps))
-    pct = lambda q: step_ms[min(len(step_ms) - 1, int(q * (len(step_ms) - 1) + 0.5))]
-    k13_us = sum(TIMER.ms(a, b) for a, b in evs) / len(evs) * 1000.0
-
-    # work accounting (after the timed region)
-    works = []
-    for lay in layers:
-        offs = lay.route["offsets"].cpu().numpy()
-        works.append(lay.work(offs))
-    w0 = works[0] if stack else None
-    if stack:
-        layer_bytes = sum(w["layer_bytes"] for w in works)
-        layer_flops = sum(w["layer_flops"] for w in works)
-        k_bytes, k_flops = works[0]["bytes13"], works[0]["flops13"]
-    else:
-        used = [works[i % nsets] for i in range(args.steps)]
-        layer_bytes = sum(w["layer_bytes"] for w in used) / len(used)
-        layer_flops = sum(w["layer_flops"] for w in used) / len(used)
-        k_bytes = sum(w["bytes13"] for w in used) / len(used)
-        k_flops = sum(w["flops13"] for w in used) / len(used)
-        w0 = works[0]
+    run = run_workload(m, cfg, args.config, cfg.layers if cfg.layers > 1 else args.copies, path, args.lr,
+                       args.steps, args.warmup)
+    ms_step = run["ms_step"]
     tokens_per_s = cfg.T / (ms_step / 1000.0)
-    prefill = cfg.T * cfg.k / cfg.E > 64
-    # the kernels the library's automatic path launches for the gate/up call:
-    # small-M only up to 32 rows per expert; small matrices (N K <= 2^22) with
-    # experts averaging 16+ rows: the 64-row tile kernel only; else both
-    pairs = cfg.T * (cfg.k + cfg.S)
-    ET = cfg.E + cfg.S
-    if prefill:
-        kname = "gemm_prefill_kernel<2,...,128> (gate/up + SwiGLU)"
-    elif cfg.T <= 32 or args.path == "decode":
-        kname = "gemm_decode_kernel<MT,2> (gate/up + SwiGLU)"
-    elif args.path == "prefill" or (cfg.F * cfg.H <= (1 << 22) and pairs >= 16 * ET):
-        kname = "gate/up call: gemm_prefill_kernel<2,...> (tile kernel for every expert)"
-    else:
-        kname = "gate/up call: gemm_decode_kernel<MT,2> + gemm_prefill_kernel<2,...> (both paths)"
-    if prefill:
-        achieved = k_flops / (k13_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
-    else:
-        achieved = k_bytes / (k13_us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(args.config, cfg.T, args.lr)}
-    roof.update({"kernel": kname, "alg_bytes_per_launch": int(k_bytes), "alg_flops_per_launch": int(k_flops),
-                 "avg_launch_us": round(k13_us, 2)})
+    roof = run["roofline"]
+    comp = run["work"]
     res = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -430,24 +428,167 @@ def main():
         "config": {
             "workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}",
             "tokens": cfg.T, "layers": cfg.layers, "experts": cfg.E, "shared": cfg.S, "top_k": cfg.k,
-            "hidden": cfg.H, "ffn": cfg.F, "weight_sets_rotated": nsets,
-            "touched_experts": w0["touched"],
-            "step_alg_bytes": int(layer_bytes), "step_alg_flops": int(layer_flops),
-            "achieved_TBps_step": round(layer_bytes / (ms_step * 1e-3) / 1e12, 3),
-            "achieved_TFLOPs_step": round(layer_flops / (ms_step * 1e-3) / 1e12, 2),
-            "host_seconds_timed": round(t_host, 3),
-            "step_ms_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
+            "hidden": cfg.H, "ffn": cfg.F, "weight_sets_rotated": run["nsets"],
+            "touched_experts": run["touched"],
+            "step_alg_bytes": int(comp["layer_bytes"]), "step_alg_flops": int(comp["layer_flops"]),
+            "step_intermediate_bytes": int(comp["intermediate_bytes"]),
+            "achieved_TBps_step": round(comp["layer_bytes"] / (ms_step * 1e-3) / 1e12, 3),
+            "achieved_TFLOPs_step": round(comp["layer_flops"] / (ms_step * 1e-3) / 1e12, 2),
+            "compensator_share": {
+                "of_step_bytes": round(comp["compensator_bytes"] / comp["layer_bytes"], 4),
+                "of_resident_weights": run["resident_comp_share"]},
+            "host_seconds_timed": run["host_s"],
+            "step_ms_p10_p50_p90": run["pcts"],
             "path": args.path,
             "compensator_factors": args.lr,
         },
         "roofline": roof,
     }
+    res["device"] = device_info(TIMER)
+    if args.config == "C2" and not args.no_prefill and args.path == "auto" and not args.batch:
+        # the prefill half of the metric, measured in the same run: the same
+        # Mixtral-shaped layer at 4096 tokens (matrix-core path)
+        c3 = SC.get_config("C3")
+        log("prefill sub-record: C3")
+        pr = run_workload(m, c3, "C3", 1, 0, args.lr, args.prefill_steps, 2)
+        pc = pr["work"]
+        res["prefill"] = {
+            "workload": f"C3: {WORKLOAD_TEXT['C3']}",
+            "ms_per_step": round(pr["ms_step"], 4),
+            "tokens_per_s": round(c3.T / (pr["ms_step"] * 1e-3), 1),
+            "steps": args.prefill_steps,
+            "step_alg_flops": int(pc["layer_flops"]),
+            "achieved_TFLOPs_step": round(pc["layer_flops"] / (pr["ms_step"] * 1e-3) / 1e12, 2),
+            "mfma_frac_step": round(pc["layer_flops"] / (pr["ms_step"] * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+            "roofline": pr["roofline"],
+        }
+        if not args.no_cpu:
+            res["prefill"]["check"] = prefill_check(c3, pr["layers"][0], args.prefill_check_tokens)
+            del pr
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample")
-        res["cpu_baseline"] = cpu_baseline(cfg, layers[0], None, args.cpu_seconds)
+        res["cpu_baseline"], res["check"] = cpu_baseline(cfg, run["layers"][0], args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res))
+    ok = res.get("check", {}).get("pass", True) and res.get("prefill", {}).get("check", {}).get("pass", True)
+    if not ok:
+        log("the timed output does not match the oracle (see check)")
+        sys.exit(3)
+
+
+def run_workload(m, cfg, name, nsets, path, lr, steps, warmup):
+    """Build nsets weight sets of a workload (one per layer for a stack),
+    warm up, time `steps` steps with HIP events on the library's stream, and
+    account the work."""
+    import torch
+    import synth
+    stack = cfg.layers > 1
+    log(f"building {nsets} weight set(s) of {name} (T={cfg.T}) on the GPU")
+    X = synth.gen_tokens(cfg, 0, device="cuda")
+    t0 = time.time()
+    layers = []
+    for i in range(nsets):
+        logits = synth.gen_logits(cfg, i if stack else 0, device="cuda")
+        layers.append(Layer(m, cfg, i if stack else 0, X, logits, path, lr) if (stack or i == 0)
+                      else Layer(m, cfg, 100 + i, X, logits, path, lr))
+    ws = torch.zeros(max(lay.ws_need for lay in layers), dtype=torch.uint8, device="cuda")
+    for lay in layers:
+        lay.ws = ws
+    torch.cuda.synchronize()
+    log(f"weights ready in {time.time() - t0:.1f} s")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run_step(i, ev=None):
+        if stack:
+            for li, lay in enumerate(layers):
+                lay.step(stream, ev if li == 0 else None)
+        else:
+            layers[i % nsets].step(stream, ev)
+
+    for i in range(warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    evs = [(TIMER.event(), TIMER.event()) for _ in range(steps)]
+    marks = [TIMER.event() for _ in range(steps + 1)]   # step boundaries
+    start, stop = TIMER.event(), TIMER.event()
+    torch.cuda.synchronize()
+    t_host = time.perf_counter()
+    TIMER.record(start, stream)
+    TIMER.record(marks[0], stream)
+    for i in range(steps):
+        run_step(i, evs[i])
+        TIMER.record(marks[i + 1], stream)
+    TIMER.record(stop, stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    ms_step = TIMER.ms(start, stop) / steps
+    step_ms = sorted(TIMER.ms(marks[i], marks[i + 1]) for i in range(steps))
+    pct = lambda q: step_ms[min(len(step_ms) - 1, int(q * (len(step_ms) - 1) + 0.5))]
+    k13_us = sum(TIMER.ms(a, b) for a, b in evs) / len(evs) * 1000.0
+
+    # work accounting (after the timed region)
+    works = [lay.work(lay.route["offsets"].cpu().numpy()) for lay in layers]
+    keys = ("layer_bytes", "layer_flops", "bytes13", "flops13", "weight_bytes", "compensator_bytes",
+            "io_bytes", "intermediate_bytes")
+    if stack:
+        comp = {k: sum(w[k] for w in works) for k in keys}
+        comp["bytes13"], comp["flops13"] = works[0]["bytes13"], works[0]["flops13"]
+    else:
+        used = [works[i % nsets] for i in range(steps)]
+        comp = {k: sum(w[k] for w in used) / len(used) for k in keys}
+    # share of the compensator factors in the resident expert weights (layer 0)
+    fams = layers[0].fam.values()
+    nb = [f.nbytes() for f in fams]
+    comp_b = sum(v for d in nb for k, v in d.items() if k not in ("packed", "sz"))
+    resident_comp = round(comp_b / sum(sum(d.values()) for d in nb), 4)
+    prefill = cfg.T * cfg.k / cfg.E > 64
+    pairs = cfg.T * (cfg.k + cfg.S)
+    ET = cfg.E + cfg.S
+    # the kernels the library's automatic path launches for the gate/up call
+    if prefill:
+        kname = "gemm_prefill_kernel<2,...,128> (gate/up + SwiGLU)"
+    elif cfg.T <= 32 or path == 1:
+        kname = "gemm_decode_kernel<MT,2> (gate/up + SwiGLU)"
+    elif path == 2 or (cfg.F * cfg.H <= (1 << 22) and pairs >= 16 * ET):
+        kname = "gate/up call: gemm_prefill_kernel<2,...> (tile kernel for every expert)"
+    else:
+        kname = "gate/up call: gemm_decode_kernel<MT,2> + gemm_prefill_kernel<2,...> (both paths)"
+    k_bytes, k_flops = comp["bytes13"], comp["flops13"]
+    if prefill:
+        achieved = k_flops / (k13_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = k_bytes / (k13_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(name, cfg.T, lr)}
+    roof.update({"kernel": kname, "alg_bytes_per_launch": int(k_bytes), "alg_flops_per_launch": int(k_flops),
+                 "avg_launch_us": round(k13_us, 2)})
+    return {"ms_step": ms_step, "pcts": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
+            "host_s": round(t_host, 3), "roofline": roof, "work": comp, "touched": works[0]["touched"],
+            "nsets": nsets, "layers": layers, "resident_comp_share": resident_comp}
+
+
+def prefill_check(cfg, layer, ntok):
+    """Sampled oracle check of the prefill layer: every output column of
+    ntok tokens (their expert FFNs recomputed in full width in float64)."""
+    import numpy as np
+    import oracle
+    import synth
+    toks = [0, cfg.T - 1, cfg.T // 2, cfg.T // 3][:max(1, ntok)]
+    X = layer.X.cpu().numpy()[toks]
+    logits = layer.logits.cpu().numpy()[toks]
+
+    def get_expert(e):
+        d = synth.gen_expert(cfg, layer.layer_idx, e, layer.ranks[e], device="cuda")
+        return oracle.quantize_expert({k: v.cpu() for k, v in d.items()}, lr_format=layer.lr_format)
+
+    ref = oracle.moe_layer_ref(X, logits, get_expert, cfg.k, cfg.S, cfg.renormalize)["out"]
+    got = layer.out.cpu().numpy().astype(np.float64)[toks]
+    rf, ma = oracle.rel_fro(got, ref), oracle.max_abs(got, ref)
+    return {"what": f"layer output of tokens {toks}, all {cfg.H} columns", "out_rel_fro": rf, "out_max_abs": ma,
+            "pass": bool(rf <= REL_FRO_TOL and ma <= MAX_ABS_TOL)}
 
 
 def traffic_for(config, T, lr="fp16"):

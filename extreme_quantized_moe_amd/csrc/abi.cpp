@@ -70,6 +70,7 @@ GemmArgs make_gemm_args(const milo_gemm_desc* d, const GemmPlan& p, char* ws) {
   a.ksplit = p.dec_ksplit;
   a.dec_max_rows = p.dec_max_rows;
   a.pre_min_rows = p.pre_launch ? (p.dec_mt ? p.dec_max_rows : 0) : 0;
+  a.x_bytes_32 = (uint64_t)d->x_rows * (uint64_t)d->K * 2u < (1ull << 32) ? 1 : 0;
   return a;
 }
 

@@ -26,6 +26,7 @@ struct GemmArgs {
   int epilogue, ksplit, dec_max_rows, pre_min_rows;
   int m_lo, m_hi;          // row-count range of the experts a decode launch handles
   int poison_over;         // decode launch: NaN-fill the rows of experts above m_hi
+  int x_bytes_32;          // x (rows x K fp16) spans under 4 GiB: 32-bit row offsets
 };
 
 struct GemmPlan;
@@ -56,6 +57,20 @@ __device__ __forceinline__ f16x8 dequant_step(const uint32_t h[16], int step, co
     o[v] = dequant_pair(h[pi], g.s, pair_offset(pi) == 64 ? g.c64 : g.c8);
   }
   u32x4 u = {o[0], o[1], o[2], o[3]};
+  return __builtin_bit_cast(f16x8, u);
+}
+
+// fp16 constant B fragments of the folded dequantization: all ones, and the
+// per-slot offset (64 or 8) of the pairs of K step `step`; a product with the
+// activation fragment gives the rows' sums of x and of x * off.
+__device__ __forceinline__ f16x8 ones_frag() {
+  const u32x4 u = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+  return __builtin_bit_cast(f16x8, u);
+}
+__device__ __forceinline__ f16x8 offset_frag(int step) {
+  u32x4 u;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) u[v] = pair_offset(4 * step + v) == 64 ? 0x54005400u : 0x48004800u;
   return __builtin_bit_cast(f16x8, u);
 }
 

@@ -92,17 +92,6 @@ __device__ void poison_over_rows(const GemmArgs& a, const DecShared& sh) {
   }
 }
 
-// fp16 constant fragments: all ones, and the per-slot offset of step `step`
-__device__ __forceinline__ f16x8 ones_frag() {
-  const u32x4 u = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
-  return __builtin_bit_cast(f16x8, u);
-}
-__device__ __forceinline__ f16x8 offset_frag(int step) {
-  u32x4 u;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) u[v] = pair_offset(4 * step + v) == 64 ? 0x54005400u : 0x48004800u;
-  return __builtin_bit_cast(f16x8, u);
-}
 
 template <int MP, int NW, int EPI>
 struct Dec {

@@ -23,9 +23,15 @@
 // interleaves, issued at raised wave priority.
 // Epilogue: low-rank term as two more matrix-core K-steps per 32 ranks, then
 // SWIGLU through LDS, or fp16 store, or route-weighted fp32 scatter.
+#include <type_traits>
+
 #include "gemm_common.hpp"
 
 namespace milo {
+
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle), as used
+// for plain byte-addressed buffer loads on this architecture family.
+constexpr int kBufRsrcWord3 = 0x00020000;
 
 constexpr int kXStride = kTileK;         // LDS row stride in halves (256 B; chunks swizzled)
 constexpr int kExStride = 68;            // floats per row of the SwiGLU exchange
@@ -34,10 +40,25 @@ constexpr size_t prefill_lds(int bm) {
   return 2 * bm * kExStride * 4 > 2 * bm * kXStride * 2 ? (size_t)2 * bm * kExStride * 4 : (size_t)2 * bm * kXStride * 2;
 }
 
-// Weight dequantization in packed fp16: from the extracted pair h = (off + q)
-// (exact), q = h - off is exact, and (q - z) s = fma(q, s, -z s) with -z s
-// rounded to fp16 once per group: two packed instructions per pair.  Error
-// per weight at most half an fp16 ulp of z s plus half an ulp of the result.
+// Weight dequantization, two forms.  Both start from the extracted pair
+// h = (off + q): two exact fp16 values.
+//
+// Packed (two roundings): q = h - off (exact), then fma(q, s, -z s) in packed
+// fp16 with -z s rounded to fp16 once per group -- two packed instructions
+// per pair of weights; error per weight at most half an fp16 ulp of z s plus
+// half an ulp of the result (about 4.8e-4 relative on one product).
+//
+// Mixed (one rounding): fp16(h s + c) with the group constant c = -(off + z) s
+// in fp32; the fused multiply-add runs in fp32 on the fp16 inputs and rounds
+// once (v_fma_mixlo / v_fma_mixhi, one instruction per weight), so the matrix
+// cores see (q - z) s rounded once (about 2.1e-4 relative on one product).
+// Constants: c64 = -s z - 64 s, c8 = c64 + 56 s (fp32), four instructions per
+// group.  Measured slower than the packed form (C3 gate/up +7 %, C4 +21 %).
+//
+// The kernels use the mixed form (tiles of up to two m-tiles fold the
+// dequantization out instead, see tile_products_fold): measured layer error
+// at 4096 tokens 9.2e-4 with the packed form (bound 1e-3), 4.7e-4 with the
+// mixed one.  The packed form is kept for reference and measurement.
 struct GroupConstPk {
   f16x2 s, nzs;
 };
@@ -53,7 +74,6 @@ __device__ __forceinline__ GroupConstPk group_const_pk(uint32_t szword) {
   return g;
 }
 
-// B operand of K step `step` from the step's four extracted pairs h4.
 __device__ __forceinline__ f16x8 dequant_pairs_pk(const uint32_t h4[4], int step, const GroupConstPk& g) {
   const f16x2 off64 = {(_Float16)64.f, (_Float16)64.f}, off8 = {(_Float16)8.f, (_Float16)8.f};
   u32x4 u;
@@ -66,12 +86,33 @@ __device__ __forceinline__ f16x8 dequant_pairs_pk(const uint32_t h4[4], int step
   return __builtin_bit_cast(f16x8, u);
 }
 
+struct GroupConstMix {
+  float s, c64, c8;
+};
+
+__device__ __forceinline__ GroupConstMix group_const_mix(uint32_t szword) {
+  const f16x2 sz = __builtin_bit_cast(f16x2, szword);   // (s, z)
+  GroupConstMix g;
+  g.s = (float)sz[0];
+  g.c64 = __builtin_fmaf(-g.s, (float)sz[1], -64.f * g.s);
+  g.c8 = __builtin_fmaf(56.f, g.s, g.c64);
+  return g;
+}
+
+__device__ __forceinline__ f16x8 dequant_pairs_mix(const uint32_t h4[4], int step, const GroupConstMix& g) {
+  u32x4 u;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) u[v] = dequant_pair(h4[v], g.s, pair_offset(4 * step + v) == 64 ? g.c64 : g.c8);
+  return __builtin_bit_cast(f16x8, u);
+}
+
 // Products of one K block of a wave: the codes of each of the lane's four
 // triplets (q: three planes, one word per row group) are extracted once; K
 // step s dequantizes its four B operands (one per 16-wide output group, with
-// the scale/zero words z) and multiplies them with the A fragments of the
-// NMT m-tiles, read from the LDS staging buffer xb at xoff[s].
-template <int NMT>
+// the scale/zero words z; mixed form if MIX) and multiplies them with the A
+// fragments of the NMT m-tiles, read from the LDS staging buffer xb at
+// xoff[s].
+template <int NMT, bool MIX>
 __device__ __forceinline__ void tile_products(const u32x4 (&q)[3], const u32x4 (&z)[2], const uint16_t* xb,
                                               const int (&xoff)[4], f32x4 (&acc)[NMT][4], const CodeConsts& kc) {
   uint32_t h[4][16];
@@ -86,13 +127,72 @@ __device__ __forceinline__ void tile_products(const u32x4 (&q)[3], const u32x4 (
       uint32_t h4[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) h4[v] = h[i][4 * s + v];
-      wf[i] = dequant_pairs_pk(h4, s, group_const_pk(idx < 4 ? z[0][idx] : z[1][idx - 4]));
+      const uint32_t zw = idx < 4 ? z[0][idx] : z[1][idx - 4];
+      if constexpr (MIX) wf[i] = dequant_pairs_mix(h4, s, group_const_mix(zw));
+      else wf[i] = dequant_pairs_pk(h4, s, group_const_pk(zw));
     }
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       const f16x8 xa = *(const f16x8*)(xb + xoff[s] + mt * 16 * kXStride);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[mt][i] = mfma16x16x32(xa, wf[i], acc[mt][i]);
+    }
+  }
+}
+
+// Products of one K block with the dequantization folded out (for tiles of
+// at most two m-tiles, where it costs fewer vector instructions than
+// dequantizing every weight, and rounds no weight): the extracted pairs
+// (off + q) are exact fp16 B operands; per 64-wide group g of the block the
+// accumulator p starts at -(z sum x) - (sum x off) and two products add
+// sum x (off + q), so p = sum x (q - z), and acc += s p in fp32.  The row sums
+// of x and of x * off are products of the A fragments with constant
+// fragments (ones, offsets).
+template <int NMT>
+__device__ __forceinline__ void tile_products_fold(const u32x4 (&q)[3], const u32x4 (&z)[2], const uint16_t* xb,
+                                                   const int (&xoff)[4], f32x4 (&acc)[NMT][4],
+                                                   const CodeConsts& kc) {
+  f16x8 xa[NMT][4];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xa[mt][s] = *(const f16x8*)(xb + xoff[s] + mt * 16 * kXStride);
+  const f16x8 one = ones_frag();
+  f32x4 xs[NMT][2], xo[NMT][2];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      xs[mt][g] = mfma16x16x32(xa[mt][2 * g], one, zero);
+      xs[mt][g] = mfma16x16x32(xa[mt][2 * g + 1], one, xs[mt][g]);
+      xo[mt][g] = mfma16x16x32(xa[mt][2 * g], offset_frag(2 * g), zero);
+      xo[mt][g] = mfma16x16x32(xa[mt][2 * g + 1], offset_frag(2 * g + 1), xo[mt][g]);
+    }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t h[16];
+    extract_triplet(q[0][i], q[1][i], q[2][i], h, kc);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int idx = 2 * i + g;
+      const uint32_t w = idx < 4 ? z[0][idx] : z[1][idx - 4];
+      const float sc = half_bits_to_float(w & 0xFFFFu);
+      const float zp = half_bits_to_float(w >> 16);
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        f32x4 p;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = __builtin_fmaf(-zp, xs[mt][g][r], -xo[mt][g][r]);
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+          const int step = 2 * g + ss;
+          const u32x4 u = {h[4 * step], h[4 * step + 1], h[4 * step + 2], h[4 * step + 3]};
+          p = mfma16x16x32(xa[mt][step], __builtin_bit_cast(f16x8, u), p);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mt][i][r] = __builtin_fmaf(sc, p[r], acc[mt][i][r]);
+      }
     }
   }
 }
@@ -237,12 +337,13 @@ __device__ __forceinline__ void tile_finish(const GemmArgs& a, const RowTile& rt
 }
 
 // One block's tile: NMT active 16-row m-tiles (the tile's rows, rounded up).
-template <int NW, bool LRQ, int NMT>
+template <int NW, bool LRQ, int NMT, bool X32>
 __device__ __forceinline__ void tile_body(const GemmArgs& a, const RowTile& rt, uint16_t* lds,
                                           const CodeConsts& kc) {
   constexpr int D = TileDepth<NMT>::D;
   constexpr int kXBuf = NMT * 16 * kXStride;   // halves per staging buffer
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
   const int f = (NW == 2) ? (wave & 1) : 0;
   const int nt = (NW == 2) ? (2 * blockIdx.x + (wave >> 1)) : (4 * blockIdx.x + wave);
@@ -263,22 +364,40 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const RowTile& rt, 
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) xoff[s4] = (lane & 15) * kXStride + 8 * ((4 * s4 + (lane >> 4)) ^ (lane & 15));
 
-  // ---- weights of this wave (a wave without an output tile loads tile 0)
+  // ---- weights of this wave (a wave without an output tile loads tile 0).
+  // Loads are buffer loads: a scalar resource per array, the lane's byte
+  // offset in a register, the K block's advance as a scalar offset.
   const int ntc = wave_on ? nt : 0;
-  const uint32_t* tbase = a.packed[f] + e * a.words_per_expert + (size_t)ntc * a.kblocks * kTileWords + 4 * lane;
-  const uint32_t* sbase =
-      a.sz[f] + e * a.sz_per_expert + (size_t)ntc * a.kblocks * kTileSzWords + 8 * (lane & 15);
+  const uint32_t* tbase = a.packed[f] + e * a.words_per_expert + (size_t)ntc * a.kblocks * kTileWords;
+  const uint32_t* sbase = a.sz[f] + e * a.sz_per_expert + (size_t)ntc * a.kblocks * kTileSzWords;
   const int KB = a.kblocks;
-  auto issue = [&](TileStage<NMT>& S, int kb) {
-    const uint32_t* tp = tbase + (size_t)kb * kTileWords;
-    S.q[0] = *(const u32x4*)(tp);
-    S.q[1] = *(const u32x4*)(tp + 256);
-    S.q[2] = *(const u32x4*)(tp + 512);
-    const uint32_t* sp = sbase + (size_t)kb * kTileSzWords;
-    S.z[0] = *(const u32x4*)(sp);
-    S.z[1] = *(const u32x4*)(sp + 4);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)tbase, 0, KB * kTileWords * 4, kBufRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)sbase, 0, KB * kTileSzWords * 4, kBufRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, X32 ? (int)(0xFFFFFFFFu >> 1) : 0, kBufRsrcWord3);
+  uint32_t xoff32[NMT];
+  if constexpr (X32) {
 #pragma unroll
-    for (int j = 0; j < NMT; ++j) S.x[j] = *(const u32x4*)(xsrc[j] + (size_t)kb * kTileK);
+    for (int j = 0; j < NMT; ++j) xoff32[j] = (uint32_t)((const char*)xsrc[j] - (const char*)a.x);
+  }
+  auto issue = [&](TileStage<NMT>& S, int kb) {
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      S.q[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, 16 * lane + 1024 * p,
+                                                                                kb * kTileWords * 4, 0));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      S.z[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 32 * (lane & 15) + 16 * h,
+                                                                                kb * kTileSzWords * 4, 0));
+#pragma unroll
+    for (int j = 0; j < NMT; ++j) {
+      if constexpr (X32)
+        S.x[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff32[j], kb * kTileK * 2, 0));
+      else
+        S.x[j] = *(const u32x4*)(xsrc[j] + (size_t)kb * kTileK);
+    }
   };
   auto put_x = [&](const TileStage<NMT>& S, int buf) {
 #pragma unroll
@@ -295,7 +414,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const RowTile& rt, 
   // are extracted once; K step s dequantizes its four B operands (one per
   // 16-wide output group) and multiplies them with the m-tiles' A fragments
   auto compute = [&](const TileStage<NMT>& S, int buf) {
-    tile_products<NMT>(S.q, S.z, lds + buf * kXBuf, xoff, acc, kc);
+    if constexpr (NMT <= 2) tile_products_fold<NMT>(S.q, S.z, lds + buf * kXBuf, xoff, acc, kc);
+    else tile_products<NMT, true>(S.q, S.z, lds + buf * kXBuf, xoff, acc, kc);
   };
 
   // ---- K loop over a ring of D register stages.  Stage j (K block j) sits
@@ -356,40 +476,67 @@ __device__ __forceinline__ void dma4(const void* g, void* l) {
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
-template <int NW, bool LRQ, int NMT>
+template <int NW, bool LRQ, int NMT, bool X32>
 __device__ __forceinline__ void tile_body_lds(const GemmArgs& a, const RowTile& rt, uint16_t* lds,
                                               const CodeConsts& kc) {
   constexpr int kXBuf = NMT * 16 * kXStride;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
   const int f = (NW == 2) ? (wave & 1) : 0;
   const int nt = (NW == 2) ? (2 * blockIdx.x + (wave >> 1)) : (4 * blockIdx.x + wave);
   const bool wave_on = nt < a.n_tiles;
 
   // activation staging as in tile_body, but by LDS transfers: load j of a
-  // wave fills rows 16 j + 4 wave .. + 3 (lane l: row + l / 16, slot l % 16)
+  // wave fills rows 16 j + 4 wave .. + 3 (lane l: row + l / 16, slot l % 16).
+  // Sources as a wave-uniform base plus a per-lane byte offset (32-bit when
+  // the activations are under 4 GiB), so that only scalar adds advance them.
   const int srow = 4 * wave + (lane >> 4);
   const uint16_t* xsrc[NMT];
   stage_rows<NMT>(a, m0, M, base, srow, lane, xsrc);
+  uint32_t xoff32[NMT];
+  if constexpr (X32) {
+#pragma unroll
+    for (int j = 0; j < NMT; ++j) xoff32[j] = (uint32_t)((const char*)xsrc[j] - (const char*)a.x);
+  }
   int xoff[4];
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) xoff[s4] = (lane & 15) * kXStride + 8 * ((4 * s4 + (lane >> 4)) ^ (lane & 15));
 
   const int ntc = wave_on ? nt : 0;
-  const uint32_t* tbase = a.packed[f] + e * a.words_per_expert + (size_t)ntc * a.kblocks * kTileWords + 4 * lane;
-  const uint32_t* sbase = a.sz[f] + e * a.sz_per_expert + (size_t)ntc * a.kblocks * kTileSzWords + lane;
+  const char* tbase = (const char*)(a.packed[f] + e * a.words_per_expert + (size_t)ntc * a.kblocks * kTileWords);
+  const char* sbase = (const char*)(a.sz[f] + e * a.sz_per_expert + (size_t)ntc * a.kblocks * kTileSzWords);
   uint16_t* wslot = lds + 2 * kXBuf + wave * kWSlotHalves;
   const int KB = a.kblocks;
-  auto issue = [&](int kb, int buf) {
+  // With activations under 4 GiB every transfer is a buffer load into LDS:
+  // a scalar resource per array, the per-lane byte offset in a register and
+  // the K block's advance as a scalar offset (no vector address arithmetic).
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, X32 ? (int)(0xFFFFFFFFu >> 1) : 0, kBufRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)tbase, 0, KB * kTileWords * 4, kBufRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)sbase, 0, KB * kTileSzWords * 4, kBufRsrcWord3);
+  auto issue = [&](int kb, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
 #pragma unroll
-    for (int j = 0; j < NMT; ++j)
-      dma16(xsrc[j] + (size_t)kb * kTileK, lds + buf * kXBuf + (16 * j + 4 * wave) * kXStride);
-    const uint32_t* tp = tbase + (size_t)kb * kTileWords;
+    for (int j = 0; j < NMT; ++j) {
+      uint16_t* dst = lds + buf * kXBuf + (16 * j + 4 * wave) * kXStride;
+      if constexpr (X32) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)dst, 16, xoff32[j],
+                                                 kb * kTileK * 2, 0, 0);
+      } else {
+        dma16((const char*)xsrc[j] + (size_t)kb * kTileK * 2, dst);
+      }
+    }
 #pragma unroll
-    for (int p = 0; p < 3; ++p) dma16(tp + 256 * p, wslot + 512 * p);
-    const uint32_t* sp = sbase + (size_t)kb * kTileSzWords;
-    dma4(sp, wslot + 1536);
-    dma4(sp + 64, wslot + 1536 + 128);
+    for (int p = 0; p < 3; ++p)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(wslot + 512 * p), 16,
+                                               16 * lane + 1024 * p, kb * kTileWords * 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(wslot + 1536), 4,
+                                             4 * lane, kb * kTileSzWords * 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(wslot + 1536 + 128), 4,
+                                             4 * lane + 256, kb * kTileSzWords * 4, 0, 0);
   };
 
   f32x4 acc[NMT][4];
@@ -398,13 +545,13 @@ __device__ __forceinline__ void tile_body_lds(const GemmArgs& a, const RowTile& 
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
-  for (int kb = 0; kb < KB; ++kb) {
-    const int buf = kb & 1;
-    // the wave's weights of block kb: slot -> registers (lane l: its 16 bytes
-    // of each plane; the scale/zero words of its rows, 32 bytes at 32 (l mod 16))
+  // one K block: the wave's weights of block kb from its slot into registers
+  // (lane l: its 16 bytes of each plane; the scale/zero words of its rows, 32
+  // bytes at 32 (l mod 16)), the next block's transfers issued into the slot
+  // and the other activation buffer, then the products; the loop is unrolled
+  // by two so the buffer offsets are constants
+  auto step = [&](int kb, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     u32x4 q[3], z[2];
 #pragma unroll
     for (int p = 0; p < 3; ++p) q[p] = *(const u32x4*)(wslot + 512 * p + 8 * lane);
@@ -412,13 +559,21 @@ __device__ __forceinline__ void tile_body_lds(const GemmArgs& a, const RowTile& 
     z[1] = *(const u32x4*)(wslot + 1536 + 16 * (lane & 15) + 8);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_sched_barrier(0);
-    issue(kb + 1 < KB ? kb + 1 : kb, buf ^ 1);   // the last block re-loads its own data
+    issue(kb + 1 < KB ? kb + 1 : kb, std::integral_constant<int, buf ^ 1>());   // the last block re-loads its own data
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(2);
-    if (wave_on) tile_products<NMT>(q, z, lds + buf * kXBuf, xoff, acc, kc);
+    if (wave_on) tile_products<NMT, true>(q, z, lds + buf * kXBuf, xoff, acc, kc);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+  };
+
+  issue(0, std::integral_constant<int, 0>());
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  for (int kb = 0; kb < KB; kb += 2) {
+    step(kb, std::integral_constant<int, 0>());
+    if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>());
   }
   tile_finish<NW, LRQ, NMT>(a, rt, lds, kc, acc, f, nt, wave_on);
 }
@@ -436,11 +591,16 @@ gemm_prefill_kernel(GemmArgs a) {
     // only the tile's own rows: fewer products and staged rows for the
     // small experts (a 3-row expert costs one m-tile, not four)
     const int rows = rt.rows - rt.m0;
-    if (rows <= 16) tile_body<NW, LRQ, 1>(a, rt, lds, kc);
-    else if (rows <= 32) tile_body<NW, LRQ, 2>(a, rt, lds, kc);
-    else tile_body<NW, LRQ, 4>(a, rt, lds, kc);
+    if (a.x_bytes_32) {
+      if (rows <= 16) tile_body<NW, LRQ, 1, true>(a, rt, lds, kc);
+      else if (rows <= 32) tile_body<NW, LRQ, 2, true>(a, rt, lds, kc);
+      else tile_body<NW, LRQ, 4, true>(a, rt, lds, kc);
+    } else {
+      tile_body<NW, LRQ, 4, false>(a, rt, lds, kc);
+    }
   } else {
-    tile_body_lds<NW, LRQ, BM / 16>(a, rt, lds, kc);
+    if (a.x_bytes_32) tile_body_lds<NW, LRQ, BM / 16, true>(a, rt, lds, kc);
+    else tile_body_lds<NW, LRQ, BM / 16, false>(a, rt, lds, kc);
   }
 }
 

@@ -74,7 +74,8 @@ def _check_g(cfg, layer, lay, ncols, seed, lr_format="fp16"):
             q, s, z = _quantize_rows(d[n], cols)
             h.append(oracle.linear_ref(rows, q, s, z, d[a], d[b][:, cols]))
         want[off[e]:off[e + 1]] = oracle.silu(h[0]) * h[1]
-    assert_close(got, want, f"{cfg.name} G (all pairs, {ncols} columns, {lr_format} factors)")
+    rf, ma = assert_close(got, want, f"{cfg.name} G (all pairs, {ncols} columns, {lr_format} factors)")
+    print(f"{cfg.name} G (all pairs, {ncols} columns, {lr_format} factors): rel_fro {rf:.2e} max_abs {ma:.2e}")
 
 
 def _check_out(cfg, layer, lay, toks, ncols, seed, lr_format="fp16"):
@@ -95,7 +96,8 @@ def _check_out(cfg, layer, lay, toks, ncols, seed, lr_format="fp16"):
     ref = oracle.moe_layer_ref(X, logits, get_expert, cfg.k, cfg.S, cfg.renormalize,
                                out_cols=np.arange(len(cols)))
     got = lay.out.cpu().numpy().astype(np.float64)[toks][:, cols]
-    assert_close(got, ref["out"], f"{cfg.name} out (tokens {list(toks)}, {len(cols)} columns, {lr_format} factors)")
+    rf, ma = assert_close(got, ref["out"], f"{cfg.name} out ({len(toks)} tokens, {len(cols)} columns, {lr_format} factors)")
+    print(f"{cfg.name} out ({len(toks)} tokens, {len(cols)} columns, {lr_format} factors): rel_fro {rf:.2e} max_abs {ma:.2e}")
 
 
 def _check_tokens_full(cfg, layer, lay, toks, what):
