@@ -13,7 +13,10 @@
 //   2. route_scan  (one block): per expert, exclusive prefix of the block
 //      counts; exclusive prefix over experts -> offsets.
 //   3. route_scatter: final positions.
-// With a single token block, phase 1 does all three (one launch).
+// With a single token block, phase 1 does all three (one launch), except for
+// rows wider than 16 experts: then route_topk_wave selects on one wave per
+// token across many compute units and route_sort_block ranks, scans and
+// scatters in one block (two launches).
 #include "milo_internal.hpp"
 
 namespace milo {
@@ -391,11 +394,187 @@ route_scatter(int T, int E, int k, int S, const int32_t* __restrict__ ids,
   }
 }
 
+// Wide rows (more than 16 experts), up to 256 tokens: two launches that
+// spread the selection over many compute units instead of one block.
+//
+// route_topk_wave: one wave per token.  Lane l holds experts l + 64 u
+// (u < NV); the row maximum and the softmax denominator are butterfly
+// reductions (every lane ends with the same value); each of the k picks is a
+// wave arg-max over (logit, lower expert id on ties) of the lanes' best
+// remaining expert, the owning lane then marks it taken.  Lane j < k writes
+// pick j's id and weight; lanes k .. k+S-1 the shared slots' weight 1.
+template <int NV>
+__global__ void __launch_bounds__(256)
+route_topk_wave(const float* __restrict__ logits, int T, int E, int k, int S, int renorm,
+                int32_t* __restrict__ ids, float* __restrict__ topw, float* __restrict__ slot_w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;                       // the whole wave
+  const int slots = k + S;
+  const float* row = logits + (size_t)t * E;
+  float v[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) v[u] = lane + 64 * u < E ? row[lane + 64 * u] : -INFINITY;
+  float mx = v[0];
+#pragma unroll
+  for (int u = 1; u < NV; ++u) mx = fmaxf(mx, v[u]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  float den = 0.f;
+#pragma unroll
+  for (int u = 0; u < NV; ++u)
+    if (lane + 64 * u < E) den += expf(v[u] - mx);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
+  uint32_t taken = 0;
+  float bsel[kMaxK];
+  int isel[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    bsel[j] = -INFINITY;
+    isel[j] = 0;
+    if (j < k) {
+      float bv = -INFINITY;
+      int bi = 1 << 30;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int e = lane + 64 * u;
+        if (e < E && !((taken >> u) & 1u) && (bi == (1 << 30) || v[u] > bv)) {
+          bv = v[u];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      bsel[j] = bv;
+      isel[j] = bi;
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    }
+  }
+  float sel[kMaxK], selsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    sel[j] = j < k ? expf(bsel[j] - mx) : 0.f;
+    selsum += sel[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k && lane == j) {
+      const float w = renorm ? sel[j] / selsum : sel[j] / den;
+      ids[(size_t)t * k + j] = isel[j];
+      topw[(size_t)t * k + j] = w;
+      slot_w[(size_t)t * slots + j] = w;
+    }
+  }
+  if (lane >= k && lane < slots) slot_w[(size_t)t * slots + lane] = 1.0f;
+}
+
+// route_sort_block: one block, up to 256 tokens.  Each slot's expert (from
+// the picks, or the shared experts) sets its token's bit in an LDS bitmap
+// per expert; the expert counts are scanned by one wave into the offsets;
+// a slot's position is its expert's offset plus the number of earlier
+// tokens with that expert (popcounts of the bitmap), which keeps pairs in
+// slot order within an expert.
+__global__ void __launch_bounds__(1024)
+route_sort_block(const int32_t* __restrict__ ids, int T, int E, int k, int S, int32_t* __restrict__ sorted_pairs,
+                 int32_t* __restrict__ pair_pos, int32_t* __restrict__ offsets) {
+  __shared__ uint32_t bits[kMaxExperts][kBitWords];
+  __shared__ int scan_lds[kMaxExperts];
+  const int tid = threadIdx.x;
+  const int ET = E + S, slots = k + S, P = T * slots;
+  for (int x = tid; x < ET * kBitWords; x += 1024) (&bits[0][0])[x] = 0u;
+  __syncthreads();
+  constexpr int kPer = kRouteBlock * kMaxSlots / 1024;   // slots per thread, at most
+  int ex[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int s = tid + 1024 * u;
+    ex[u] = 0;
+    if (s < P) {
+      const int t = s / slots, j = s - t * slots;
+      ex[u] = j < k ? ids[(size_t)t * k + j] : E + (j - k);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int s = tid + 1024 * u;
+    if (s < P) {
+      const int t = s / slots;
+      atomicOr(&bits[ex[u]][t >> 5], 1u << (t & 31));
+    }
+  }
+  __syncthreads();
+  // one wave scans the expert counts, four experts per lane
+  if (tid < 64) {
+    int c[4], lsum = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * tid + u;
+      c[u] = 0;
+      if (e < ET)
+        for (int w = 0; w < kBitWords; ++w) c[u] += __popc(bits[e][w]);
+      lsum += c[u];
+    }
+    int incl = lsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (tid >= o) incl += v;
+    }
+    int run = incl - lsum;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * tid + u;
+      if (e < ET) {
+        scan_lds[e] = run;
+        offsets[e] = run;
+      }
+      run += c[u];
+    }
+    if (tid == 63) offsets[ET] = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int s = tid + 1024 * u;
+    if (s < P) {
+      const int t = s / slots;
+      const uint32_t* brow = bits[ex[u]];
+      int r = 0;
+      for (int w = 0; w < (t >> 5); ++w) r += __popc(brow[w]);
+      r += __popc(brow[t >> 5] & ((1u << (t & 31)) - 1u));
+      const int pos = scan_lds[ex[u]] + r;
+      sorted_pairs[pos] = s;
+      pair_pos[s] = pos;
+    }
+  }
+}
+
 int32_t launch_route(const float* logits, int T, int E, int k, int S, int renorm,
                      int32_t* ids, float* w, float* slot_w, int32_t* sorted_pairs,
                      int32_t* pair_pos, int32_t* offsets, void* ws, hipStream_t st) {
   const int nblocks = (T + kRouteBlock - 1) / kRouteBlock;
   int32_t* counts = (int32_t*)ws;
+  if (E > 16 && T <= kRouteBlock) {
+    // wide rows, one token block: the selection on one wave per token over
+    // many compute units, then the sort in one block (C4: 23.6 us in one
+    // block before)
+    const dim3 g((T + 3) / 4);
+    if (E <= 64) hipLaunchKernelGGL(route_topk_wave<1>, g, dim3(256), 0, st, logits, T, E, k, S, renorm, ids, w, slot_w);
+    else if (E <= 128) hipLaunchKernelGGL(route_topk_wave<2>, g, dim3(256), 0, st, logits, T, E, k, S, renorm, ids, w, slot_w);
+    else hipLaunchKernelGGL(route_topk_wave<4>, g, dim3(256), 0, st, logits, T, E, k, S, renorm, ids, w, slot_w);
+    int32_t rc = hip_status(hipGetLastError(), "route_topk_wave launch");
+    if (rc != MILO_OK) return rc;
+    hipLaunchKernelGGL(route_sort_block, dim3(1), dim3(1024), 0, st, ids, T, E, k, S, sorted_pairs, pair_pos, offsets);
+    return hip_status(hipGetLastError(), "route_sort_block launch");
+  }
   // one thread per token up to 16 experts, four above (shorter selection chains)
 #define MILO_ROUTE_LAUNCH(L, NV)                                                                             \
   hipLaunchKernelGGL((route_topk<L, NV>), dim3(nblocks), dim3(L * kRouteBlock), 0, st, logits, T, E, k, S, \
