@@ -179,6 +179,7 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
   p->dec_max_rows = 16 * p->dec_mt;
   p->pre_bm = P >= 256 * d->num_experts ? 128 : 64;
   p->pre_tiles = (P + p->pre_bm - 1) / p->pre_bm + d->num_experts;
+  p->pre_slots = 2 * device_cu_count();
 
   if (p->dec_mt) {
     // persistent grid: two blocks per compute unit (the kernel's register

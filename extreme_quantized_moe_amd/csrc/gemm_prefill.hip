@@ -33,6 +33,7 @@ namespace milo {
 // for plain byte-addressed buffer loads on this architecture family.
 constexpr int kBufRsrcWord3 = 0x00020000;
 
+constexpr int kMaxTileExperts = 256;
 constexpr int kXStride = kTileK;         // LDS row stride in halves (256 B; chunks swizzled)
 constexpr int kExStride = 68;            // floats per row of the SwiGLU exchange
 // LDS of a BM-row block: two staging buffers, or the SwiGLU exchange
@@ -337,16 +338,15 @@ __device__ __forceinline__ void tile_finish(const GemmArgs& a, const RowTile& rt
 }
 
 // One block's tile: NMT active 16-row m-tiles (the tile's rows, rounded up).
-template <int NW, bool LRQ, int NMT, bool X32>
+template <int NW, bool LRQ, int NMT, bool X32, int D = TileDepth<NMT>::D>
 __device__ __forceinline__ void tile_body(const GemmArgs& a, const RowTile& rt, uint16_t* lds,
-                                          const CodeConsts& kc) {
-  constexpr int D = TileDepth<NMT>::D;
+                                          const CodeConsts& kc, int ng) {
   constexpr int kXBuf = NMT * 16 * kXStride;   // halves per staging buffer
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
   const int f = (NW == 2) ? (wave & 1) : 0;
-  const int nt = (NW == 2) ? (2 * blockIdx.x + (wave >> 1)) : (4 * blockIdx.x + wave);
+  const int nt = (NW == 2) ? (2 * ng + (wave >> 1)) : (4 * ng + wave);
   const bool wave_on = nt < a.n_tiles;
 
   // ---- activation staging: lane l of wave w stages, for j < NMT, row
@@ -478,13 +478,13 @@ constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
 template <int NW, bool LRQ, int NMT, bool X32>
 __device__ __forceinline__ void tile_body_lds(const GemmArgs& a, const RowTile& rt, uint16_t* lds,
-                                              const CodeConsts& kc) {
+                                              const CodeConsts& kc, int ng) {
   constexpr int kXBuf = NMT * 16 * kXStride;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
   const int f = (NW == 2) ? (wave & 1) : 0;
-  const int nt = (NW == 2) ? (2 * blockIdx.x + (wave >> 1)) : (4 * blockIdx.x + wave);
+  const int nt = (NW == 2) ? (2 * ng + (wave >> 1)) : (4 * ng + wave);
   const bool wave_on = nt < a.n_tiles;
 
   // activation staging as in tile_body, but by LDS transfers: load j of a
@@ -592,18 +592,131 @@ gemm_prefill_kernel(GemmArgs a) {
     // small experts (a 3-row expert costs one m-tile, not four)
     const int rows = rt.rows - rt.m0;
     if (a.x_bytes_32) {
-      if (rows <= 16) tile_body<NW, LRQ, 1, true>(a, rt, lds, kc);
-      else if (rows <= 32) tile_body<NW, LRQ, 2, true>(a, rt, lds, kc);
-      else tile_body<NW, LRQ, 4, true>(a, rt, lds, kc);
+      if (rows <= 16) tile_body<NW, LRQ, 1, true>(a, rt, lds, kc, blockIdx.x);
+      else if (rows <= 32) tile_body<NW, LRQ, 2, true>(a, rt, lds, kc, blockIdx.x);
+      else tile_body<NW, LRQ, 4, true>(a, rt, lds, kc, blockIdx.x);
     } else {
-      tile_body<NW, LRQ, 4, false>(a, rt, lds, kc);
+      tile_body<NW, LRQ, 4, false>(a, rt, lds, kc, blockIdx.x);
     }
   } else {
-    if (a.x_bytes_32) tile_body_lds<NW, LRQ, BM / 16, true>(a, rt, lds, kc);
-    else tile_body_lds<NW, LRQ, BM / 16, false>(a, rt, lds, kc);
+    if (a.x_bytes_32) tile_body_lds<NW, LRQ, BM / 16, true>(a, rt, lds, kc, blockIdx.x);
+    else tile_body_lds<NW, LRQ, BM / 16, false>(a, rt, lds, kc, blockIdx.x);
   }
 }
 
+
+// 64-row tiles, persistent: a grid of two blocks per compute unit walks the
+// work items (row tile, n-tile group), n-tile groups fastest (consecutive
+// items share activation rows).  The row tiles are listed once per block:
+// the experts' full 64-row tiles first, then their partial last tiles (the
+// bigger tiles start first), as prefix sums in LDS; an item finds its tile by
+// binary search.  No block starts past the last item, and the expert scan
+// runs once per block instead of once per tile.  With three tile shapes in
+// one loop the registers allow two stages in flight for the 2- and 4-m-tile
+// shapes; that suits the gate/up form (two weight families per wave), while
+// the one-family form keeps its three stages in the one-tile-per-block
+// kernel, measured faster there.
+template <int NW, bool LRQ>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_prefill_persistent(GemmArgs a, int n_groups) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  __shared__ int tab_full[kMaxTileExperts + 1], tab_part[kMaxTileExperts + 1];
+  __shared__ int e_base[kMaxTileExperts], e_rows[kMaxTileExperts], e_rk0[kMaxTileExperts],
+      e_rk1[kMaxTileExperts];
+  const CodeConsts kc = make_code_consts();
+  const int E = a.num_experts;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int32_t* rk0 = a.rp ? a.rank[0] : a.offsets;   // valid dummy when unused
+    const int32_t* rk1 = a.rp ? a.rank[1] : a.offsets;
+    int nf[4], np[4], o0[4], o1[4], r0[4], r1[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = 4 * lane + c;
+      const int ec = e < E ? e : E - 1;
+      o0[c] = a.offsets[ec];
+      o1[c] = a.offsets[ec + 1];
+      r0[c] = rk0[ec];
+      r1[c] = rk1[ec];
+    }
+    int sf = 0, sp = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = 4 * lane + c;
+      const int M = e < E ? o1[c] - o0[c] : 0;
+      const bool in = M > a.pre_min_rows;
+      nf[c] = in ? M / 64 : 0;
+      np[c] = in && (M % 64) ? 1 : 0;
+      sf += nf[c];
+      sp += np[c];
+      if (e < E) {
+        e_base[e] = o0[c];
+        e_rows[e] = M;
+        e_rk0[e] = a.rp ? r0[c] : 0;
+        e_rk1[e] = a.rp ? r1[c] : 0;
+      }
+    }
+    int incf = sf, incp = sp;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int vf = __shfl_up(incf, o), vp = __shfl_up(incp, o);
+      if (lane >= o) {
+        incf += vf;
+        incp += vp;
+      }
+    }
+    int rf = incf - sf, rp = incp - sp;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = 4 * lane + c;
+      if (e < E) {
+        tab_full[e] = rf;
+        tab_part[e] = rp;
+      }
+      rf += nf[c];
+      rp += np[c];
+    }
+    if (lane == 63) {   // the totals (E may be 256, past every lane's experts)
+      tab_full[E] = incf;
+      tab_part[E] = incp;
+    }
+  }
+  __syncthreads();
+  const int TF = tab_full[E], TP = tab_part[E];
+  const int n_items = (TF + TP) * n_groups;
+  // the last expert with tab[e] <= t (experts without tiles share their
+  // successor's start and are skipped)
+  auto find = [&](const int* tab, int t) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tab[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  for (int w = blockIdx.x; w < n_items; w += gridDim.x) {
+    const int tile = w / n_groups, ng = w - tile * n_groups;
+    RowTile rt;
+    if (tile < TF) {
+      rt.e = find(tab_full, tile);
+      rt.m0 = (tile - tab_full[rt.e]) * 64;
+    } else {
+      rt.e = find(tab_part, tile - TF);
+      rt.m0 = (e_rows[rt.e] / 64) * 64;
+    }
+    rt.rows = e_rows[rt.e];
+    rt.base = e_base[rt.e];
+    rt.rank0 = e_rk0[rt.e];
+    rt.rank1 = e_rk1[rt.e];
+    // the launcher takes this kernel only when the activations fit 32-bit
+    // offsets
+    if (rt.rows - rt.m0 <= 16) tile_body<NW, LRQ, 1, true>(a, rt, lds, kc, ng);
+    else if (rt.rows - rt.m0 <= 32) tile_body<NW, LRQ, 2, true, 2>(a, rt, lds, kc, ng);
+    else tile_body<NW, LRQ, 4, true, 2>(a, rt, lds, kc, ng);
+    __syncthreads();   // the next item reuses the LDS
+  }
+}
 
 int32_t launch_gemm_prefill(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hipStream_t st) {
   if (!p.pre_launch) return MILO_OK;
@@ -622,7 +735,13 @@ int32_t launch_gemm_prefill(const milo_gemm_desc* d, const GemmPlan& p, char* ws
     }
   } else {
     const size_t lds = prefill_lds(64);
-    if (d->n_w == 2) {
+    const int n_groups = grid.x;
+    const int items_bound = n_groups * p.pre_tiles;
+    const int pgrid = items_bound < p.pre_slots ? items_bound : p.pre_slots;
+    if (d->n_w == 2 && a.x_bytes_32) {
+      if (a.lrq) hipLaunchKernelGGL((gemm_prefill_persistent<2, true>), dim3(pgrid), dim3(256), lds, st, a, n_groups);
+      else hipLaunchKernelGGL((gemm_prefill_persistent<2, false>), dim3(pgrid), dim3(256), lds, st, a, n_groups);
+    } else if (d->n_w == 2) {
       if (a.lrq) hipLaunchKernelGGL((gemm_prefill_kernel<2, true, 64>), grid, dim3(256), lds, st, a);
       else hipLaunchKernelGGL((gemm_prefill_kernel<2, false, 64>), grid, dim3(256), lds, st, a);
     } else {

@@ -266,6 +266,7 @@ struct GemmPlan {
   int pre_launch;    // launch the tile kernel
   int pre_tiles;     // grid.y bound of the tile kernel (row tiles)
   int pre_bm;        // rows per block of the tile kernel (64 or 128)
+  int pre_slots;     // persistent grid of the 64-row tile kernel (two blocks per compute unit)
   // workspace carve-up (byte offsets)
   size_t off_t, off_xg, off_pw, off_dec_part, off_tpart, total;
 };

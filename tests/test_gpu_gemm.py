@@ -193,6 +193,24 @@ def test_prefill_large_experts(T, K, epi):
     assert_close(got, want, f"large experts T={T} K={K} {epi}")
 
 
+@pytest.mark.parametrize("epi", ["swiglu", "route"])
+def test_prefill_every_tile_shape_256_experts(epi):
+    """64-row tile launch over 256 experts whose row counts give every tile
+    shape: none (0 rows), one m-tile (1, 16 rows), two (17, 32), four (33,
+    63), full tiles alone (64, 128) and full tiles with each shape of
+    partial tile (65, 81, 100, 150); the expert table of the gate/up launch
+    holds its totals past the last expert."""
+    m = _m()
+    pattern = [0, 1, 16, 17, 32, 33, 63, 64, 65, 81, 100, 128, 150]
+    E = 256
+    counts = [pattern[(5 * e) % len(pattern)] for e in range(E)]
+    epilogue = {"swiglu": m.EPI_SWIGLU, "route": m.EPI_ROUTE_SCALE}[epi]
+    got, want = _moe_case(E=E, S=0, N=128, K=256, ranks=[16, 0, 64, 8, 32, 24, 48, 40][:4] * 64,
+                          T=sum(counts), k=1, epilogue=epilogue, path=PATHS["prefill"], seed=400,
+                          logits=_counts_logits(counts, E), max_rows=max(counts))
+    assert_close(got, want, f"256 experts, every tile shape, {epi}")
+
+
 @pytest.mark.parametrize("epi,lr", [("swiglu", "fp16"), ("route", "fp16"), ("swiglu", "int3")])
 def test_auto_small_matrices_sparse_batch(epi, lr):
     """Automatic path, small matrices, experts averaging under 16 rows with
