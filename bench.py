@@ -293,7 +293,6 @@ def cpu_model():
 def device_info(timer):
     """GPU name, compute units and clocks: the runtime's figures, and the
     shader clock the driver reports after the timed region (best effort)."""
-    import subprocess
     import torch
     pr = torch.cuda.get_device_properties(0)
     info = {"gpu": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count}
@@ -303,15 +302,18 @@ def device_info(timer):
     HIP_ATTR_CLOCK_RATE = 5            # kHz, peak
     if h.hipDeviceGetAttribute(C.byref(v), HIP_ATTR_CLOCK_RATE, 0) == 0:
         info["peak_clock_mhz"] = v.value // 1000
+    # the current shader clock level from the driver's sysfs table (the line
+    # marked '*'); a file read, so no helper program is started
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        d = json.loads(r.stdout)
-        for card in d.values():
-            for k, val in card.items():
-                if "sclk" in k.lower():
-                    info["sclk_after_run"] = val
-                    break
-            break
+        import glob
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        info["sclk_after_run"] = line.split(":", 1)[1].replace("*", "").strip()
+                        break
+            if "sclk_after_run" in info:
+                break
     except Exception:
         pass
     return info
@@ -438,7 +440,7 @@ def main():
                 "of_step_bytes": round(comp["compensator_bytes"] / comp["layer_bytes"], 4),
                 "of_resident_weights": run["resident_comp_share"]},
             "host_seconds_timed": run["host_s"],
-            "step_ms_p10_p50_p90": run["pcts"],
+            "step_ms_p10_p50_p90_event_pass": run["pcts"],
             "path": args.path,
             "compensator_factors": args.lr,
         },
@@ -479,8 +481,9 @@ def main():
 
 def run_workload(m, cfg, name, nsets, path, lr, steps, warmup):
     """Build nsets weight sets of a workload (one per layer for a stack),
-    warm up, time `steps` steps with HIP events on the library's stream, and
-    account the work."""
+    warm up, time `steps` steps with HIP events on the library's stream (only
+    the two bracketing the steps), run them once more with per-step and
+    per-kernel events, and account the work."""
     import torch
     import synth
     stack = cfg.layers > 1
@@ -509,20 +512,28 @@ def run_workload(m, cfg, name, nsets, path, lr, steps, warmup):
     for i in range(warmup):
         run_step(i)
     torch.cuda.synchronize()
-    evs = [(TIMER.event(), TIMER.event()) for _ in range(steps)]
-    marks = [TIMER.event() for _ in range(steps + 1)]   # step boundaries
+    # the timed region: the K steps and nothing else on the stream between its
+    # two events (an event between kernels costs about 2.5 us of its own)
     start, stop = TIMER.event(), TIMER.event()
     torch.cuda.synchronize()
     t_host = time.perf_counter()
     TIMER.record(start, stream)
-    TIMER.record(marks[0], stream)
     for i in range(steps):
-        run_step(i, evs[i])
-        TIMER.record(marks[i + 1], stream)
+        run_step(i)
     TIMER.record(stop, stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
     ms_step = TIMER.ms(start, stop) / steps
+    # kernel pass, after the timed region: the same K steps again with events
+    # at the step boundaries and around the gate/up GEMM call, for the
+    # per-launch duration of the roofline line and the spread of step times
+    evs = [(TIMER.event(), TIMER.event()) for _ in range(steps)]
+    marks = [TIMER.event() for _ in range(steps + 1)]
+    TIMER.record(marks[0], stream)
+    for i in range(steps):
+        run_step(i, evs[i])
+        TIMER.record(marks[i + 1], stream)
+    torch.cuda.synchronize()
     step_ms = sorted(TIMER.ms(marks[i], marks[i + 1]) for i in range(steps))
     pct = lambda q: step_ms[min(len(step_ms) - 1, int(q * (len(step_ms) - 1) + 0.5))]
     k13_us = sum(TIMER.ms(a, b) for a, b in evs) / len(evs) * 1000.0

@@ -168,6 +168,21 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
     // 0.205 ms per layer with both paths -> 0.198 ms)
     p->dec_mt = 0;
     p->pre_launch = 1;
+  } else if (rows_bound <= kDecodeChunkRows && P < 32 * d->num_experts &&
+             (int64_t)d->N * d->K > kSmallMatrixElems) {
+    // large matrices, experts averaging under 32 rows, none above
+    // kDecodeChunkRows: the small-M kernel alone, the few experts above 32
+    // rows in 32-row chunks (each chunk streams the expert's weights again),
+    // instead of a tile launch that mostly finds no expert (measured 4.6 us
+    // per empty launch at 64 tokens over 8 experts)
+    p->dec_mt = 2;
+    p->dec_chunked = 1;
+  } else if (P >= 64 * d->num_experts) {
+    // experts averaging 64 rows or more: the tile kernel for every expert
+    // (a small-M launch would find few experts or none; measured 4-5 us per
+    // empty launch at 4096 tokens over 8 experts)
+    p->dec_mt = 0;
+    p->pre_launch = 1;
   } else {
     // both paths: the small-M kernel takes experts of up to 32 rows (two
     // m-tiles), or for small matrices only those of up to 16 rows, the tile
@@ -202,7 +217,7 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
         ks = k;
       }
     }
-    p->dec_ksplit = ks;
+    p->dec_ksplit = p->dec_chunked ? 1 : ks;   // chunk entries have no split-K slot
     p->dec_blocks = items * ks < slots ? items * ks : slots;
   }
   p->lr_tiles = (P + 15) / 16 + d->num_experts;

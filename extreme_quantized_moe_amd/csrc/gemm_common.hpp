@@ -26,6 +26,7 @@ struct GemmArgs {
   int epilogue, ksplit, dec_max_rows, pre_min_rows;
   int m_lo, m_hi;          // row-count range of the experts a decode launch handles
   int poison_over;         // decode launch: NaN-fill the rows of experts above m_hi
+  int dec_chunk;           // decode launch: every expert with rows, in chunks of m_hi rows
   int x_bytes_32;          // x (rows x K fp16) spans under 4 GiB: 32-bit row offsets
 };
 

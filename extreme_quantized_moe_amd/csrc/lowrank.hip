@@ -729,7 +729,9 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
   a.max_rank = d->max_rank;
   a.aux_y = aux_blocks ? rank_blocks : -1;
   a.aux_parts = 1;
-  a.dec_max_rows = p.dec_max_rows;
+  // rows gathered for the small-M kernel: its own experts, or every expert
+  // when it takes them all (no tile launch, chunks)
+  a.dec_max_rows = (!p.pre_launch && p.dec_ksplit == 1) ? 0x7FFFFFFF : p.dec_max_rows;
   a.tpart = nullptr;
   a.ks_steps = d->K / 32;
   a.num_pairs = d->num_pairs;

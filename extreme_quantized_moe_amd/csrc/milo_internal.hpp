@@ -24,6 +24,7 @@ constexpr int kTileSzWords = 128;  // 64 rows x 2 groups
 constexpr int kGroup = 64;
 constexpr int kMaxRank = 64;
 constexpr int kDecodeMaxRows = 32;  // largest expert row count of the small-M path
+constexpr int kDecodeChunkRows = 128; // largest row bound of a chunked small-M plan
 constexpr int64_t kSmallMatrixElems = (int64_t)1 << 22;  // N x K at most: mid-sized experts take the tile kernel
 constexpr int kPrepassTileRows = 128;  // rows per block of the fp16 prefill pre-pass for large experts
 constexpr int kPrepassBlocks = 512; // the fp16 prefill pre-pass splits K until its grid has about this many blocks
@@ -267,6 +268,7 @@ struct GemmPlan {
   int pre_tiles;     // grid.y bound of the tile kernel (row tiles)
   int pre_bm;        // rows per block of the tile kernel (64 or 128)
   int pre_slots;     // persistent grid of the 64-row tile kernel (two blocks per compute unit)
+  int dec_chunked;   // planned as small-M only with experts above 32 rows in chunks
   // workspace carve-up (byte offsets)
   size_t off_t, off_xg, off_pw, off_dec_part, off_tpart, total;
 };

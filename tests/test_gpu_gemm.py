@@ -338,22 +338,40 @@ def test_fp16_factors_beyond_rank_are_never_read(path):
 
 
 @pytest.mark.parametrize("epi", ["swiglu", "route"])
-def test_row_bound_too_small_poisons_rows(epi):
-    """A caller bound below the real rows per expert: the automatic plan is
-    the small-M kernel alone (it takes up to 16 rows per expert here), so the
-    rows of heavier experts have no kernel -- they must come back as NaN, not
-    as whatever the output held, while every other row is correct."""
+def test_row_bound_too_small_chunks_rows(epi):
+    """A caller bound below the real rows per expert, small-M plan without
+    split K: the kernel takes the heavier experts in 16-row chunks, so every
+    row is still correct."""
     m = _m()
     E, N, K, T, k = 4, 128, 256, 40, 2
     e_epi = m.EPI_SWIGLU if epi == "swiglu" else m.EPI_ROUTE_SCALE
     got, want = _moe_case(E, 0, N, K, [16] * E, T, k, e_epi, PATHS["auto"], 91, skew=0, max_rows=8, fill=0.0)
     ref_r = oracle.route_ref(_route(T, E, k, 0, 91, 0).numpy(), k, 0, True)
+    rows = np.diff(ref_r["offsets"])
+    assert rows.max() > 32 and rows.min() <= 16, rows    # one, two and three chunks
+    assert_close(got, want, f"row bound 8, experts of {rows.tolist()} rows, {epi}")
+
+
+@pytest.mark.parametrize("epi", ["swiglu", "route"])
+def test_row_bound_too_small_poisons_rows(epi):
+    """A caller bound below the real rows per expert with a split-K small-M
+    plan (long K, few items; its partial sums are kept per expert, so it does
+    not chunk): the rows of the experts above its 16 rows have no kernel and
+    must come back as NaN, not as whatever the output held, while every other
+    row is correct."""
+    m = _m()
+    E, N, K, T, k = 3, 128, 4096, 40, 1
+    e_epi = m.EPI_SWIGLU if epi == "swiglu" else m.EPI_ROUTE_SCALE
+    counts = [25, 9, 6]
+    got, want = _moe_case(E, 0, N, K, [16] * E, T, k, e_epi, PATHS["auto"], 92, max_rows=8, fill=0.0,
+                          logits=_counts_logits(counts, E))
+    ref_r = oracle.route_ref(_counts_logits(counts, E).numpy(), k, 0, True)
     off, sp = ref_r["offsets"], ref_r["sorted_pairs"]
     rows = np.diff(off)
-    assert rows.max() > 16 and rows.min() <= 16, rows
+    assert rows.tolist() == counts, rows
     for e in range(E):
         idx = sp[off[e]:off[e + 1]] if e_epi == m.EPI_ROUTE_SCALE else np.arange(off[e], off[e + 1])
         if rows[e] > 16:
             assert np.all(np.isnan(got[idx])), f"expert {e} ({rows[e]} rows): rows not poisoned"
-        elif rows[e]:
+        else:
             assert_close(got[idx], want[idx], f"expert {e} ({rows[e]} rows) next to a poisoned expert")
