@@ -160,8 +160,11 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
   } else if (d->path == MILO_PATH_PREFILL) {
     p->dec_mt = 0;
     p->pre_launch = 1;
-  } else if (rows_bound <= kDecodeMaxRows) {
+  } else if (rows_bound <= kDecodeMaxRows && !(rows_bound > 16 && (int64_t)d->N * d->K > kSmallMatrixElems)) {
     p->dec_mt = mt_for(rows_bound);
+  } else if (rows_bound <= kDecodeMaxRows) {
+    p->dec_mt = 1;
+    p->dec_chunked = 1;
   } else if ((int64_t)d->N * d->K <= kSmallMatrixElems && P >= 16 * d->num_experts) {
     // small matrices, experts averaging 16 rows or more: the tile kernel for
     // every expert (measured: 1408 x 2048 experts, 31 rows on average,
@@ -175,7 +178,7 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
     // rows in 32-row chunks (each chunk streams the expert's weights again),
     // instead of a tile launch that mostly finds no expert (measured 4.6 us
     // per empty launch at 64 tokens over 8 experts)
-    p->dec_mt = 2;
+    p->dec_mt = 1;
     p->dec_chunked = 1;
   } else if (P >= 64 * d->num_experts) {
     // experts averaging 64 rows or more: the tile kernel for every expert

@@ -30,6 +30,11 @@ struct GemmArgs {
   int x_bytes_32;          // x (rows x K fp16) spans under 4 GiB: 32-bit row offsets
 };
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; a field at its maximum does not wait)
+constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
+
 struct GemmPlan;
 GemmArgs make_gemm_args(const milo_gemm_desc* d, const GemmPlan& p, char* ws);
 

@@ -471,10 +471,6 @@ __device__ __forceinline__ void dma4(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)l, 4, 0, 0);
 }
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8; a field at its maximum does not wait)
-constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
-constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
 template <int NW, bool LRQ, int NMT, bool X32>
 __device__ __forceinline__ void tile_body_lds(const GemmArgs& a, const RowTile& rt, uint16_t* lds,
