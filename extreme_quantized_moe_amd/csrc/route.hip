@@ -35,9 +35,9 @@ __device__ __forceinline__ int slot_expert(const int32_t* ids_row, int j, int k,
 // pass j picks the largest logit (lowest id on ties) among the experts not
 // picked before; also the row maximum and the softmax denominator.  The row
 // is held in registers (NE >= E; all loads issued at once).
-template <int NE>
-__device__ __forceinline__ void topk_regs(const float* row, int E, int k, float (&bv)[kMaxK],
-                                          int (&bi)[kMaxK], float& mx, float& den) {
+template <int NE, int MK>
+__device__ __forceinline__ void topk_regs(const float* row, int E, int k, float (&bv)[MK],
+                                          int (&bi)[MK], float& mx, float& den) {
   float v[NE];
   if (E == NE && ((uintptr_t)row & 15) == 0) {
     // whole 16-byte vectors: a quarter of the cache-line requests of scalar
@@ -57,7 +57,7 @@ __device__ __forceinline__ void topk_regs(const float* row, int E, int k, float 
     if (e < E) mx = fmaxf(mx, v[e]);
   uint64_t taken = 0;
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
+  for (int j = 0; j < MK; ++j) {
     bv[j] = -INFINITY;
     bi[j] = -1;
     if (j < k) {
@@ -90,9 +90,9 @@ __device__ __forceinline__ void topk_regs(const float* row, int E, int k, float 
 // four (larger value, then lower id), the winner dropping its head.  The
 // softmax denominator: each thread's sum of exp(v - max) over its experts,
 // then (with four) the partial sums as (t0 + t1) + (t2 + t3).
-template <int LANES, int NL>
-__device__ __forceinline__ void topk_lanes(const float* row, int E, int k, int q, float (&bv)[kMaxK],
-                                           int (&bi)[kMaxK], float& den) {
+template <int LANES, int NL, int MK>
+__device__ __forceinline__ void topk_lanes(const float* row, int E, int k, int q, float (&bv)[MK],
+                                           int (&bi)[MK], float& den) {
   float v[NL];
   const int e0 = q * NL;
   if (E == LANES * NL && NL % 4 == 0 && ((uintptr_t)row & 15) == 0) {
@@ -106,11 +106,11 @@ __device__ __forceinline__ void topk_lanes(const float* row, int E, int k, int q
     for (int e = 0; e < NL; ++e) v[e] = e0 + e < E ? row[e0 + e] : -INFINITY;
   }
   // own list, best first; entries past the own experts are (-inf, E + 1)
-  float lv[kMaxK];
-  int li[kMaxK];
+  float lv[MK];
+  int li[MK];
   uint64_t taken = 0;
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
+  for (int j = 0; j < MK; ++j) {
     lv[j] = -INFINITY;
     li[j] = E + 1;
     if (j < k) {
@@ -133,14 +133,14 @@ __device__ __forceinline__ void topk_lanes(const float* row, int E, int k, int q
   }
   if constexpr (LANES == 1) {
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
+    for (int j = 0; j < MK; ++j) {
       bv[j] = j < k ? lv[j] : -INFINITY;
       bi[j] = j < k ? li[j] : -1;
     }
   }
   // merge the four lists
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
+  for (int j = 0; j < MK; ++j) {
     if (LANES == 1) break;
     bv[j] = -INFINITY;
     bi[j] = -1;
@@ -160,13 +160,13 @@ __device__ __forceinline__ void topk_lanes(const float* row, int E, int k, int q
       bi[j] = ci;
       const bool mine = li[0] == ci;
 #pragma unroll
-      for (int u = 0; u + 1 < kMaxK; ++u) {
+      for (int u = 0; u + 1 < MK; ++u) {
         lv[u] = mine ? lv[u + 1] : lv[u];
         li[u] = mine ? li[u + 1] : li[u];
       }
       if (mine) {
-        lv[kMaxK - 1] = -INFINITY;
-        li[kMaxK - 1] = E + 1;
+        lv[MK - 1] = -INFINITY;
+        li[MK - 1] = E + 1;
       }
     }
   }
@@ -200,10 +200,12 @@ __device__ int block_exclusive_scan(int v, int* lds, int* total) {
 }
 
 // NV: experts per token row this instantiation handles (LANES = 1: 8 or 16
-// in registers; LANES = 4: 32, 64, 128 or 256, a quarter per thread); one
-// width per kernel keeps each kernel's code small (a single block runs it
-// cold from the instruction cache).
-template <int LANES, int NV>
+// in registers; LANES = 4: 32, 64, 128 or 256, a quarter per thread); MK and
+// MS bound k and the slots per token (k + shared).  One width and bound per
+// kernel keeps each kernel's code small: a single block runs it cold from the
+// instruction cache, and the fully unrolled slot loops are most of the code
+// (top-2 over 8 experts: 2655 instructions with bounds 8 / 16).
+template <int LANES, int NV, int MK, int MS>
 __global__ void __launch_bounds__(LANES * kRouteBlock)
 route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int renorm,
            int32_t* __restrict__ ids, float* __restrict__ topw, float* __restrict__ slot_w,
@@ -220,10 +222,10 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
 
   // per-thread arrays are indexed only by unrolled loop counters (registers);
   // slot j of a token is handled by its thread j % LANES
-  int my_ids[kMaxSlots];
-  int rank[kMaxSlots];
+  int my_ids[MS];
+  int rank[MS];
 #pragma unroll
-  for (int j = 0; j < kMaxSlots; ++j) {
+  for (int j = 0; j < MS; ++j) {
     my_ids[j] = 0;
     rank[j] = 0;
   }
@@ -232,22 +234,22 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
     // the LANES threads of a token are all live or all not, so the shuffles
     // inside topk_lanes only read live threads
     const float* row = logits + (size_t)t * E;
-    float bv[kMaxK];
-    int bi[kMaxK];
+    float bv[MK];
+    int bi[MK];
     float den;
     float mx1 = 0.f;
-    if constexpr (LANES == 1) topk_regs<NV>(row, E, k, bv, bi, mx1, den);
-    else topk_lanes<4, NV / 4>(row, E, k, q, bv, bi, den);
+    if constexpr (LANES == 1) topk_regs<NV, MK>(row, E, k, bv, bi, mx1, den);
+    else topk_lanes<4, NV / 4, MK>(row, E, k, q, bv, bi, den);
     const float mx = bv[0];
-    float sel[kMaxK];
+    float sel[MK];
     float selsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
+    for (int j = 0; j < MK; ++j) {
       sel[j] = j < k ? expf(bv[j] - mx) : 0.f;
       selsum += sel[j];
     }
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
+    for (int j = 0; j < MK; ++j) {
       if (j < k) {
         my_ids[j] = bi[j];
         if (j % LANES == q) {
@@ -259,14 +261,14 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
       }
     }
 #pragma unroll
-    for (int j = 0; j < kMaxSlots; ++j) {
+    for (int j = 0; j < MS; ++j) {
       if (j >= k && j < slots) {
         my_ids[j] = E + (j - k);
         if (j % LANES == q) slot_w[(size_t)t * slots + j] = 1.0f;
       }
     }
 #pragma unroll
-    for (int j = 0; j < kMaxSlots; ++j)
+    for (int j = 0; j < MS; ++j)
       if (j < slots && j % LANES == q) atomicOr(&bits[my_ids[j]][tl >> 5], 1u << (tl & 31));
   }
   __syncthreads();
@@ -274,7 +276,7 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
   // stable rank of each slot among earlier tokens of this block with the same expert
   if (live) {
 #pragma unroll
-    for (int j = 0; j < kMaxSlots; ++j) {
+    for (int j = 0; j < MS; ++j) {
       if (j < slots && j % LANES == q) {
         const uint32_t* brow = bits[my_ids[j]];
         int c = 0;
@@ -341,7 +343,7 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
     }
     if (live) {
 #pragma unroll
-      for (int j = 0; j < kMaxSlots; ++j) {
+      for (int j = 0; j < MS; ++j) {
         if (j < slots && j % LANES == q) {
           const int s = t * slots + j;
           const int pos = scan_lds[my_ids[j]] + rank[j];
@@ -354,7 +356,7 @@ route_topk(const float* __restrict__ logits, int T, int E, int k, int S, int ren
     if (tid < ET) block_counts[(size_t)blockIdx.x * ET + tid] = count;
     if (live) {
 #pragma unroll
-      for (int j = 0; j < kMaxSlots; ++j)
+      for (int j = 0; j < MS; ++j)
         if (j < slots && j % LANES == q) pair_pos[t * slots + j] = rank[j];
     }
   }
@@ -576,15 +578,18 @@ int32_t launch_route(const float* logits, int T, int E, int k, int S, int renorm
     return hip_status(hipGetLastError(), "route_sort_block launch");
   }
   // one thread per token up to 16 experts, four above (shorter selection chains)
-#define MILO_ROUTE_LAUNCH(L, NV)                                                                             \
-  hipLaunchKernelGGL((route_topk<L, NV>), dim3(nblocks), dim3(L * kRouteBlock), 0, st, logits, T, E, k, S, \
+#define MILO_ROUTE_LAUNCH(L, NV, MK, MS)                                                                             \
+  hipLaunchKernelGGL((route_topk<L, NV, MK, MS>), dim3(nblocks), dim3(L * kRouteBlock), 0, st, logits, T, E, k, S, \
                      renorm, ids, w, slot_w, sorted_pairs, pair_pos, offsets, counts)
-  if (E <= 8) MILO_ROUTE_LAUNCH(1, 8);
-  else if (E <= 16) MILO_ROUTE_LAUNCH(1, 16);
-  else if (E <= 32) MILO_ROUTE_LAUNCH(4, 32);
-  else if (E <= 64) MILO_ROUTE_LAUNCH(4, 64);
-  else if (E <= 128) MILO_ROUTE_LAUNCH(4, 128);
-  else MILO_ROUTE_LAUNCH(4, 256);
+  const bool narrow = k <= 2 && k + S <= 4;   // top-1/top-2 with few shared experts
+  if (E <= 8 && narrow) MILO_ROUTE_LAUNCH(1, 8, 2, 4);
+  else if (E <= 8) MILO_ROUTE_LAUNCH(1, 8, kMaxK, kMaxSlots);
+  else if (E <= 16 && narrow) MILO_ROUTE_LAUNCH(1, 16, 2, 4);
+  else if (E <= 16) MILO_ROUTE_LAUNCH(1, 16, kMaxK, kMaxSlots);
+  else if (E <= 32) MILO_ROUTE_LAUNCH(4, 32, kMaxK, kMaxSlots);
+  else if (E <= 64) MILO_ROUTE_LAUNCH(4, 64, kMaxK, kMaxSlots);
+  else if (E <= 128) MILO_ROUTE_LAUNCH(4, 128, kMaxK, kMaxSlots);
+  else MILO_ROUTE_LAUNCH(4, 256, kMaxK, kMaxSlots);
 #undef MILO_ROUTE_LAUNCH
   int32_t rc = hip_status(hipGetLastError(), "route_topk launch");
   if (rc != MILO_OK || nblocks == 1) return rc;
