@@ -590,14 +590,20 @@ def run_workload(m, cfg, name, nsets, path, lr, steps, warmup):
     pairs = cfg.T * (cfg.k + cfg.S)
     ET = cfg.E + cfg.S
     # the kernels the library's automatic path launches for the gate/up call
-    if prefill:
-        kname = "gemm_prefill_kernel<2,...,128> (gate/up + SwiGLU)"
-    elif cfg.T <= 32 or path == 1:
+    # (the host plan's rules, with the row bound the bench passes: T)
+    small = cfg.F * cfg.H <= (1 << 22)
+    if path == 1 or (path == 0 and (cfg.T <= 16 or (cfg.T <= 32 and not small))):
         kname = "gemm_decode_kernel<MT,2> (gate/up + SwiGLU)"
-    elif path == 2 or (cfg.F * cfg.H <= (1 << 22) and pairs >= 16 * ET):
-        kname = "gate/up call: gemm_prefill_kernel<2,...> (tile kernel for every expert)"
+    elif path == 0 and cfg.T <= 32:
+        kname = "gemm_decode_kernel<2,2> (gate/up + SwiGLU, two m-tiles)"
+    elif path == 0 and not small and cfg.T <= 128 and pairs < 32 * ET:
+        kname = "gemm_decode_kernel<1,2> (gate/up + SwiGLU, experts above 16 rows in chunks)"
+    elif prefill and (path == 2 or pairs >= 256 * ET):
+        kname = "gemm_prefill_kernel<2,...,128> (gate/up + SwiGLU)"
+    elif path == 2 or (small and pairs >= 16 * ET) or pairs >= 64 * ET:
+        kname = "gate/up call: 64-row tile kernel for every expert (gemm_prefill_persistent<2,...>)"
     else:
-        kname = "gate/up call: gemm_decode_kernel<MT,2> + gemm_prefill_kernel<2,...> (both paths)"
+        kname = "gate/up call: gemm_decode_kernel<MT,2> + gemm_prefill_persistent<2,...> (both paths)"
     k_bytes, k_flops = comp["bytes13"], comp["flops13"]
     if prefill:
         achieved = k_flops / (k13_us * 1e-6) / 1e12
