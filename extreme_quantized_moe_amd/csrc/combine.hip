@@ -7,22 +7,25 @@
 
 namespace milo {
 
+// MS bounds the slots per token (the slot loop is unrolled to it: the kernel
+// runs cold from the instruction cache, so top-2 routing gets a short one);
+// the element index is 32-bit (the launcher checks that T * H / 4 fits).
+template <int MS>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ y, int T, int slots,
                                                       int H, uint16_t* __restrict__ out) {
   const int hq = H >> 2;
-  const int64_t total = (int64_t)T * hq;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = i / hq;
-    const int h4 = (int)(i - t * hq);
+  const int total = T * hq;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const int t = i / hq;
+    const int h4 = i - t * hq;
     const float4* src = (const float4*)(y + (size_t)t * slots * H) + h4;
-    float4 v[16];                         // all slot loads issued before the sum
+    float4 v[MS];                         // all slot loads issued before the sum
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < MS; ++j)
       if (j < slots) v[j] = src[(size_t)j * hq];
     float4 acc = v[0];
 #pragma unroll
-    for (int j = 1; j < 16; ++j)
+    for (int j = 1; j < MS; ++j)
       if (j < slots) {
         acc.x += v[j].x; acc.y += v[j].y; acc.z += v[j].z; acc.w += v[j].w;
       }
@@ -35,9 +38,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 
 int32_t launch_combine(const float* y, int T, int slots, int H, uint16_t* out, hipStream_t st) {
   const int64_t work = (int64_t)T * (H / 4);
+  if (work > 0x7F000000) {   // headroom for the grid-stride step
+    set_error("T * H / 4 = %lld elements exceed the combine kernel's 32-bit index", (long long)work);
+    return MILO_ERR_SHAPE;
+  }
   int64_t g = (work + 255) / 256;
   if (g > 16384) g = 16384;
-  hipLaunchKernelGGL(combine_kernel, dim3((int)g), dim3(256), 0, st, y, T, slots, H, out);
+  if (slots <= 4) hipLaunchKernelGGL(combine_kernel<4>, dim3((int)g), dim3(256), 0, st, y, T, slots, H, out);
+  else hipLaunchKernelGGL(combine_kernel<16>, dim3((int)g), dim3(256), 0, st, y, T, slots, H, out);
   return hip_status(hipGetLastError(), "combine_kernel launch");
 }
 

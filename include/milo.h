@@ -490,7 +490,8 @@ int32_t milo_moe_w3a16_lowrank_gemm_static(const milo_gemm_desc* desc, void* str
  * holds the route-weighted slot outputs (MILO_EPI_ROUTE_SCALE).
  * [talk] Background: a token's output is the combination of the outputs of
  * the experts it activates.
- * y   : float32 [T*slots][H];  out : fp16 [T][H].  H % 4 == 0, 16-byte aligned.
+ * y   : float32 [T*slots][H];  out : fp16 [T][H].  H % 4 == 0, 16-byte aligned;
+ * 1 <= slots <= 16; T * H / 4 at most 0x7F000000 (MILO_ERR_SHAPE otherwise).
  */
 int32_t milo_moe_combine(const float* y, int32_t T, int32_t slots, int32_t H,
                          uint16_t* out, void* stream);
