@@ -187,6 +187,7 @@ def test_combine_rejects(L):
     assert lib.milo_moe_combine(f, 4, 2, 66, f, None) == 2
     assert lib.milo_moe_combine(f, 4, 0, 64, f, None) == 2
     assert lib.milo_moe_combine(C.c_void_p(0x1004), 4, 2, 64, f, None) == 3
+    assert lib.milo_moe_combine(f, 1 << 29, 2, 64, f, None) == 2   # T * H / 4 past the 32-bit index
 
 
 def test_lowrank_and_build_reject_before_launch(L):
