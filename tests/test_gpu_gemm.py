@@ -337,6 +337,19 @@ def test_fp16_factors_beyond_rank_are_never_read(path):
     assert torch.equal(clean, dirty)
 
 
+@pytest.mark.parametrize("T,epi", [(24, "swiglu"), (40, "route")])
+def test_large_matrices_chunked_small_m_plan(T, epi):
+    """Large matrices (N K > 2^22) with a row bound of 17..128 and experts
+    averaging under 32 rows: the automatic plan runs the one-m-tile small-M
+    kernel alone and takes experts above 16 rows in 16-row chunks (no tile
+    launch)."""
+    m = _m()
+    epilogue = {"swiglu": m.EPI_SWIGLU, "route": m.EPI_ROUTE_SCALE}[epi]
+    got, want = _moe_case(E=4, S=0, N=1088, K=4096, ranks=[16, 64, 0, 40], T=T, k=2, epilogue=epilogue,
+                          path=PATHS["auto"], seed=500 + T, skew=1)
+    assert_close(got, want, f"chunked small-M plan T={T} {epi}")
+
+
 @pytest.mark.parametrize("epi", ["swiglu", "route"])
 def test_row_bound_too_small_chunks_rows(epi):
     """A caller bound below the real rows per expert, small-M plan without
