@@ -46,6 +46,16 @@ def test_route_ties(T):
     _check(logits, 3, 1, True)
 
 
+@pytest.mark.parametrize("T,E,k,S", [(64, 8, 2, 2), (200, 16, 2, 1), (256, 5, 1, 3), (300, 16, 2, 2)])
+def test_route_ties_top2_kernel(T, E, k, S):
+    """Top-1/top-2 routing with up to four slots per token runs on the router
+    instantiation unrolled for two picks and four slots (one and several
+    token blocks); integer logits make ties common."""
+    g = torch.Generator().manual_seed(T * 3 + E + S)
+    logits = torch.randint(-2, 3, (T, E), generator=g).float()
+    _check(logits, k, S, True)
+
+
 @pytest.mark.parametrize("T,E,k,S", [(256, 64, 6, 2), (100, 32, 4, 0)])
 def test_route_ties_four_lanes(T, E, k, S):
     """More than 16 experts: four threads per token, each with its own top-k
