@@ -49,7 +49,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
     ap.add_argument("--batch", type=int, default=None, help="tokens (C5 sweep: 1/8/32/64)")
-    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--copies", type=int, default=8,
+                    help="weight sets rotated per step (8 x 650 MB at C2: neither the codes nor "
+                         "the compensator factors of all sets fit the 256 MB last-level cache)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-prefill", action="store_true",
@@ -57,6 +59,9 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-check-tokens", type=int, default=2)
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="run the workload's steps for this long before the warm-up, so the card "
+                         "is at its sustained clock when the timed steps start")
     ap.add_argument("--graph", action="store_true",
                     help="replay one captured HIP graph per step in the timed region instead of "
                          "launching every call from Python (measured slower on this stack: C2 "
@@ -413,6 +418,7 @@ def main():
     global TIMER
     TIMER = HipTimer()
     GRAPH[0] = args.graph
+    SETTLE_S[0] = args.settle_ms / 1000.0
     run = run_workload(m, cfg, args.config, cfg.layers if cfg.layers > 1 else args.copies, path, args.lr,
                        args.steps, args.warmup)
     ms_step = run["ms_step"]
@@ -445,6 +451,7 @@ def main():
                 "of_step_bytes": round(comp["compensator_bytes"] / comp["layer_bytes"], 4),
                 "of_resident_weights": run["resident_comp_share"]},
             "host_seconds_timed": run["host_s"],
+            "settle": {"ms": args.settle_ms, "steps": run["settle_steps"]},
             "launch": run["launch"],
             "step_ms_p10_p50_p90_event_pass": run["pcts"],
             "path": args.path,
@@ -486,6 +493,7 @@ def main():
 
 
 GRAPH = [False]   # --graph: replay one captured HIP graph per step in the timed region
+SETTLE_S = [0.25]  # --settle-ms: wall time of steps run before the warm-up
 
 
 def run_workload(m, cfg, name, nsets, path, lr, steps, warmup):
@@ -518,6 +526,19 @@ def run_workload(m, cfg, name, nsets, path, lr, steps, warmup):
         else:
             layers[i % nsets].step(stream, ev)
 
+    # Settle: run the workload's own steps for SETTLE_S seconds of wall time
+    # before the warm-up.  The card raises its clocks only under sustained
+    # load: measured on C2, the first 50 steps after 10 warm-up steps ran at
+    # 0.158 ms, after 0.2 s idle at 0.173 ms, and from about 60 ms of load on
+    # at 0.143 ms; timing a cold card would report its power ramp, not the
+    # kernels.  Not part of the K timed steps.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_S[0]:
+        for _ in range(8):
+            run_step(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
     for i in range(warmup):
         run_step(i)
     torch.cuda.synchronize()
@@ -616,7 +637,7 @@ def run_workload(m, cfg, name, nsets, path, lr, steps, warmup):
     roof.update({"kernel": kname, "alg_bytes_per_launch": int(k_bytes), "alg_flops_per_launch": int(k_flops),
                  "avg_launch_us": round(k13_us, 2)})
     return {"ms_step": ms_step, "pcts": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
-            "host_s": round(t_host, 3), "roofline": roof,
+            "host_s": round(t_host, 3), "roofline": roof, "settle_steps": settle_steps,
             "launch": ("one captured HIP graph per step, replayed" if graphs else "eager calls from Python"), "work": comp, "touched": works[0]["touched"],
             "nsets": nsets, "layers": layers, "resident_comp_share": resident_comp}
 
