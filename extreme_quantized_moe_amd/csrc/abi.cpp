@@ -174,10 +174,13 @@ int32_t plan_gemm(const milo_gemm_desc* d, GemmPlan* p) {
   } else if (rows_bound <= kDecodeChunkRows && P < 32 * d->num_experts &&
              (int64_t)d->N * d->K > kSmallMatrixElems) {
     // large matrices, experts averaging under 32 rows, none above
-    // kDecodeChunkRows: the small-M kernel alone, the few experts above 32
-    // rows in 32-row chunks (each chunk streams the expert's weights again),
-    // instead of a tile launch that mostly finds no expert (measured 4.6 us
-    // per empty launch at 64 tokens over 8 experts)
+    // kDecodeChunkRows: the small-M kernel alone, experts above its rows in
+    // chunks (each chunk streams the expert's weights again), instead of a
+    // tile launch that mostly finds no expert (measured 4.6 us per empty
+    // launch at 64 tokens over 8 experts).  16-row chunks on the one-m-tile
+    // kernel: at 64 tokens over 8 experts (8..27 rows) as fast as 32-row
+    // chunks on the two-m-tile gate/up kernel (gate/up 122 vs 124 us), which
+    // reads the weights once but does twice the arithmetic per weight
     p->dec_mt = 1;
     p->dec_chunked = 1;
   } else if (P >= 64 * d->num_experts) {

@@ -46,11 +46,11 @@ namespace milo {
 
 constexpr int kMaxE = 256;
 
-template <int NW>
+template <int WF, int WMT>
 struct Stage {
-  u32x4 q[NW][3];    // three planes of the 64 x 128 code tile
-  u32x4 z[NW][2];    // eight scale/zero words of this lane's rows
-  f16x8 x[4];        // activation fragments of the four 32-wide K steps
+  u32x4 q[WF][3];    // three planes of the 64 x 128 code tile, per family of the wave
+  u32x4 z[WF][2];    // eight scale/zero words of this lane's rows
+  f16x8 x[WMT][4];   // activation fragments of the four 32-wide K steps, per m-tile of the wave
 };
 
 struct Item {
@@ -97,18 +97,26 @@ __device__ void poison_over_rows(const GemmArgs& a, const DecShared& sh) {
 }
 
 
-template <int MP, int NW, int EPI>
+// Wave split of an item.  Default (FS = false): wave w takes m-tile w / KW
+// and every KW-th K block from w % KW (KW = 4 / MP), with every weight family.
+// Family split (FS = true, two m-tiles and two families): wave w takes family
+// w % 2 and every second K block from w / 2, with both m-tiles, so each code
+// is extracted once per item instead of once per m-tile.
+template <int MP, int NW, int EPI, bool FS>
 struct Dec {
-  static constexpr int KW = 4 / MP;   // waves per m-tile (they split the K blocks)
+  static constexpr int KW = FS ? 2 : 4 / MP;   // waves that split the K blocks of one output set
+  static constexpr int WF = FS ? 1 : NW;       // weight families per wave
+  static constexpr int WMT = FS ? MP : 1;      // m-tiles per wave
   const GemmArgs& a;
   const DecShared& sh;
-  int lane, wave, kw, mtile, total;
+  int lane, wave, kw, mtile, fam, total;
   CodeConsts kc;
 
   __device__ __forceinline__ Dec(const GemmArgs& a_, const DecShared& sh_, int total_)
       : a(a_), sh(sh_), lane(threadIdx.x & 63), wave(threadIdx.x >> 6),
-        kw(__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) % KW)),
-        mtile(__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) / KW)), total(total_),
+        kw(__builtin_amdgcn_readfirstlane(FS ? (threadIdx.x >> 6) / 2 : (threadIdx.x >> 6) % KW)),
+        mtile(__builtin_amdgcn_readfirstlane(FS ? 0 : (threadIdx.x >> 6) / KW)),
+        fam(__builtin_amdgcn_readfirstlane(FS ? (threadIdx.x >> 6) % 2 : 0)), total(total_),
         kc(make_code_consts()) {}
 
   __device__ __forceinline__ void enter(Cursor& c, int it) const {
@@ -144,49 +152,55 @@ struct Dec {
   // A wave whose first K block lies past the item's range (K splits of fewer
   // than four blocks) gets one null element: real codes of the item's first
   // block with zero activations, which adds exactly zero.
-  __device__ __forceinline__ void load(Stage<NW>& S, const Cursor& c) const {
+  __device__ __forceinline__ void load(Stage<WF, WMT>& S, const Cursor& c) const {
     const Item& m = c.item;
     const bool live = c.kb < m.kbB;
     const int kb = live ? c.kb : m.kbA;
 #pragma unroll
-    for (int f = 0; f < NW; ++f) {
+    for (int fl = 0; fl < WF; ++fl) {
+      const int f = FS ? fam : fl;
       const uint32_t* tp = a.packed[f] + m.e * a.words_per_expert +
                            ((size_t)m.nt * a.kblocks + kb) * kTileWords + 4 * lane;
       // codes are read once per launch: non-temporal loads (measured: C2
       // gate/up 85.2 -> 83.7 us)
-      S.q[f][0] = __builtin_nontemporal_load((const u32x4*)(tp));
-      S.q[f][1] = __builtin_nontemporal_load((const u32x4*)(tp + 256));
-      S.q[f][2] = __builtin_nontemporal_load((const u32x4*)(tp + 512));
+      S.q[fl][0] = __builtin_nontemporal_load((const u32x4*)(tp));
+      S.q[fl][1] = __builtin_nontemporal_load((const u32x4*)(tp + 256));
+      S.q[fl][2] = __builtin_nontemporal_load((const u32x4*)(tp + 512));
       const uint32_t* sp = a.sz[f] + m.e * a.sz_per_expert +
                            ((size_t)m.nt * a.kblocks + kb) * kTileSzWords + 8 * (lane & 15);
-      S.z[f][0] = *(const u32x4*)(sp);
-      S.z[f][1] = *(const u32x4*)(sp + 4);
+      S.z[fl][0] = *(const u32x4*)(sp);
+      S.z[fl][1] = *(const u32x4*)(sp + 4);
     }
-    const int row = mtile * 16 + (lane & 15);
-    const bool ok = live && row < m.M;
-    const uint16_t* xp =
-        a.x + (size_t)(m.base + (row < m.M ? row : 0)) * a.K + (size_t)kb * kTileK + 8 * (lane >> 4);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f16x8 v = *(const f16x8*)(xp + 32 * s);
-      S.x[s] = ok ? v : f16x8{};
+    for (int mt = 0; mt < WMT; ++mt) {
+      const int row = (mtile + mt) * 16 + (lane & 15);
+      const bool ok = live && row < m.M;
+      const uint16_t* xp =
+          a.x + (size_t)(m.base + (row < m.M ? row : 0)) * a.K + (size_t)kb * kTileK + 8 * (lane >> 4);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 v = *(const f16x8*)(xp + 32 * s);
+        S.x[mt][s] = ok ? v : f16x8{};
+      }
     }
   }
 
-  __device__ __forceinline__ void consume(const Stage<NW>& S, f32x4 (&acc)[NW][4]) const {
+  __device__ __forceinline__ void consume(const Stage<WF, WMT>& S, f32x4 (&acc)[WF][WMT][4]) const {
     const f16x8 one = ones_frag();
     // activation sums per group: xs = sum x, xo = sum x * off (rows of this lane)
-    f32x4 xs[2], xo[2];
+    f32x4 xs[WMT][2], xo[WMT][2];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      xs[g] = mfma16x16x32(S.x[2 * g], one, zero);
-      xs[g] = mfma16x16x32(S.x[2 * g + 1], one, xs[g]);
-      xo[g] = mfma16x16x32(S.x[2 * g], offset_frag(2 * g), zero);
-      xo[g] = mfma16x16x32(S.x[2 * g + 1], offset_frag(2 * g + 1), xo[g]);
-    }
+    for (int mt = 0; mt < WMT; ++mt)
 #pragma unroll
-    for (int f = 0; f < NW; ++f)
+      for (int g = 0; g < 2; ++g) {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        xs[mt][g] = mfma16x16x32(S.x[mt][2 * g], one, zero);
+        xs[mt][g] = mfma16x16x32(S.x[mt][2 * g + 1], one, xs[mt][g]);
+        xo[mt][g] = mfma16x16x32(S.x[mt][2 * g], offset_frag(2 * g), zero);
+        xo[mt][g] = mfma16x16x32(S.x[mt][2 * g + 1], offset_frag(2 * g + 1), xo[mt][g]);
+      }
+#pragma unroll
+    for (int f = 0; f < WF; ++f)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t h[16];
@@ -197,17 +211,20 @@ struct Dec {
           const uint32_t w = idx < 4 ? S.z[f][0][idx] : S.z[f][1][idx - 4];
           const float sc = half_bits_to_float(w & 0xFFFFu);
           const float zp = half_bits_to_float(w >> 16);
-          f32x4 p;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) p[r] = __builtin_fmaf(-zp, xs[g][r], -xo[g][r]);
+          for (int mt = 0; mt < WMT; ++mt) {
+            f32x4 p;
 #pragma unroll
-          for (int ss = 0; ss < 2; ++ss) {
-            const int step = 2 * g + ss;
-            const u32x4 u = {h[4 * step], h[4 * step + 1], h[4 * step + 2], h[4 * step + 3]};
-            p = mfma16x16x32(S.x[step], __builtin_bit_cast(f16x8, u), p);
+            for (int r = 0; r < 4; ++r) p[r] = __builtin_fmaf(-zp, xs[mt][g][r], -xo[mt][g][r]);
+#pragma unroll
+            for (int ss = 0; ss < 2; ++ss) {
+              const int step = 2 * g + ss;
+              const u32x4 u = {h[4 * step], h[4 * step + 1], h[4 * step + 2], h[4 * step + 3]};
+              p = mfma16x16x32(S.x[mt][step], __builtin_bit_cast(f16x8, u), p);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[f][mt][i][r] = __builtin_fmaf(sc, p[r], acc[f][mt][i][r]);
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[f][i][r] = __builtin_fmaf(sc, p[r], acc[f][i][r]);
         }
       }
   }
@@ -228,24 +245,26 @@ struct LateU<true, NS> {
 };
 
 // Per-item values loaded when an item starts and used at its end.
-template <int MP, bool LRQ, int NS>
+template <int MP, bool LRQ, int NS, int WMT>
 struct ItemLate {
-  f16x8 t[NS];        // low-rank T fragments (rows of this wave's m-tile x 32 ranks)
+  f16x8 t[WMT][NS];   // low-rank T fragments (rows of each m-tile of the wave x 32 ranks)
   LateU<LRQ, NS> lu;  // U operand of this wave's family
   int32_t sp[MP * 4]; // ROUTE_SCALE: slot index of each output row of this thread
   float pw[MP * 4];   // ROUTE_SCALE: route weight of those rows
 };
 
-template <int MP, int NW, int EPI, int DEPTH, bool LRQ>
+template <int MP, int NW, int EPI, int DEPTH, bool LRQ, bool FS = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_decode_kernel(GemmArgs a) {
-  using DecT = Dec<MP, NW, EPI>;
+  using DecT = Dec<MP, NW, EPI, FS>;
   constexpr int KW = DecT::KW;
+  constexpr int WF = DecT::WF, WMT = DecT::WMT;
   __shared__ DecShared sh;
   constexpr int kTile = 16 * 64;           // outputs of one m-tile per family
   constexpr int kOut = MP * kTile;         // outputs per family per item
   constexpr int kPer = kOut / 256;         // per thread
-  __shared__ float red[4][NW][kTile];      // wave partials of their own m-tile
+  // wave partials: [wave][family of the wave][m-tile of the wave] (WF x WMT = NW or MP tiles)
+  __shared__ float red[4][WF * WMT][kTile];
 
   // ---- experts with rows for this path, and their ranks
   for (int e = threadIdx.x; e <= a.num_experts; e += 256) sh.off[e] = a.offsets[e];
@@ -307,24 +326,29 @@ gemm_decode_kernel(GemmArgs a) {
   DecT D(a, sh, total);
   const int lane = D.lane, wave = D.wave, kw = D.kw, mtile = D.mtile;
   const int RW = a.n_w * a.rp;
-  // low-rank work of this wave: family kw mod NW, rank steps (32 ranks each)
-  // kw / NW + l LRW for l < NS, so the waves of an m-tile share the item-end
-  // work (steps past the padded rank are skipped)
-  constexpr int LRW = KW / NW;
-  constexpr int NS = LRW >= 2 ? 1 : 2;
-  const int lrf = kw % NW;
-  const int s2_0 = kw / NW;
+  // low-rank work of this wave: family lrf, rank steps (32 ranks each)
+  // s2_0 + l LRW for l < NS, so the waves that share an output set share its
+  // item-end work (steps past the padded rank are skipped).  Default split:
+  // family kw mod NW, steps from kw / NW in strides of KW / NW.  Family split:
+  // the wave's own family, steps from kw in strides of KW (one step each for
+  // ranks up to 64).
+  constexpr int LRW = FS ? KW : KW / NW;
+  constexpr int NS = FS ? 1 : (LRW >= 2 ? 1 : 2);
+  const int lrf = FS ? D.fam : kw % NW;
+  const int s2_0 = FS ? kw : kw / NW;
 
-  f32x4 acc[NW][4];
+  f32x4 acc[WF][WMT][4];
 #pragma unroll
-  for (int f = 0; f < NW; ++f)
+  for (int f = 0; f < WF; ++f)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < WMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[f][mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // item-start loads: low-rank fragments (every wave loads, waves that add no
   // low-rank term ignore them) and the epilogue's row metadata.  Addresses are
   // clamped to valid memory and masked values replaced, so every load is issued.
-  ItemLate<MP, LRQ, NS> late;
+  ItemLate<MP, LRQ, NS, WMT> late;
   auto load_late = [&](const Item& m) {
     if (a.rp > 0) {
       const int rk = sh.rank[lrf][m.e];
@@ -334,10 +358,14 @@ gemm_decode_kernel(GemmArgs a) {
         const int j0 = 32 * s2 + 8 * (lane >> 4);
         const bool jok = j0 < rk;
         const int jc = jok ? j0 : 0;
-        const int row = mtile * 16 + (lane & 15);
-        const bool ok = jok && row < m.M;
-        const f16x8 v = *(const f16x8*)(a.T + (size_t)(m.base + (row < m.M ? row : 0)) * RW + lrf * a.rp + jc);
-        late.t[l] = ok ? v : f16x8{};    // ranks >= rank: zero, so U's padding adds nothing
+#pragma unroll
+        for (int mt = 0; mt < WMT; ++mt) {
+          const int row = (mtile + mt) * 16 + (lane & 15);
+          const bool ok = jok && row < m.M;
+          const f16x8 v =
+              *(const f16x8*)(a.T + (size_t)(m.base + (row < m.M ? row : 0)) * RW + lrf * a.rp + jc);
+          late.t[mt][l] = ok ? v : f16x8{};    // ranks >= rank: zero, so U's padding adds nothing
+        }
         if constexpr (LRQ) {
           // 32-rank tile s2 if the expert has ranks there, else tile 0 (valid memory, unused)
           const int jt = 32 * s2 < rk ? s2 : 0;
@@ -371,7 +399,7 @@ gemm_decode_kernel(GemmArgs a) {
 
   auto finish_item = [&](const Item& m) {
     // low-rank term of family lrf, rank steps s2_0 + l LRW, for this wave's
-    // m-tile (added once: by the first K split)
+    // m-tiles (added once: by the first K split)
     if (a.rp > 0 && m.ks == 0) {
 #pragma unroll
       for (int l = 0; l < NS; ++l) {
@@ -384,31 +412,41 @@ gemm_decode_kernel(GemmArgs a) {
           for (int i = 0; i < 4; ++i) {
             const f16x8 ub = dequant_step(h, i, group_const(late.lu.sz[i]));
 #pragma unroll
-            for (int f = 0; f < NW; ++f)
-              if (f == lrf) acc[f][i] = mfma16x16x32(late.t[l], ub, acc[f][i]);
+            for (int f = 0; f < WF; ++f)
+#pragma unroll
+              for (int mt = 0; mt < WMT; ++mt)
+                if (FS || f == lrf) acc[f][mt][i] = mfma16x16x32(late.t[mt][l], ub, acc[f][mt][i]);
           }
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int f = 0; f < NW; ++f)
-              if (f == lrf) acc[f][i] = mfma16x16x32(late.t[l], late.lu.u[i][l], acc[f][i]);
+            for (int f = 0; f < WF; ++f)
+#pragma unroll
+              for (int mt = 0; mt < WMT; ++mt)
+                if (FS || f == lrf)
+                  acc[f][mt][i] = mfma16x16x32(late.t[mt][l], late.lu.u[i][l], acc[f][mt][i]);
         }
       }
     }
     __syncthreads();   // previous item's readers of red are done
 #pragma unroll
-    for (int f = 0; f < NW; ++f)
+    for (int f = 0; f < WF; ++f)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int mt = 0; mt < WMT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 4 * (lane >> 4) + r, n = 16 * i + (lane & 15);
-          red[wave][f][row * 64 + n] = acc[f][i][r];
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 4 * (lane >> 4) + r, n = 16 * i + (lane & 15);
+            red[wave][f * WMT + mt][row * 64 + n] = acc[f][mt][i][r];
+          }
+          acc[f][mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        acc[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
     __syncthreads();
+    // the item's outputs per family, the K-split waves added in wave order:
+    // default split, waves mt KW .. mt KW + KW - 1 hold m-tile mt (every
+    // family); family split, waves 2 kw + f hold family f (every m-tile)
     float res[NW][kPer];
 #pragma unroll
     for (int f = 0; f < NW; ++f)
@@ -418,7 +456,7 @@ gemm_decode_kernel(GemmArgs a) {
         const int mt = o / kTile, ol = o - mt * kTile;   // m-tile and offset within it
         float v = 0.f;
 #pragma unroll
-        for (int w = 0; w < KW; ++w) v += red[mt * KW + w][f][ol];
+        for (int w = 0; w < KW; ++w) v += FS ? red[2 * w + f][mt][ol] : red[mt * KW + w][f][ol];
         res[f][c] = v;
       }
     if (a.ksplit > 1) {
@@ -449,7 +487,7 @@ gemm_decode_kernel(GemmArgs a) {
   D.enter(pf, blockIdx.x);
   cs = pf;
   load_late(cs.item);
-  Stage<NW> ring[DEPTH];
+  Stage<WF, WMT> ring[DEPTH];
 #pragma unroll
   for (int d = 0; d < DEPTH - 1; ++d) {
     D.load(ring[d], pf);
@@ -477,10 +515,12 @@ gemm_decode_kernel(GemmArgs a) {
 template <int MP, int NW, int EPI>
 static void launch_one(const GemmArgs& a, int blocks, int num_experts, hipStream_t st) {
   constexpr int depth = NW == 1 ? 3 : 2;
+  // two m-tiles of gate/up: the family split (each code extracted once)
+  constexpr bool fs = MP == 2 && NW == 2;
   if (a.lrq)
-    hipLaunchKernelGGL((gemm_decode_kernel<MP, NW, EPI, depth, true>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_decode_kernel<MP, NW, EPI, depth, true, fs>), dim3(blocks), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((gemm_decode_kernel<MP, NW, EPI, depth, false>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_decode_kernel<MP, NW, EPI, depth, false, fs>), dim3(blocks), dim3(256), 0, st, a);
   if (a.ksplit > 1)
     hipLaunchKernelGGL((gemm_split_reduce<16 * MP, NW, EPI>), dim3(a.n_tiles, num_experts), dim3(256), 0,
                        st, a);
