@@ -407,10 +407,13 @@ typedef struct milo_gemm_desc {
   int32_t max_rows_per_expert;  /* host upper bound on offsets[e+1]-offsets[e]
                                    (e.g. T for top-k routing); 0 = num_pairs.
                                    The plan is chosen from it without reading
-                                   the device offsets; if an expert exceeds it
-                                   and the plan has no kernel for that many
-                                   rows, that expert's output rows are set to
-                                   NaN (never left unwritten)                 */
+                                   the device offsets.  If an expert exceeds
+                                   it: a plan of the small-M kernel alone
+                                   without split K takes the expert in row
+                                   chunks (correct, slower); a plan with no
+                                   kernel for that many rows sets the
+                                   expert's output rows to NaN (never left
+                                   unwritten)                                  */
   const float* slot_w;          /* ROUTE_SCALE only: float32 [y_rows]          */
   int32_t y_rows;               /* ROUTE_SCALE only: rows of y                 */
   int32_t epilogue;             /* MILO_EPI_*                                  */
@@ -441,7 +444,12 @@ size_t milo_moe_gemm_workspace_bytes(const milo_gemm_desc* desc);
  * (silu(u) = u / (1 + exp(-u))); ROUTE_SCALE stores Y_0 * slot_w[s] as fp32
  * into row s = sorted_pairs[i] (rows of y that no pair maps to are not
  * written).  The path (small-M streaming kernel or matrix-core tile kernel)
- * is chosen per expert from its row count on the device unless forced.
+ * is chosen per expert from its row count on the device unless forced; with
+ * MILO_PATH_AUTO the host plans which kernels to launch from
+ * max_rows_per_expert, num_pairs and the matrix size (N K), never from the
+ * device offsets.  MILO_PATH_DECODE needs max_rows_per_expert <= 32
+ * (MILO_ERR_SHAPE otherwise).  The call is capturable into a HIP graph: it
+ * allocates, synchronizes and clears nothing.
  *
  * workspace: milo_moe_gemm_workspace_bytes(desc) bytes (may be 0), 256-byte
  *   aligned, scratch only (no initialisation needed, contents undefined after
