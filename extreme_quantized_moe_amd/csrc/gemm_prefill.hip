@@ -5,22 +5,29 @@
 // with fused dequantization; asynchronous global loads overlap memory with
 // compute.  MiLo Algorithm: W_out = W_quant + U V.
 //
-// Grid: x = n-tile groups (fastest), y = row tiles of BM rows (128 where
-// experts average 256 rows or more, else 64), so the blocks that run together
-// share activation rows (L2 hits) while the weights stream.
+// Work: (row tile of BM rows, n-tile group), n-tile groups fastest, so the
+// blocks that run together share activation rows (L2 hits) while the weights
+// stream.  BM = 128 where experts average 256 rows or more, else 64.  One
+// block per work item (grid x = n-tile groups, y = row tiles), except the
+// 64-row gate/up form, which runs persistent: two blocks per CU walk the
+// items of a per-block table of the experts' row tiles (prefix sums in LDS),
+// so no block is empty and the expert scan runs once per block.
 // Block = BM rows of one expert (pairs in sorted order) x 4 waves.  Each wave
 // owns one 64-wide output tile of one weight family (SWIGLU: waves (W1, W3) x
 // two n-tiles; otherwise four n-tiles of the one family), so every packed
-// weight tile is read and dequantized by exactly one wave.  Activation rows
-// go straight from global memory into LDS (global_load_lds_dwordx4: BM rows
-// x 128 K, double buffered, 16-byte chunks XOR-swizzled per row against bank
-// conflicts) and are shared by the four waves; the next K block's
-// activations (into LDS) and weights (into registers) load while the current
-// one is computed.  Weights are dequantized in registers (int3 pair
-// extraction, then packed fp16: subtract the offset, one fused multiply-add
-// by the scale with -z s) and multiplied on v_mfma_f32_16x16x32_f16 with fp32
-// accumulation; each K block is one branch-free region the scheduler
-// interleaves, issued at raised wave priority.
+// weight tile is read and dequantized by exactly one wave.
+// Loads: 128-row tiles move activations (BM rows x 128 K, double buffered,
+// 16-byte chunks XOR-swizzled per row against bank conflicts) and weights
+// (one slot per wave) from global memory straight into LDS with buffer
+// loads, so the loop waits only where it says so; 64-row tiles stage the
+// activations through LDS and keep a register ring of 2-4 weight stages.
+// The next K blocks load while the current one is computed.
+// Dequantization: tiles of up to 32 rows fold it into per-group fp32
+// corrections (codes reach the matrix cores as exact fp16 off + q); larger
+// tiles form (q - z) s in fp32 and round it once to fp16 (v_fma_mix).
+// Products on v_mfma_f32_16x16x32_f16 with fp32 accumulation; each K block
+// is one branch-free region the scheduler interleaves, issued at raised wave
+// priority.
 // Epilogue: low-rank term as two more matrix-core K-steps per 32 ranks, then
 // SWIGLU through LDS, or fp16 store, or route-weighted fp32 scatter.
 #include <type_traits>
