@@ -581,15 +581,91 @@ __device__ __forceinline__ void tile_body_lds(const GemmArgs& a, const RowTile& 
   tile_finish<NW, LRQ, NMT>(a, rt, lds, kc, acc, f, nt, wave_on);
 }
 
+// Row tile `tile` of the 64-row tiling, with the tiles ordered by cost: the
+// experts' full tiles first, then their partial last tiles of 33..63, 17..32
+// and 1..16 rows, each class in expert order.  The hardware starts blocks in
+// index order, so the costliest tiles start first and the cheapest fill the
+// tail.  Experts of at most min_rows rows have no tiles.  Block-uniform
+// result through LDS; false past the last tile.  The first wave reads the
+// offsets and ranks of four experts per lane (up to 256 experts) and scans
+// the four classes' tile counts with lane shuffles.  Every thread of the
+// block must call it.
+__device__ __forceinline__ bool find_row_tile64_by_cost(const GemmArgs& a, int tile, RowTile* out) {
+  __shared__ int res[6];
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x, E = a.num_experts;
+    const int32_t* rk0 = a.rp ? a.rank[0] : a.offsets;   // valid dummy when unused
+    const int32_t* rk1 = a.rp ? a.rank[1] : a.offsets;
+    int o0[4], o1[4], r0[4], r1[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = 4 * lane + c;
+      const int ec = e < E ? e : E - 1;
+      o0[c] = a.offsets[ec];
+      o1[c] = a.offsets[ec + 1];
+      r0[c] = rk0[ec];
+      r1[c] = rk1[ec];
+    }
+    if (lane == 0) res[0] = -1;
+    int n[4][4], sum[4] = {0, 0, 0, 0};   // [class][expert of the lane]
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int M = 4 * lane + c < E ? o1[c] - o0[c] : 0;
+      const bool in = M > a.pre_min_rows;
+      const int rem = M % 64;
+      n[0][c] = in ? M / 64 : 0;
+      n[1][c] = in && rem > 32 ? 1 : 0;
+      n[2][c] = in && rem > 16 && rem <= 32 ? 1 : 0;
+      n[3][c] = in && rem > 0 && rem <= 16 ? 1 : 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sum[k] += n[k][c];
+    }
+    int before = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      int inc = sum[k];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o);
+        if (lane >= o) inc += v;
+      }
+      int first = before + inc - sum[k];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (n[k][c] > 0 && tile >= first && tile < first + n[k][c]) {
+          const int M = o1[c] - o0[c];
+          res[0] = 4 * lane + c;
+          res[1] = k == 0 ? (tile - first) * 64 : (M / 64) * 64;
+          res[2] = M;
+          res[3] = o0[c];
+          res[4] = a.rp ? r0[c] : 0;
+          res[5] = a.rp ? r1[c] : 0;
+        }
+        first += n[k][c];
+      }
+      before += __shfl(inc, 63);
+    }
+  }
+  __syncthreads();
+  out->e = res[0];
+  out->m0 = res[1];
+  out->rows = res[2];
+  out->base = res[3];
+  out->rank0 = res[4];
+  out->rank1 = res[5];
+  return out->e >= 0;
+}
+
 template <int NW, bool LRQ, int BM>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_prefill_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   const CodeConsts kc = make_code_consts();
   RowTile rt;
-  if (!find_row_tile(a.offsets, a.num_experts, a.pre_min_rows, BM, blockIdx.y, a.rp ? a.rank[0] : nullptr,
-                     a.rp ? a.rank[1] : nullptr, &rt))
-    return;
+  const bool found = BM == 64 ? find_row_tile64_by_cost(a, blockIdx.y, &rt)
+                              : find_row_tile(a.offsets, a.num_experts, a.pre_min_rows, BM, blockIdx.y,
+                                              a.rp ? a.rank[0] : nullptr, a.rp ? a.rank[1] : nullptr, &rt);
+  if (!found) return;
   if constexpr (BM == 64) {
     // only the tile's own rows: fewer products and staged rows for the
     // small experts (a 3-row expert costs one m-tile, not four)
@@ -610,10 +686,18 @@ gemm_prefill_kernel(GemmArgs a) {
 
 // 64-row tiles, persistent: a grid of two blocks per compute unit walks the
 // work items (row tile, n-tile group), n-tile groups fastest (consecutive
-// items share activation rows).  The row tiles are listed once per block:
-// the experts' full 64-row tiles first, then their partial last tiles (the
-// bigger tiles start first), as prefix sums in LDS; an item finds its tile by
-// binary search.  No block starts past the last item, and the expert scan
+// items share activation rows).  The row tiles are listed once per block, by
+// cost: the experts' full 64-row tiles first, then their partial last tiles
+// of 33..63, 17..32 and 1..16 rows (four, two and one m-tiles), each class as
+// prefix sums over the experts in LDS; an item finds its tile by binary
+// search.  Items are dealt in rounds of one per block, every other round in
+// reverse block order, so a block that took one of the costliest items of a
+// round takes one of the cheapest of the next (a Zipf-skewed routing leaves
+// about 1.5 items per block, where a plain round robin gives some blocks two
+// costly items and others one cheap one; C4 gate/up 83 -> 78 us).  Dealing
+// a round's consecutive items to the blocks of one XCD instead (blocks are
+// placed on the eight XCDs round robin) was slower (84 us): it puts a round's
+// costliest items on one XCD.  No block starts past the last item, and the expert scan
 // runs once per block instead of once per tile.  With three tile shapes in
 // one loop the registers allow two stages in flight for the 2- and 4-m-tile
 // shapes; that suits the gate/up form (two weight families per wave), while
@@ -623,7 +707,8 @@ template <int NW, bool LRQ>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_prefill_persistent(GemmArgs a, int n_groups) {
   extern __shared__ __align__(16) uint16_t lds[];
-  __shared__ int tab_full[kMaxTileExperts + 1], tab_part[kMaxTileExperts + 1];
+  // tab[0]: full tiles; tab[1..3]: partial last tiles of 33..63, 17..32, 1..16 rows
+  __shared__ int tab[4][kMaxTileExperts + 1];
   __shared__ int e_base[kMaxTileExperts], e_rows[kMaxTileExperts], e_rk0[kMaxTileExperts],
       e_rk1[kMaxTileExperts];
   const CodeConsts kc = make_code_consts();
@@ -632,7 +717,7 @@ gemm_prefill_persistent(GemmArgs a, int n_groups) {
     const int lane = threadIdx.x;
     const int32_t* rk0 = a.rp ? a.rank[0] : a.offsets;   // valid dummy when unused
     const int32_t* rk1 = a.rp ? a.rank[1] : a.offsets;
-    int nf[4], np[4], o0[4], o1[4], r0[4], r1[4];
+    int o0[4], o1[4], r0[4], r1[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int e = 4 * lane + c;
@@ -642,16 +727,19 @@ gemm_prefill_persistent(GemmArgs a, int n_groups) {
       r0[c] = rk0[ec];
       r1[c] = rk1[ec];
     }
-    int sf = 0, sp = 0;
+    int n[4][4], sum[4] = {0, 0, 0, 0};   // [class][expert of the lane]
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int e = 4 * lane + c;
       const int M = e < E ? o1[c] - o0[c] : 0;
       const bool in = M > a.pre_min_rows;
-      nf[c] = in ? M / 64 : 0;
-      np[c] = in && (M % 64) ? 1 : 0;
-      sf += nf[c];
-      sp += np[c];
+      const int rem = M % 64;
+      n[0][c] = in ? M / 64 : 0;
+      n[1][c] = in && rem > 32 ? 1 : 0;
+      n[2][c] = in && rem > 16 && rem <= 32 ? 1 : 0;
+      n[3][c] = in && rem > 0 && rem <= 16 ? 1 : 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sum[k] += n[k][c];
       if (e < E) {
         e_base[e] = o0[c];
         e_rows[e] = M;
@@ -659,53 +747,51 @@ gemm_prefill_persistent(GemmArgs a, int n_groups) {
         e_rk1[e] = a.rp ? r1[c] : 0;
       }
     }
-    int incf = sf, incp = sp;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int vf = __shfl_up(incf, o), vp = __shfl_up(incp, o);
-      if (lane >= o) {
-        incf += vf;
-        incp += vp;
-      }
-    }
-    int rf = incf - sf, rp = incp - sp;
+    for (int k = 0; k < 4; ++k) {
+      int inc = sum[k];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e = 4 * lane + c;
-      if (e < E) {
-        tab_full[e] = rf;
-        tab_part[e] = rp;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o);
+        if (lane >= o) inc += v;
       }
-      rf += nf[c];
-      rp += np[c];
-    }
-    if (lane == 63) {   // the totals (E may be 256, past every lane's experts)
-      tab_full[E] = incf;
-      tab_part[E] = incp;
+      int r = inc - sum[k];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = 4 * lane + c;
+        if (e < E) tab[k][e] = r;
+        r += n[k][c];
+      }
+      if (lane == 63) tab[k][E] = inc;   // the totals (E may be 256, past every lane's experts)
     }
   }
   __syncthreads();
-  const int TF = tab_full[E], TP = tab_part[E];
-  const int n_items = (TF + TP) * n_groups;
-  // the last expert with tab[e] <= t (experts without tiles share their
-  // successor's start and are skipped)
-  auto find = [&](const int* tab, int t) {
+  const int T0 = tab[0][E], T1 = T0 + tab[1][E], T2 = T1 + tab[2][E], T3 = T2 + tab[3][E];
+  const int n_items = T3 * n_groups;
+  // the last expert with tab[e] <= t (experts without tiles of the class
+  // share their successor's start and are skipped)
+  auto find = [&](const int* t_, int t) {
     int lo = 0, hi = E - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (tab[mid] <= t) lo = mid;
+      if (t_[mid] <= t) lo = mid;
       else hi = mid - 1;
     }
     return lo;
   };
-  for (int w = blockIdx.x; w < n_items; w += gridDim.x) {
+  const int G = gridDim.x, b = blockIdx.x;
+  for (int round = 0;; ++round) {
+    const int w = round * G + ((round & 1) ? G - 1 - b : b);
+    if (w >= n_items) break;
     const int tile = w / n_groups, ng = w - tile * n_groups;
     RowTile rt;
-    if (tile < TF) {
-      rt.e = find(tab_full, tile);
-      rt.m0 = (tile - tab_full[rt.e]) * 64;
+    if (tile < T0) {
+      rt.e = find(tab[0], tile);
+      rt.m0 = (tile - tab[0][rt.e]) * 64;
     } else {
-      rt.e = find(tab_part, tile - TF);
+      const int k = tile < T1 ? 1 : (tile < T2 ? 2 : 3);
+      const int first = k == 1 ? T0 : (k == 2 ? T1 : T2);
+      rt.e = find(tab[k], tile - first);
       rt.m0 = (e_rows[rt.e] / 64) * 64;
     }
     rt.rows = e_rows[rt.e];
