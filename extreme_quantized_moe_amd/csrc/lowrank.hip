@@ -789,9 +789,9 @@ int32_t launch_lowrank(const milo_gemm_desc* d, const GemmPlan& p, char* ws, hip
         set_error("internal: unsupported rank-tile count %d", per);
         return MILO_ERR_RANK;
       }
-      // unsplit K of 64 steps or more: eight waves with all eight of their
+      // unsplit K of 32 steps or more: eight waves with all eight of their
       // steps' loads in flight at once (one batch per wave where K <= 2048)
-      const bool wide = p.lr_ks == 1 && d->K / 32 >= 64;
+      const bool wide = p.lr_ks == 1 && d->K / 32 >= 32;
       if (tpb == 2 && wide) hipLaunchKernelGGL((prepass_kernel<2, 8, 8, 1>), grid, dim3(512), 0, st, a);
       else if (tpb == 2) hipLaunchKernelGGL((prepass_kernel<2, 4, 4, 1>), grid, dim3(256), 0, st, a);
       else if (wide) hipLaunchKernelGGL((prepass_kernel<4, 8, 8, 1>), grid, dim3(512), 0, st, a);
