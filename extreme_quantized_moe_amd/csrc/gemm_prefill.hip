@@ -247,44 +247,123 @@ struct TileDepth {
   static constexpr int D = NMT <= 1 ? 4 : (NMT <= 4 ? 3 : 2);
 };
 
+// One 32-rank step of the low-rank term of a wave's output tile: the U
+// operand (fp16 fragments, or the lane's int3 triplet and the scale/zero
+// words of its four rows) and the T fragments of the m-tiles.
+template <bool LRQ, int NMT>
+struct LrStep {
+  f16x8 u[4];
+  uint32_t q[3];
+  u32x4 sz;
+  f16x8 t[NMT];
+};
+
+template <bool LRQ, int NMT>
+__device__ __forceinline__ void lr_load(const GemmArgs& a, const RowTile& rt, int f, int nt, int s2,
+                                        LrStep<LRQ, NMT>& L) {
+  const int lane = threadIdx.x & 63;
+  const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
+  const int RW = a.n_w * a.rp;
+  const int j0 = 32 * s2 + 8 * (lane >> 4);
+  if constexpr (LRQ) {
+    L.sz = *(const u32x4*)(a.Usz[f] + (size_t)e * a.N + nt * kTileRows + 4 * (lane & 15));
+    const uint32_t* up = a.Uq[f] + e * a.uq_per_expert + ((size_t)nt * (a.rp / 32) + s2) * 192 + lane;
+    L.q[0] = up[0];
+    L.q[1] = up[64];
+    L.q[2] = up[128];
+  } else {
+    const int rk = rt.rank(f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = nt * kTileRows + 16 * i + (lane & 15);
+      L.u[i] = j0 < rk ? *(const f16x8*)(a.U[f] + ((size_t)e * a.N + n) * a.max_rank + j0) : f16x8{};
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    const int m = m0 + mt * 16 + (lane & 15);
+    const f16x8 tv = *(const f16x8*)(a.T + (size_t)(base + (m < M ? m : m0)) * RW + f * a.rp + j0);
+    L.t[mt] = m < M ? tv : f16x8{};
+  }
+}
+
+template <bool LRQ, int NMT>
+__device__ __forceinline__ void lr_apply(const LrStep<LRQ, NMT>& L, int rk, int s2, const CodeConsts& kc,
+                                         f32x4 (&acc)[NMT][4]) {
+  const int lane = threadIdx.x & 63;
+  const int j0 = 32 * s2 + 8 * (lane >> 4);
+  f16x8 ub[4];
+  if constexpr (LRQ) {
+    uint32_t h[16];
+    extract_triplet(L.q[0], L.q[1], L.q[2], h, kc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ub[i] = j0 < rk ? dequant_step(h, i, group_const(L.sz[i])) : f16x8{};
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ub[i] = L.u[i];
+  }
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[mt][i] = mfma16x16x32(L.t[mt], ub[i], acc[mt][i]);
+}
+
+// Epilogue values loaded when a tile starts, so that their latency hides
+// behind the K loop: with ROUTE_SCALE lane l holds the pair index and the
+// route weight of tile rows l and 64 + l; with PRE the first 32-rank step of
+// the low-rank term is loaded too.
+template <bool LRQ, int NMT, bool PRE>
+struct TilePre {
+  int sp[2];
+  float w[2];
+  LrStep<LRQ, NMT> lr;
+};
+
+// Pair indexes of the tile's rows (first half of TilePre; the weights need
+// them, so tile_pre_weights issues their loads later, once they have arrived).
+template <int NW, bool LRQ, int NMT, bool PRE>
+__device__ __forceinline__ void tile_pre_pairs(const GemmArgs& a, const RowTile& rt, int f, int nt, bool wave_on,
+                                               TilePre<LRQ, NMT, PRE>& P) {
+  const int lane = threadIdx.x & 63;
+  if (NW == 1 && a.epilogue == MILO_EPI_ROUTE_SCALE) {
+#pragma unroll
+    for (int h = 0; h < (NMT > 4 ? 2 : 1); ++h) {
+      const int row = rt.m0 + 64 * h + lane;
+      P.sp[h] = row < rt.rows ? a.sorted_pairs[rt.base + row] : 0;
+    }
+  }
+  if constexpr (PRE) {
+    if (wave_on && a.rp > 0) lr_load<LRQ, NMT>(a, rt, f, nt, 0, P.lr);
+  }
+}
+
+template <int NW, bool LRQ, int NMT, bool PRE>
+__device__ __forceinline__ void tile_pre_weights(const GemmArgs& a, TilePre<LRQ, NMT, PRE>& P) {
+  if (NW == 1 && a.epilogue == MILO_EPI_ROUTE_SCALE) {
+#pragma unroll
+    for (int h = 0; h < (NMT > 4 ? 2 : 1); ++h) P.w[h] = a.slot_w[P.sp[h]];
+  }
+}
+
 // After the K loop: the low-rank term and the epilogue of a wave's output
 // tile (NMT m-tiles x 64 columns of family f, n-tile nt).
-template <int NW, bool LRQ, int NMT>
+template <int NW, bool LRQ, int NMT, bool PRE>
 __device__ __forceinline__ void tile_finish(const GemmArgs& a, const RowTile& rt, uint16_t* lds,
                                             const CodeConsts& kc, f32x4 (&acc)[NMT][4], int f, int nt,
-                                            bool wave_on) {
+                                            bool wave_on, const TilePre<LRQ, NMT, PRE>& P) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = rt.e, m0 = rt.m0, M = rt.rows, base = rt.base;
+  const int m0 = rt.m0, M = rt.rows, base = rt.base;
   // ---- low-rank term: (x V^T) U^T as extra K steps (int3 U: the lane's
   // triplet of each 32-rank U tile is its B operand for the four row groups)
   if (wave_on && a.rp > 0) {
-    const int RW = a.n_w * a.rp;
     const int rk = rt.rank(f);
-    u32x4 usz = {0u, 0u, 0u, 0u};
-    if constexpr (LRQ) usz = *(const u32x4*)(a.Usz[f] + (size_t)e * a.N + nt * kTileRows + 4 * (lane & 15));
     for (int s2 = 0; s2 < a.rp / 32; ++s2) {
-      const int j0 = 32 * s2 + 8 * (lane >> 4);
-      f16x8 ub[4];
-      if constexpr (LRQ) {
-        const uint32_t* up = a.Uq[f] + e * a.uq_per_expert + ((size_t)nt * (a.rp / 32) + s2) * 192 + lane;
-        uint32_t h[16];
-        extract_triplet(up[0], up[64], up[128], h, kc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ub[i] = j0 < rk ? dequant_step(h, i, group_const(usz[i])) : f16x8{};
+      if (PRE && s2 == 0) {
+        lr_apply<LRQ, NMT>(P.lr, rk, 0, kc, acc);
       } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = nt * kTileRows + 16 * i + (lane & 15);
-          ub[i] = j0 < rk ? *(const f16x8*)(a.U[f] + ((size_t)e * a.N + n) * a.max_rank + j0) : f16x8{};
-        }
-      }
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-        const int m = m0 + mt * 16 + (lane & 15);
-        const f16x8 tv = *(const f16x8*)(a.T + (size_t)(base + (m < M ? m : m0)) * RW + f * a.rp + j0);
-        const f16x8 ta = m < M ? tv : f16x8{};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][i] = mfma16x16x32(ta, ub[i], acc[mt][i]);
+        LrStep<LRQ, NMT> L;
+        lr_load<LRQ, NMT>(a, rt, f, nt, s2, L);
+        lr_apply<LRQ, NMT>(L, rk, s2, kc, acc);
       }
     }
   }
@@ -323,16 +402,23 @@ __device__ __forceinline__ void tile_finish(const GemmArgs& a, const RowTile& rt
     return;
   }
   if (!wave_on) return;
+  const bool route = a.epilogue == MILO_EPI_ROUTE_SCALE;
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int mm = mt * 16 + 4 * (lane >> 4) + r;
+      // row mm's pair and weight from the lane that loaded them (half mt / 4
+      // of the tile, lane mm mod 64), read while every lane is active
+      int s = 0;
+      float w = 0.f;
+      if (NW == 1 && route) {
+        s = __shfl(P.sp[mt >> 2], mm & 63);
+        w = __shfl(P.w[mt >> 2], mm & 63);
+      }
       if (m0 + mm >= M) continue;
       const int i_pair = base + m0 + mm;
-      if (a.epilogue == MILO_EPI_ROUTE_SCALE) {
-        const int s = a.sorted_pairs[i_pair];
-        const float w = a.slot_w[s];
+      if (NW == 1 && route) {
         float* yrow = (float*)a.y + (size_t)s * a.N + nt * kTileRows;
 #pragma unroll
         for (int i = 0; i < 4; ++i) yrow[16 * i + (lane & 15)] = acc[mt][i][r] * w;
@@ -432,11 +518,17 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const RowTile& rt, 
   // after the barrier.  The loop is unrolled by D so slots are registers.
   // Blocks past the end re-load the last block (never computed): every
   // iteration issues the same loads.
+  // epilogue values (pair indexes and weights, the first low-rank step for
+  // tiles of up to two m-tiles, where the registers allow) loaded ahead
+  constexpr bool kPre = NW == 1 && NMT <= 2;
+  TilePre<LRQ, NMT, kPre> pre;
+  tile_pre_pairs<NW, LRQ, NMT, kPre>(a, rt, f, nt, wave_on, pre);
   TileStage<NMT> ring[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(ring[d], d < KB ? d : KB - 1);
   put_x(ring[0], 0);
   __syncthreads();
+  tile_pre_weights<NW, LRQ, NMT, kPre>(a, pre);
   for (int kb0 = 0; kb0 < KB; kb0 += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
@@ -455,7 +547,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const RowTile& rt, 
     }
   }
 
-  tile_finish<NW, LRQ, NMT>(a, rt, lds, kc, acc, f, nt, wave_on);
+  tile_finish<NW, LRQ, NMT, kPre>(a, rt, lds, kc, acc, f, nt, wave_on, pre);
 }
 
 // 128-row tiles (eight m-tiles): the accumulators take half the registers,
@@ -571,14 +663,19 @@ __device__ __forceinline__ void tile_body_lds(const GemmArgs& a, const RowTile& 
     __syncthreads();
   };
 
+  // pair indexes and route weights of the epilogue loaded ahead (the
+  // weights once the indexes are in; the first block's wait covers them)
+  TilePre<LRQ, NMT, false> pre;
+  tile_pre_pairs<NW, LRQ, NMT, false>(a, rt, f, nt, wave_on, pre);
   issue(0, std::integral_constant<int, 0>());
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
+  tile_pre_weights<NW, LRQ, NMT, false>(a, pre);
   for (int kb = 0; kb < KB; kb += 2) {
     step(kb, std::integral_constant<int, 0>());
     if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>());
   }
-  tile_finish<NW, LRQ, NMT>(a, rt, lds, kc, acc, f, nt, wave_on);
+  tile_finish<NW, LRQ, NMT, false>(a, rt, lds, kc, acc, f, nt, wave_on, pre);
 }
 
 // Row tile `tile` of the 64-row tiling, with the tiles ordered by cost: the
