@@ -228,6 +228,25 @@ __device__ __forceinline__ void stage_rows(const GemmArgs& a, int m0, int M, int
   }
 }
 
+// The tile's activation row of each lane (tile row l for lane l < 64; rows
+// past the expert's count take its first row), loaded ahead of the tile.
+__device__ __forceinline__ int tile_row_of_lane(const GemmArgs& a, const RowTile& rt) {
+  const int m = rt.m0 + (int)(threadIdx.x & 63);
+  const int i = rt.base + (m < rt.rows ? m : rt.m0);
+  return a.gather_div > 0 ? a.sorted_pairs[i] / a.gather_div : i;
+}
+
+// stage_rows from rows loaded ahead by tile_row_of_lane.
+template <int NMT>
+__device__ __forceinline__ void stage_rows_pre(const GemmArgs& a, int lane_row, int srow, int lane,
+                                               const uint16_t* (&xsrc)[NMT]) {
+#pragma unroll
+  for (int j = 0; j < NMT; ++j) {
+    const int xr = __shfl(lane_row, srow + 16 * j);
+    xsrc[j] = a.x + (size_t)xr * a.K + 8 * ((lane & 15) ^ (srow & 15));
+  }
+}
+
 // Loads of one K block of a wave: its 64 x 128 code tile (three planes), the
 // eight scale/zero words of its lane's rows, and its NMT 16-byte chunks of
 // the block's activation rows.  Register stages of a ring: everything is a
@@ -431,9 +450,9 @@ __device__ __forceinline__ void tile_finish(const GemmArgs& a, const RowTile& rt
 }
 
 // One block's tile: NMT active 16-row m-tiles (the tile's rows, rounded up).
-template <int NW, bool LRQ, int NMT, bool X32, int D = TileDepth<NMT>::D>
+template <int NW, bool LRQ, int NMT, bool X32, int D = TileDepth<NMT>::D, bool ROWPRE = false>
 __device__ __forceinline__ void tile_body(const GemmArgs& a, const RowTile& rt, uint16_t* lds,
-                                          const CodeConsts& kc, int ng) {
+                                          const CodeConsts& kc, int ng, int lane_row = 0) {
   constexpr int kXBuf = NMT * 16 * kXStride;   // halves per staging buffer
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -450,7 +469,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const RowTile& rt, 
   // stored.
   const int srow = 4 * wave + (lane >> 4);
   const uint16_t* xsrc[NMT];
-  stage_rows<NMT>(a, m0, M, base, srow, lane, xsrc);
+  if constexpr (ROWPRE) stage_rows_pre<NMT>(a, lane_row, srow, lane, xsrc);
+  else stage_rows<NMT>(a, m0, M, base, srow, lane, xsrc);
   const int xdst = srow * kXStride + 8 * (lane & 15);
   // fragment of K step s: row lane % 16 of each m-tile, chunk 4 s + lane / 16
   int xoff[4];
@@ -877,11 +897,9 @@ gemm_prefill_persistent(GemmArgs a, int n_groups) {
     return lo;
   };
   const int G = gridDim.x, b = blockIdx.x;
-  for (int round = 0;; ++round) {
-    const int w = round * G + ((round & 1) ? G - 1 - b : b);
-    if (w >= n_items) break;
-    const int tile = w / n_groups, ng = w - tile * n_groups;
-    RowTile rt;
+  auto item = [&](int round) { return round * G + ((round & 1) ? G - 1 - b : b); };
+  auto lookup = [&](int w, RowTile& rt) {
+    const int tile = w / n_groups;
     if (tile < T0) {
       rt.e = find(tab[0], tile);
       rt.m0 = (tile - tab[0][rt.e]) * 64;
@@ -895,11 +913,30 @@ gemm_prefill_persistent(GemmArgs a, int n_groups) {
     rt.base = e_base[rt.e];
     rt.rank0 = e_rk0[rt.e];
     rt.rank1 = e_rk1[rt.e];
+  };
+  // each item's activation row indexes are loaded while the previous item
+  // runs (one register per lane), so an item starts with its first loads
+  RowTile nrt;
+  int nrow = 0;
+  if (item(0) < n_items) {
+    lookup(item(0), nrt);
+    nrow = tile_row_of_lane(a, nrt);
+  }
+  for (int round = 0;; ++round) {
+    const int w = item(round);
+    if (w >= n_items) break;
+    const int ng = w % n_groups;
+    const RowTile rt = nrt;
+    const int row = nrow;
+    if (item(round + 1) < n_items) {
+      lookup(item(round + 1), nrt);
+      nrow = tile_row_of_lane(a, nrt);
+    }
     // the launcher takes this kernel only when the activations fit 32-bit
     // offsets
-    if (rt.rows - rt.m0 <= 16) tile_body<NW, LRQ, 1, true>(a, rt, lds, kc, ng);
-    else if (rt.rows - rt.m0 <= 32) tile_body<NW, LRQ, 2, true, 2>(a, rt, lds, kc, ng);
-    else tile_body<NW, LRQ, 4, true, 2>(a, rt, lds, kc, ng);
+    if (rt.rows - rt.m0 <= 16) tile_body<NW, LRQ, 1, true, TileDepth<1>::D, true>(a, rt, lds, kc, ng, row);
+    else if (rt.rows - rt.m0 <= 32) tile_body<NW, LRQ, 2, true, 2, true>(a, rt, lds, kc, ng, row);
+    else tile_body<NW, LRQ, 4, true, 2, true>(a, rt, lds, kc, ng, row);
     __syncthreads();   // the next item reuses the LDS
   }
 }
