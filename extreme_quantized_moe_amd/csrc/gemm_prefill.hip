@@ -814,10 +814,12 @@ gemm_prefill_kernel(GemmArgs a) {
 // costly items and others one cheap one; C4 gate/up 83 -> 78 us).  Dealing
 // a round's consecutive items to the blocks of one XCD instead (blocks are
 // placed on the eight XCDs round robin) was slower (84 us): it puts a round's
-// costliest items on one XCD.  No block starts past the last item, and the expert scan
-// runs once per block instead of once per tile.  With three tile shapes in
-// one loop the registers allow two stages in flight for the 2- and 4-m-tile
-// shapes; that suits the gate/up form (two weight families per wave), while
+// costliest items on one XCD.  The next item's activation row indexes are
+// loaded while the current item runs.  No block starts past the last item,
+// and the expert scan runs once per block instead of once per tile.  With
+// three tile shapes in one loop the registers allow two stages in flight for
+// the 2- and 4-m-tile shapes; that suits the gate/up form (two weight
+// families per wave), while
 // the one-family form keeps its three stages in the one-tile-per-block
 // kernel, measured faster there.
 template <int NW, bool LRQ>
