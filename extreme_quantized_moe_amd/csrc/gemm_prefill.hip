@@ -206,26 +206,28 @@ __device__ __forceinline__ void tile_products_fold(const u32x4 (&q)[3], const u3
 }
 
 // Source addresses of the activation chunks a lane stages: rows
-// srow + 16 j (j < NMT) of the tile, gathered through sorted_pairs; rows past
-// the expert's count take its first row.  All index loads are issued before
-// any is used (no dependent round trip per row).
+// srow + 16 j (j < NMT) of the tile, gathered through sorted_pairs (or in
+// pair order already: no index load); rows past the expert's count take its
+// first row.  All index loads are issued before any is used (no dependent
+// round trip per row).
 template <int NMT>
 __device__ __forceinline__ void stage_rows(const GemmArgs& a, int m0, int M, int base, int srow, int lane,
                                            const uint16_t* (&xsrc)[NMT]) {
-  const bool gather = a.gather_div > 0;
-  const int32_t* idx_src = gather ? a.sorted_pairs : a.offsets;   // a valid array either way
-  int i[NMT], v[NMT];
+  int i[NMT], xr[NMT];
 #pragma unroll
   for (int j = 0; j < NMT; ++j) {
     const int m = m0 + srow + 16 * j;
     i[j] = base + (m < M ? m : m0);
-    v[j] = idx_src[gather ? i[j] : 0];
+    xr[j] = i[j];
+  }
+  if (a.gather_div > 0) {   // uniform: rows in pair order need no index load
+#pragma unroll
+    for (int j = 0; j < NMT; ++j) xr[j] = a.sorted_pairs[i[j]];
+#pragma unroll
+    for (int j = 0; j < NMT; ++j) xr[j] /= a.gather_div;
   }
 #pragma unroll
-  for (int j = 0; j < NMT; ++j) {
-    const int xr = gather ? v[j] / a.gather_div : i[j];
-    xsrc[j] = a.x + (size_t)xr * a.K + 8 * ((lane & 15) ^ (srow & 15));
-  }
+  for (int j = 0; j < NMT; ++j) xsrc[j] = a.x + (size_t)xr[j] * a.K + 8 * ((lane & 15) ^ (srow & 15));
 }
 
 // The tile's activation row of each lane (tile row l for lane l < 64; rows
