@@ -211,6 +211,21 @@ def test_prefill_every_tile_shape_256_experts(epi):
     assert_close(got, want, f"256 experts, every tile shape, {epi}")
 
 
+def test_prefill_persistent_several_rounds():
+    """The persistent 64-row gate/up launch with several rounds of items per
+    block (256 experts of every tile shape, 4 n-tile groups: about 1400
+    items for a grid of at most two blocks per CU), so that items are dealt
+    in forward and in reverse block order; every output is compared."""
+    m = _m()
+    pattern = [0, 1, 16, 17, 32, 33, 63, 64, 65, 81, 100, 128, 150]
+    E = 256
+    counts = [pattern[(7 * e) % len(pattern)] for e in range(E)]
+    got, want = _moe_case(E=E, S=0, N=512, K=256, ranks=[16, 32, 0, 8] * 64, T=sum(counts), k=1,
+                          epilogue=m.EPI_SWIGLU, path=PATHS["prefill"], seed=410,
+                          logits=_counts_logits(counts, E), max_rows=max(counts))
+    assert_close(got, want, "persistent launch, several rounds")
+
+
 @pytest.mark.parametrize("epi,lr", [("swiglu", "fp16"), ("route", "fp16"), ("swiglu", "int3")])
 def test_auto_small_matrices_sparse_batch(epi, lr):
     """Automatic path, small matrices, experts averaging under 16 rows with
