@@ -304,7 +304,11 @@ def device_info(timer):
     shader clock the driver reports after the timed region (best effort)."""
     import torch
     pr = torch.cuda.get_device_properties(0)
-    info = {"gpu": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count}
+    arch = getattr(pr, "gcnArchName", None)
+    # some driver installs report no marketing name (their device id table
+    # is missing); the architecture then names the part
+    name = pr.name or f"unnamed by the driver ({(arch or '?').split(':')[0]})"
+    info = {"gpu": name, "arch": arch, "compute_units": pr.multi_processor_count}
     v = C.c_int()
     h = timer.h
     h.hipDeviceGetAttribute.argtypes = [C.POINTER(C.c_int), C.c_int, C.c_int]
