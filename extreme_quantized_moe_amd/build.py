@@ -16,7 +16,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmilo.so")
 SOURCES = ["abi.cpp", "quant_pack.hip", "route.hip", "combine.hip", "lowrank.hip",
-           "gemm_decode.hip", "gemm_prefill.hip", "builder.hip", "rank_policy.hip"]
+           "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_128.hip", "builder.hip", "rank_policy.hip"]
+# per-file flags: the 128-row tile kernels under the max-ILP scheduler
+# (measured faster there; the other kernels are neutral or spill under it)
+FILE_FLAGS = {"gemm_prefill_128.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"]}
 ARCH = os.environ.get("MILO_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,7 +34,7 @@ FLAGS = [
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     return src, obj, r.returncode, r.stdout + r.stderr, cmd
 
